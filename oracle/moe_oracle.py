@@ -1,0 +1,200 @@
+"""fp64 CPU oracle for one routed mixture-of-experts layer with an always-on shared expert,
+and for a stack of such layers joined by RMSNorm and a residual add.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path may import, call or link this module:
+only the test-suite, the smoke check and the benchmark's CPU-baseline leg use it. It shares
+no code with the HIP path; the two meet only at the seeded inputs.
+
+What it computes, and where that comes from
+-------------------------------------------
+The pages ("Flash Next EXL3: exact deep prefill", PR #1443, opening section) describe
+expert-major deep-prefill chunks that use one canonical routed-expert reduction, so that
+deep prefill gives the batched pass's bytes at any chunk size (the equality gate at chunk
+sizes 256 / 1,024 / 2,048 in its "Completed final functional audit" section). Deep prefill
+therefore reaches exactly the plain layer result, only in a fixed order, and the oracle is
+that plain result written out per token, in float64:
+
+  1. router logits  l[t, e] = sum_i x[t, i] * W_r[e, i] + b[e]
+  2. top-k: the k largest logits of token t; among equal logits the lower expert id wins;
+     the chosen ids are listed in ascending id order
+  3. weights: softmax of l[t, :] over all E experts, renormalised over the chosen k
+  4. each chosen expert e: gate = W_gate,e x, up = W_up,e x, h = silu(gate) * up,
+     y_e = W_down,e h, with silu(z) = z / (1 + exp(-z)); W_gu holds the gate rows first,
+     then the up rows (the pages name gate/up ("GU") and down expert kernels in the
+     "Completed device checks" and numerical-audit sections of that page, no formulas)
+  5. the shared expert (PR #1113, "Memory and execution split": a resident shared expert
+     beside the routed ones) gives s_t the same way, with weight 1
+  6. out_t = sum over chosen e in ascending id of w[t, e] * y_e, plus s_t
+  7. stack: x <- x + layer(x / sqrt(mean(x^2) + eps)) (RMSNorm without gain, pre-norm)
+
+Steps 2-7 are readings of what the pages leave open; each is listed with its reason in the
+design notes. Member lists (which rows each expert processes, in token order) and per-chunk
+expert counts are integer bookkeeping whose definition is unique; they are written out too.
+
+Parity pins: every function here is checked in the CPU test-suite against brute force,
+closed forms, library routines and invariants, not against itself.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+# ---------------------------------------------------------------- input widening
+
+def as_f64(a):
+    """Exact float64 copy. uint16 arrays are bf16 bit patterns (upper half of an fp32)."""
+    if a is None:
+        return None
+    a = np.asarray(a)
+    if a.dtype == np.uint16:
+        return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    return a.astype(np.float64)
+
+
+# ---------------------------------------------------------------- routing
+
+def router_logits(x, w_router, bias=None):
+    """l = x W_r^T + b, float64. x [T, d], w_router [E, d], bias [E] or None."""
+    logits = as_f64(x) @ as_f64(w_router).T
+    if bias is not None:
+        logits = logits + as_f64(bias)[None, :]
+    return logits
+
+
+def select_topk(logits, k):
+    """ids [T, k]: each row's k largest logits (lower id first among equal values), then
+    sorted by ascending expert id."""
+    logits = np.asarray(logits, dtype=np.float64)
+    # a stable sort of -l keeps equal values in ascending id order
+    order = np.argsort(-logits, axis=1, kind="stable")
+    return np.sort(order[:, :k], axis=1)
+
+
+def topk_margin(logits, k):
+    """l_(k) - l_(k+1) per row: the gap between the k-th and (k+1)-th largest logit
+    (+inf when k equals the number of experts)."""
+    logits = np.asarray(logits, dtype=np.float64)
+    E = logits.shape[1]
+    if k >= E:
+        return np.full(logits.shape[0], np.inf)
+    srt = -np.sort(-logits, axis=1)
+    return srt[:, k - 1] - srt[:, k]
+
+
+def topk_weights(logits, ids):
+    """Routing weights [T, k]: softmax over all experts, renormalised over the chosen ids."""
+    logits = np.asarray(logits, dtype=np.float64)
+    p = np.exp(logits - logits.max(axis=1, keepdims=True))
+    p = p / p.sum(axis=1, keepdims=True)
+    chosen = np.take_along_axis(p, np.asarray(ids), axis=1)
+    return chosen / chosen.sum(axis=1, keepdims=True)
+
+
+# ---------------------------------------------------------------- expert FFN
+
+def silu(z):
+    return z / (1.0 + np.exp(-z))
+
+
+def expert_ffn(xr, w_gu, w_down):
+    """One SwiGLU expert on rows xr [n, d]: w_gu [2I, d] (gate rows, then up rows),
+    w_down [d, I]. Returns [n, d] float64."""
+    xr = as_f64(xr)
+    w_gu = as_f64(w_gu)
+    inter = w_gu.shape[0] // 2
+    gate = xr @ w_gu[:inter].T
+    up = xr @ w_gu[inter:].T
+    h = silu(gate) * up
+    return h @ as_f64(w_down).T
+
+
+# ---------------------------------------------------------------- bookkeeping
+
+def member_lists(ids, n_experts):
+    """Expert-major member lists of one chunk (token indices local to the chunk).
+
+    counts[e]   rows routed to expert e
+    offsets[e]  first row of expert e (exclusive prefix sum, offsets[E] = n*k)
+    row_tok[r]  token of row r; rows of one expert are in ascending token order
+    row_slot[r] t*k + j, where j is the position of e among token t's ascending ids
+    """
+    ids = np.asarray(ids)
+    n, k = ids.shape
+    counts = np.zeros(n_experts, dtype=np.int64)
+    for e in ids.ravel():
+        counts[e] += 1
+    offsets = np.zeros(n_experts + 1, dtype=np.int64)
+    offsets[1:] = np.cumsum(counts)
+    row_tok = np.empty(n * k, dtype=np.int64)
+    row_slot = np.empty(n * k, dtype=np.int64)
+    fill = offsets[:-1].copy()
+    for t in range(n):                      # tokens in ascending order
+        for j in range(k):
+            e = ids[t, j]
+            row_tok[fill[e]] = t
+            row_slot[fill[e]] = t * k + j
+            fill[e] += 1
+    return counts, offsets, row_tok, row_slot
+
+
+def chunk_counts(ids, chunk, n_experts):
+    """[ceil(T/chunk), E]: tokens of chunk c = [c*chunk, min((c+1)*chunk, T)) per expert."""
+    ids = np.asarray(ids)
+    T = ids.shape[0]
+    n_chunks = (T + chunk - 1) // chunk
+    out = np.zeros((n_chunks, n_experts), dtype=np.int64)
+    for c in range(n_chunks):
+        rows = ids[c * chunk: min((c + 1) * chunk, T)]
+        out[c] = np.bincount(rows.ravel(), minlength=n_experts)
+    return out
+
+
+# ---------------------------------------------------------------- the layer
+
+def moe_layer(x, params, ids=None):
+    """One MoE layer over all rows of x [T, d] (the result is per token, so chunking does
+    not change it).
+
+    params: w_router [E, d], router_bias [E] or None, w_gu [E, 2I, d], w_down [E, d, I],
+    w_gu_shared [2Is, d] or None, w_down_shared [d, Is] or None, top_k. Arrays may be bf16
+    bit patterns (uint16) and are widened one expert at a time.
+    ids: optional [T, k] expert ids to use instead of the oracle's own top-k (the routing
+    gates substitute a set only where two logits are closer than the fp32 path can order).
+    Returns dict(out [T, d], logits [T, E], ids [T, k], weights [T, k]).
+    """
+    x64 = as_f64(x)
+    T, d = x64.shape
+    k = int(params["top_k"])
+    logits = router_logits(x64, params["w_router"], params.get("router_bias"))
+    E = logits.shape[1]
+    if ids is None:
+        ids = select_topk(logits, k)
+    ids = np.asarray(ids, dtype=np.int64)
+    w = topk_weights(logits, ids)
+
+    out = np.zeros((T, d), dtype=np.float64)
+    for e in range(E):                      # ascending expert id
+        t_idx, j_idx = np.nonzero(ids == e)
+        if t_idx.size == 0:
+            continue
+        y = expert_ffn(x64[t_idx], params["w_gu"][e], params["w_down"][e])
+        out[t_idx] += w[t_idx, j_idx][:, None] * y   # a token picks e at most once
+    if params.get("w_gu_shared") is not None:
+        out += expert_ffn(x64, params["w_gu_shared"], params["w_down_shared"])
+    return {"out": out, "logits": logits, "ids": ids, "weights": w}
+
+
+# ---------------------------------------------------------------- stack
+
+def rmsnorm(x, eps):
+    """x / sqrt(mean(x^2) + eps) per row (no gain)."""
+    x = as_f64(x)
+    return x / np.sqrt(np.mean(x * x, axis=1, keepdims=True) + eps)
+
+
+def moe_stack(x, layers, eps):
+    """x <- x + layer_l(rmsnorm(x)) for each layer, float64 throughout."""
+    x = as_f64(x)
+    for p in layers:
+        x = x + moe_layer(rmsnorm(x, eps), p)["out"]
+    return x

@@ -1,0 +1,10 @@
+"""The fp64 oracle against its pins (CPU only)."""
+import pytest
+
+import oracle.moe_oracle as orc
+from tests.oracle_pins import ALL_PINS
+
+
+@pytest.mark.parametrize("pin", ALL_PINS, ids=[p.__name__ for p in ALL_PINS])
+def test_pin(pin):
+    pin(orc)

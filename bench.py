@@ -1,0 +1,237 @@
+#!/usr/bin/env python3
+"""Benchmark of expert-major deep prefill of one routed MoE layer on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1]
+
+Workload (headline): one layer with d = 2048, E = 512 routed experts, top-8, expert
+intermediate 512 and a shared expert of intermediate 2048, bf16 storage with fp32
+accumulation, T = 16,022 prompt tokens routed without bias, all experts resident in HBM, run
+as the batched pass (one chunk of T rows). Inputs and weights are seeded synthetic tensors,
+already in HBM when timing starts. One step = the whole path once: router GEMM, top-k,
+per-chunk counts, bucketing (histogram, scan, permute), shared and routed grouped GEMMs with
+the fused SiLU epilogue, and the combine.
+
+Prints one JSON line (stdout). Per-kernel times come from HIP events that the library records
+around each of its launches on the launch's own stream, over a second pass of the same K
+steps (the headline time comes from a pass without those events). Also reported: the same
+layer at deep chunk 2,048, the layer with all experts streamed from a pinned host bank
+through a 64-line ring at chunk 2,048, and the fp64 CPU oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer prefill tokens/s and MFMA TFLOP/s fraction at T=16k, E=512, k=8"
+PEAK_BF16 = 2.5e15      # dense bf16 MFMA, FLOP/s
+PEAK_HBM = 8.0e12       # HBM3E, B/s
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic(stage: str, T: int, sh, counts):
+    """(flops, bytes) of one step's launches of a stage: data each kernel must touch once
+    (weights of used experts, activations, intermediates, outputs), no padding."""
+    d, E, k, I, Is = sh.d, sh.n_experts, sh.top_k, sh.inter, sh.inter_shared
+    Ns = T * k
+    used = int((counts > 0).sum())
+    if stage == "router":
+        return 2 * T * d * E, T * d * 2 + E * d * 2 + T * E * 4
+    if stage == "topk":
+        return 0, T * E * 4 + T * k * 8
+    if stage == "gu_routed":
+        return 2 * Ns * d * 2 * I, used * 2 * I * d * 2 + Ns * d * 2 + Ns * I * 2
+    if stage == "down_routed":
+        return 2 * Ns * I * d, used * d * I * 2 + Ns * I * 2 + Ns * d * 4
+    if stage == "gu_shared":
+        return 2 * T * d * 2 * Is, 2 * Is * d * 2 + T * d * 2 + T * Is * 2
+    if stage == "down_shared":
+        return 2 * T * Is * d, d * Is * 2 + T * Is * 2 + T * d * 4
+    if stage == "combine":
+        return 2 * Ns * d, Ns * d * 4 + T * d * 4 + T * k * 4 + T * d * 2
+    if stage in ("hist", "permute"):
+        return 0, Ns * 4 * (1 if stage == "hist" else 3)
+    return 0, 0
+
+
+def time_steps(fn, steps, warmup):
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - w0) * 1e3 / steps
+    return a.elapsed_time(b) / steps, wall
+
+
+def cpu_baseline(params, wl, x, n_tokens):
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import moe_inputs as mi
+    import oracle.moe_oracle as orc
+    from tests.parity import oracle_params
+    op = oracle_params(params, wl)
+    xs = mi.to_numpy_exact(x[:n_tokens])
+    threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    t0 = time.perf_counter()
+    orc.moe_layer(xs, op)
+    dt = time.perf_counter() - t0
+    sh = wl.shape
+    flop = n_tokens * (2 * sh.d * sh.n_experts + 6 * sh.d * sh.inter * sh.top_k
+                       + 6 * sh.d * sh.inter_shared)
+    return {"value": round(n_tokens / dt, 2), "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"first {n_tokens} of the {wl.T} tokens, same layer (all 512 experts "
+                      f"widened from bf16 as used), fp64 numpy, {dt:.1f} s",
+            "gflops_fp64": round(flop / dt / 1e9, 2)}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=384)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        log("bench.py runs on one GPU only: this build has no multi-GPU path "
+            "(no collectives or sharding); run it with --gpus 1.")
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_inputs as mi
+    import routed_expert_grouped_moe_amd as moe
+    from tests.parity import place
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    wl = mi.WORKLOADS["offload_16022"]      # T = 16,022 inputs (seeded), placed resident here
+    T = wl.T
+    log(f"[bench] generating layer and {T} tokens on cuda:0")
+    params, L = place(wl)
+    x = mi.make_x(wl, device="cuda")
+    sh = L.shape
+    torch.cuda.synchronize()
+
+    bufs = moe.layer_buffers(L, T, T)
+    step = lambda: moe.moe_prefill_layer(L, x, T, bufs=bufs)
+    log(f"[bench] batched pass: warmup {args.warmup}, steps {args.steps}")
+    ms, wall_ms = time_steps(step, args.steps, args.warmup)
+    counts = bufs["chunk_counts"][0].cpu().numpy()
+
+    moe.moe_profile_read(reset=True)
+    moe.moe_profile_enable(True)
+    ms_prof, _ = time_steps(step, args.steps, 0)
+    moe.moe_profile_enable(False)
+    prof = moe.moe_profile_read(reset=True)
+
+    flop_tok = 2 * sh.d * sh.n_experts + 6 * sh.d * sh.inter * sh.top_k + 6 * sh.d * sh.inter_shared
+    tok_s = T / (ms / 1e3)
+    tflops = flop_tok * T / (ms / 1e3) / 1e12
+    kernels = {}
+    for stage, (tot_ms, n) in prof.items():
+        if n == 0:
+            continue
+        per_launch_ms = tot_ms / n
+        f, b = algorithmic(stage, T, sh, counts)
+        per_step_launches = n / args.steps
+        f_l, b_l = f / per_step_launches, b / per_step_launches
+        ent = {"ms_per_step": round(tot_ms / args.steps, 4), "launches_per_step": per_step_launches,
+               "avg_launch_us": round(per_launch_ms * 1e3, 2)}
+        if f:
+            ent["tflops"] = round(f_l / (per_launch_ms / 1e3) / 1e12, 2)
+            ent["mfma_frac"] = round(ent["tflops"] * 1e12 / PEAK_BF16, 4)
+        if b:
+            ent["gbps"] = round(b_l / (per_launch_ms / 1e3) / 1e9, 1)
+            ent["hbm_frac"] = round(ent["gbps"] * 1e9 / PEAK_HBM, 4)
+        kernels[stage] = ent
+    gemm = ["gu_routed", "down_routed", "gu_shared", "down_shared"]
+    gemm_ms = sum(prof[s][0] for s in gemm) / args.steps
+    gemm_flop = sum(algorithmic(s, T, sh, counts)[0] for s in gemm)
+    dom = max(gemm, key=lambda s: prof[s][0])
+    f, b = algorithmic(dom, T, sh, counts)
+    n_l = prof[dom][1] / args.steps
+    avg_s = prof[dom][0] / prof[dom][1] / 1e3
+    t_mfma, t_hbm = (f / n_l) / PEAK_BF16, (b / n_l) / PEAK_HBM
+    if t_hbm >= t_mfma:
+        ach = (b / n_l) / avg_s / 1e9
+        roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": 8000.0,
+                "unit": "GB/s", "frac": round(ach / 8000.0, 4), "traffic": None,
+                "bytes_per_launch": int(b / n_l), "avg_launch_us": round(avg_s * 1e6, 2)}
+    else:
+        ach = (f / n_l) / avg_s / 1e12
+        roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": 2500.0,
+                "unit": "TFLOP/s", "frac": round(ach / 2500.0, 4), "traffic": None,
+                "flops_per_launch": int(f / n_l), "avg_launch_us": round(avg_s * 1e6, 2)}
+
+    variants = {}
+    if not args.no_variants:
+        b2 = moe.layer_buffers(L, T, 2048)
+        v_ms, _ = time_steps(lambda: moe.moe_prefill_layer(L, x, 2048, bufs=b2), max(3, args.steps // 2), 2)
+        ok = torch.equal(b2["out"].view(torch.int16), bufs["out"].view(torch.int16))
+        variants["resident_chunk2048"] = {"tokens_per_s": round(T / (v_ms / 1e3), 1),
+                                          "ms_per_step": round(v_ms, 3),
+                                          "bit_identical_to_batched": bool(ok)}
+        del b2
+        log("[bench] ring variant: all 512 experts in a pinned bank, 64 lines, chunk 2048")
+        ring = moe.Ring(sh, 64)
+        _, Lr = place(wl, offloaded=range(sh.n_experts), ring=ring, params=params)
+        br = moe.layer_buffers(Lr, T, 2048)
+        cs = torch.cuda.Stream()
+        r_ms, r_wall = time_steps(lambda: moe.moe_prefill_layer(Lr, x, 2048, bufs=br, copy_stream=cs), 3, 1)
+        ok = torch.equal(br["out"].view(torch.int16), bufs["out"].view(torch.int16))
+        st = ring.stats()
+        variants["offload_ring64_chunk2048"] = {
+            "tokens_per_s": round(T / (r_wall / 1e3), 1), "ms_per_step": round(r_wall, 2),
+            "h2d_gb_per_step": round(st["bytes_h2d"] / 4 / 1e9, 3),
+            "h2d_gbps": round(st["bytes_h2d"] / 4 / (r_wall / 1e3) / 1e9, 2),
+            "bit_identical_to_batched": bool(ok)}
+        del br, Lr
+        ring.close()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle baseline on {args.cpu_sample_tokens} tokens")
+        cpu = cpu_baseline(params, wl, x, args.cpu_sample_tokens)
+
+    line = {
+        "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic: seeded Gaussian activations and random-init weights "
+                "(1/sqrt(fan_in)), router std 0.02, uniform routing",
+        "config": {"workload": "moe_layer_T16022_d2048_E512_k8_I512_shared2048_resident_batched",
+                   "T": T, "chunk": T, "d": sh.d, "n_experts": sh.n_experts, "top_k": sh.top_k,
+                   "inter": sh.inter, "inter_shared": sh.inter_shared, "experts": "resident"},
+        "tflops": round(tflops, 2), "mfma_frac": round(tflops * 1e12 / PEAK_BF16, 4),
+        "grouped_gemm_mfma_frac": round(gemm_flop / (gemm_ms / 1e3) / PEAK_BF16, 4),
+        "wall_ms_per_step": round(wall_ms, 4), "ms_per_step_profiled": round(ms_prof, 4),
+        "roofline": roof, "cpu_baseline": cpu, "kernels": kernels, "variants": variants,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,259 @@
+/*
+ * moe_prefill.h — C ABI of the MI355X (gfx950) expert-major "deep" prefill library for one
+ * routed mixture-of-experts layer with an always-on shared expert.
+ *
+ * The operation (readings of the pages, whose own text gives no formulas):
+ *   logits = x W_r^T + b; each token takes its k largest logits (lower expert id first among
+ *   equal values), listed in ascending expert id; weights = softmax of the logits renormalised
+ *   over the chosen k; every chosen expert computes W_down (silu(W_gate x) * (W_up x)); the
+ *   shared expert does the same with weight 1; out = sum over chosen experts in ascending id of
+ *   weight * expert output, plus the shared output, accumulated in fp32 and rounded once.
+ * Sources: "Flash Next EXL3: exact deep prefill" (PR #1443), opening section — expert-major
+ * deep-prefill chunks with one canonical routed-expert reduction, so any chunk size gives the
+ * batched pass's bytes ("Completed final functional audit": chunk sizes 256/1,024/2,048);
+ * "deep prefill (slice 3 of 7)" (PR #1443, What) — a ring of staged expert lines whose copies
+ * overlap compute; "EXL3 on upstream" (PR #1113, Loading and "Latest prefill efficiency
+ * candidate") — pinned host expert banks, asynchronous host-to-device staging, one copy per
+ * expert when its projections are adjacent in the bank, release epochs guarding line reuse.
+ *
+ * Conventions for every call:
+ *   - All tensors are caller-owned; the library allocates no device memory. It owns only a
+ *     ring's host-side bookkeeping and its HIP events.
+ *   - Device pointers are 16-byte aligned, row-major, densely packed.
+ *   - Work is enqueued on the given HIP stream and returns without waiting (except where a
+ *     call says it synchronises). Buffers must stay alive until the enqueued work finishes.
+ *   - Arguments are validated before anything is enqueued: on MOE_ERR_INVALID,
+ *     MOE_ERR_WORKSPACE, MOE_ERR_RING or MOE_ERR_UNSUPPORTED nothing is enqueued and no output
+ *     byte changes. On MOE_ERR_HIP the outputs of that call are undefined.
+ *     moe_last_error() names the failing check or HIP call (per thread).
+ *   - Results do not depend on the chunk size or on where a token sits inside a chunk: every
+ *     token's bytes are the same at any chunk size, in the batched pass, and with or without the
+ *     staging ring. Repeated calls give identical bytes (no floating-point atomics).
+ */
+#ifndef MOE_PREFILL_H
+#define MOE_PREFILL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_ABI_VERSION 1
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID = 1,     /* bad shape, pointer, alignment or range */
+  MOE_ERR_WORKSPACE = 2,   /* workspace smaller than moe_workspace_bytes(shape, n) */
+  MOE_ERR_RING = 3,        /* ring missing, too small, or no bank bound for an offloaded expert */
+  MOE_ERR_HIP = 4,         /* a HIP runtime call failed; outputs of this call are undefined */
+  MOE_ERR_UNSUPPORTED = 5  /* valid request this build does not handle */
+} moe_status;
+
+typedef enum { MOE_BF16 = 0, MOE_F32 = 1 } moe_dtype;
+
+/* Layer shape. d: hidden size, multiple of 64 in [64, 16384]; n_experts (E) in [1, 1024];
+ * top_k (k) in [1, E]; inter (I): routed expert intermediate size, multiple of 64 in
+ * [64, 16384]; inter_shared (I_s): shared expert intermediate size, multiple of 64 in
+ * [0, 65536], 0 = no shared expert; dtype: storage type of x, weights and out (MOE_BF16 uses
+ * bf16 storage with fp32 accumulation and a bf16 intermediate h; MOE_F32 keeps everything fp32).
+ */
+typedef struct {
+  int32_t d;
+  int32_t n_experts;
+  int32_t top_k;
+  int32_t inter;
+  int32_t inter_shared;
+  int32_t dtype;
+} moe_shape;
+
+/* Opaque ring of device expert lines (library-owned host bookkeeping + HIP events). */
+typedef struct moe_ring moe_ring;
+
+/* An expert line is one contiguous block of 3*I*d elements: W_gu [2I, d] (gate rows 0..I-1,
+ * then up rows I..2I-1) followed by W_down [d, I]. Moving one expert is one contiguous copy. */
+
+/* One layer. All pointers are borrowed. */
+typedef struct {
+  moe_shape shape;
+  const void* w_router;            /* device [E, d], dtype */
+  const float* router_bias;        /* device [E] fp32, or NULL for no bias */
+  const void* const* expert_lines; /* HOST array [E] of device pointers to expert lines; an
+                                      entry may be NULL only when `ring` has a bank bound for
+                                      this layer that holds that expert (it is then staged) */
+  const void* w_gu_shared;         /* device [2*I_s, d] (gate rows, then up rows); NULL iff I_s==0 */
+  const void* w_down_shared;       /* device [d, I_s]; NULL iff I_s == 0 */
+  moe_ring* ring;                  /* NULL: every expert resident */
+  int32_t layer_id;                /* key of this layer's bank in the ring (>= 0) */
+} moe_layer;
+
+/* Version of this ABI (MOE_ABI_VERSION of the built library). */
+int32_t moe_abi_version(void);
+
+/* Readable name of a status code (static string). */
+const char* moe_status_string(moe_status s);
+
+/* Message of the last failing call on this thread ("" if none). Valid until the next call. */
+const char* moe_last_error(void);
+
+/* Bytes of device workspace moe_prefill_chunk needs for chunks of up to max_chunk_tokens rows
+ * (0 for an invalid shape). Pure host computation. */
+size_t moe_workspace_bytes(const moe_shape* shape, int64_t max_chunk_tokens);
+
+/* Where a moe_prefill_chunk call over n rows leaves its expert-major member lists inside the
+ * workspace (byte offsets from the workspace start; the buckets of the per-expert lists of
+ * the pages' "EXL3 on upstream" page, PR #1113, "Latest prefill efficiency candidate"). After
+ * the call: counts int32 [E] rows per expert; offsets int32 [E+1] first row of each expert
+ * (exclusive prefix sum); row_tok int32 [n*k] chunk-local token of each expert-major row, in
+ * ascending token order within an expert; row_slot int32 [n*k] t*k + j of each row (j = the
+ * expert's position among the token's ascending ids). For inspection and tests. */
+typedef struct {
+  size_t counts;
+  size_t offsets;
+  size_t row_tok;
+  size_t row_slot;
+  size_t total;   /* == moe_workspace_bytes(shape, n) */
+} moe_ws_offsets;
+
+moe_status moe_workspace_offsets(const moe_shape* shape, int64_t n, moe_ws_offsets* out);
+
+/* Routing of a whole prompt (router GEMM on MFMA, one-wavefront-per-token top-k with
+ * softmax-renormalised weights, per-chunk expert histogram).
+ *   x            device [T, d] dtype
+ *   T            tokens, >= 0 (T == 0 enqueues nothing)
+ *   chunk        chunk size used to bucket chunk_counts, >= 1
+ *   ids          device [T, k] int32 out: chosen experts, ascending per token
+ *   weights      device [T, k] fp32 out: routing weights in the order of ids
+ *   chunk_counts device [ceil(T/chunk), E] int32 out: tokens of chunk c routed to expert e
+ *   logits       device [T, E] fp32 out: router logits (bias included)
+ * Asynchronous on `stream`. */
+moe_status moe_prefill_route(const moe_layer* layer, const void* x, int64_t T, int64_t chunk,
+                             int32_t* ids, float* weights, int32_t* chunk_counts, float* logits,
+                             void* stream);
+
+/* Expert-major prefill of rows [t0, t0+n) of a routed prompt: bucket the chunk's tokens per
+ * expert (histogram, scan, stable permute on the GPU), run each expert's gate/up GEMM with the
+ * fused silu(gate)*up epilogue and its down GEMM (grouped, bf16 MFMA, fp32 accumulation), the
+ * shared expert over all n rows, then the fixed-order combine into out rows t0..t0+n-1.
+ *   x, ids, weights: the whole prompt's tensors as passed to / returned by moe_prefill_route
+ *   counts_host  HOST [E] int32 expert counts of this chunk, or NULL. Only used with a ring: if
+ *                NULL the call copies the counts to the host and waits for them (its only
+ *                synchronisation).
+ *   out          device [T, d] dtype; only rows t0..t0+n-1 are written
+ *   ws, ws_bytes device workspace of at least moe_workspace_bytes(shape, n) bytes
+ *   stream       compute stream; copy_stream: stream for ring copies (NULL = stream)
+ * The batched pass is t0 = 0, n = T. n == 0 enqueues nothing. */
+moe_status moe_prefill_chunk(const moe_layer* layer, const void* x, const int32_t* ids,
+                             const float* weights, int64_t T, int64_t t0, int64_t n,
+                             const int32_t* counts_host, void* out, void* ws, size_t ws_bytes,
+                             void* stream, void* copy_stream);
+
+/* Whole-prompt convenience: route, then moe_prefill_chunk over [c*chunk, min((c+1)*chunk, T))
+ * for every chunk in order. With a ring, the per-chunk counts come from one device-to-host copy
+ * of chunk_counts (one synchronisation per call). Arguments as in the two calls above;
+ * ws must hold moe_workspace_bytes(shape, min(chunk, T)). */
+moe_status moe_prefill_layer(const moe_layer* layer, const void* x, int64_t T, int64_t chunk,
+                             int32_t* ids, float* weights, int32_t* chunk_counts, float* logits,
+                             void* out, void* ws, size_t ws_bytes, void* stream,
+                             void* copy_stream);
+
+/* Ring of n_lines device expert lines, each line_bytes = 3*I*d*sizeof(dtype), in the
+ * caller-owned buffer device_lines [n_lines * line_bytes] (256-byte aligned). Creates 2
+ * events per line. On failure every partially created event is destroyed and *out = NULL. */
+moe_status moe_ring_create(const moe_shape* shape, void* device_lines, int32_t n_lines,
+                           moe_ring** out);
+
+/* Register layer `layer_id`'s pinned host bank (page-locked, e.g. hipHostMalloc) of expert
+ * lines: expert e lives at pinned_bank + bank_slot_of_expert[e] * line_bytes; -1 = the expert
+ * is resident (the layer's expert_lines entry is used). bank_slot_of_expert is a HOST array
+ * [E], copied. Rebinding a layer drops its cached lines. */
+moe_status moe_ring_bind_bank(moe_ring* ring, int32_t layer_id, const void* pinned_bank,
+                              const int32_t* bank_slot_of_expert);
+
+/* Make the listed experts of a layer present in ring lines. Each expert already held by a line
+ * is a hit; each miss takes the least recently used line that no unreleased call holds,
+ * waits on `copy_stream` for that line's last release, copies the expert's line from the
+ * pinned bank (one hipMemcpyAsync) and records the line's `ready` event. The lines stay held
+ * until moe_ring_release. experts: HOST [n] ids (distinct, offloaded in the bank);
+ * lines_out: HOST [n] or NULL, receives each expert's line. MOE_ERR_RING if too few lines
+ * are free (nothing changes then). */
+moe_status moe_stage_experts(moe_ring* ring, int32_t layer_id, const int32_t* experts,
+                             int32_t n, void* copy_stream, int32_t* lines_out);
+
+/* Make `stream` wait until the listed lines' copies have landed (their `ready` events). */
+moe_status moe_ring_wait_ready(moe_ring* ring, const int32_t* lines, int32_t n, void* stream);
+
+/* Record the listed lines' `release` events on `stream` (after the work that reads them) and
+ * let later staging reuse them. */
+moe_status moe_ring_release(moe_ring* ring, const int32_t* lines, int32_t n, void* stream);
+
+/* Device pointer of a ring line (NULL for a bad index). */
+const void* moe_ring_line_ptr(const moe_ring* ring, int32_t line);
+
+/* Ring counters (all cumulative since creation or moe_ring_reset_stats). */
+typedef struct {
+  int32_t version;            /* set to 1 by the library */
+  int32_t n_lines;
+  int64_t hits;               /* staged experts already present in a line */
+  int64_t misses;             /* staged experts copied from a bank */
+  int64_t bytes_h2d;          /* bytes copied host -> device */
+  int64_t copy_waits;         /* copy-stream waits on a line's release event */
+  int64_t waves;              /* staging waves run by moe_prefill_chunk */
+} moe_ring_stats_t;
+
+moe_status moe_ring_stats(const moe_ring* ring, moe_ring_stats_t* stats_out);
+moe_status moe_ring_reset_stats(moe_ring* ring);
+
+/* Forget every cached line (next staging copies again). Does not wait for the GPU. */
+moe_status moe_ring_invalidate(moe_ring* ring);
+
+/* Wait for the ring's outstanding events, destroy them and free the ring. NULL-safe. */
+void moe_ring_destroy(moe_ring* ring);
+
+/* Per-kernel timing with HIP events. While enabled, every launch the library enqueues is
+ * bracketed by two timing events recorded on the launch's own stream; moe_profile_read waits
+ * for the recorded events and adds their elapsed times to per-stage totals. Process-wide and
+ * thread-safe; off by default (then no events are recorded). */
+enum {
+  MOE_STAGE_ROUTER = 0,     /* router GEMM */
+  MOE_STAGE_TOPK = 1,       /* top-k + weights */
+  MOE_STAGE_CHUNK_COUNTS = 2,
+  MOE_STAGE_TABLE = 3,      /* expert-line pointer table uploads */
+  MOE_STAGE_HIST = 4,       /* per-block expert histogram of a chunk */
+  MOE_STAGE_SCAN = 5,       /* expert offsets and M-tile list */
+  MOE_STAGE_PERMUTE = 6,    /* stable member-list permute */
+  MOE_STAGE_GU_SHARED = 7,
+  MOE_STAGE_DOWN_SHARED = 8,
+  MOE_STAGE_GU_ROUTED = 9,
+  MOE_STAGE_DOWN_ROUTED = 10,
+  MOE_STAGE_COMBINE = 11,
+  MOE_STAGE_RMSNORM = 12,
+  MOE_STAGE_COUNT = 13
+};
+
+typedef struct {
+  int32_t version;          /* 1 */
+  int32_t n_stages;         /* MOE_STAGE_COUNT */
+  double ms[16];            /* summed kernel time per stage, milliseconds */
+  int64_t launches[16];     /* launches per stage */
+} moe_profile_t;
+
+moe_status moe_profile_enable(int32_t on);
+/* Fill *out with the totals (after waiting for pending events); reset != 0 zeroes them. */
+moe_status moe_profile_read(moe_profile_t* out, int32_t reset);
+
+/* Stack glue between layers (RMSNorm without gain, residual add), bf16 or fp32 rows.
+ *   x_new = x + delta (rounded to dtype; skipped when delta == NULL, then x_new = x)
+ *   normed = x_new / sqrt(mean(x_new^2) + eps) (fp32 arithmetic, fixed reduction order,
+ *            rounded to dtype)
+ * x, delta, x_out, normed: device [T, d]; x_out may equal x (in place) or be NULL when
+ * delta == NULL. */
+moe_status moe_add_rmsnorm(const void* x, const void* delta, int64_t T, int32_t d,
+                           int32_t dtype, float eps, void* x_out, void* normed, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_PREFILL_H */

@@ -1,0 +1,430 @@
+// C ABI entry points: argument checks, workspace layout and the launch sequence of one
+// routed MoE layer (route, then expert-major chunks).
+#include <string.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "ring.h"
+
+namespace moe {
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
+inline bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+inline size_t elt_bytes(int dtype) { return dtype == MOE_BF16 ? 2 : 4; }
+
+moe_status check_shape(const moe_shape* sh) {
+  if (!sh) return set_error(MOE_ERR_INVALID, "shape is NULL");
+  if (sh->d < 64 || sh->d > 16384 || sh->d % 64)
+    return set_error(MOE_ERR_INVALID, "d=%d must be a multiple of 64 in [64, 16384]", sh->d);
+  if (sh->n_experts < 1 || sh->n_experts > 1024)
+    return set_error(MOE_ERR_INVALID, "n_experts=%d must be in [1, 1024]", sh->n_experts);
+  if (sh->top_k < 1 || sh->top_k > sh->n_experts)
+    return set_error(MOE_ERR_INVALID, "top_k=%d must be in [1, n_experts]", sh->top_k);
+  if (sh->inter < 64 || sh->inter > 16384 || sh->inter % 64)
+    return set_error(MOE_ERR_INVALID, "inter=%d must be a multiple of 64 in [64, 16384]",
+                     sh->inter);
+  if (sh->inter_shared < 0 || sh->inter_shared > 65536 || sh->inter_shared % 64)
+    return set_error(MOE_ERR_INVALID, "inter_shared=%d must be a multiple of 64 in [0, 65536]",
+                     sh->inter_shared);
+  if (sh->dtype != MOE_BF16 && sh->dtype != MOE_F32)
+    return set_error(MOE_ERR_INVALID, "dtype=%d", sh->dtype);
+  return MOE_OK;
+}
+
+moe_status check_layer(const moe_layer* L) {
+  if (!L) return set_error(MOE_ERR_INVALID, "layer is NULL");
+  moe_status st = check_shape(&L->shape);
+  if (st != MOE_OK) return st;
+  const moe_shape& sh = L->shape;
+  if (!L->w_router || !aligned(L->w_router, 16))
+    return set_error(MOE_ERR_INVALID, "w_router NULL or not 16-byte aligned");
+  if (L->router_bias && !aligned(L->router_bias, 4))
+    return set_error(MOE_ERR_INVALID, "router_bias not 4-byte aligned");
+  if (sh.inter_shared > 0) {
+    if (!L->w_gu_shared || !L->w_down_shared || !aligned(L->w_gu_shared, 16) ||
+        !aligned(L->w_down_shared, 16))
+      return set_error(MOE_ERR_INVALID, "shared expert weights NULL or not 16-byte aligned");
+  }
+  return MOE_OK;
+}
+
+// Expert table checks (needed by the chunk calls only). Sets *offloaded when some expert
+// comes from the ring.
+moe_status check_experts(const moe_layer* L, bool* offloaded) {
+  *offloaded = false;
+  if (!L->expert_lines) return set_error(MOE_ERR_INVALID, "expert_lines is NULL");
+  const moe_ring::Bank* bank = nullptr;
+  if (L->ring) {
+    if (L->layer_id < 0) return set_error(MOE_ERR_INVALID, "layer_id=%d", L->layer_id);
+    auto it = L->ring->banks.find(L->layer_id);
+    if (it != L->ring->banks.end()) bank = &it->second;
+    const moe_shape& a = L->ring->shape;
+    const moe_shape& b = L->shape;
+    if (a.d != b.d || a.inter != b.inter || a.dtype != b.dtype || a.n_experts != b.n_experts)
+      return set_error(MOE_ERR_RING, "ring shape does not match the layer");
+  }
+  for (int e = 0; e < L->shape.n_experts; ++e) {
+    const void* p = L->expert_lines[e];
+    if (p) {
+      if (!aligned(p, 16)) return set_error(MOE_ERR_INVALID, "expert line %d not aligned", e);
+      continue;
+    }
+    if (!bank) return set_error(MOE_ERR_RING, "expert %d has no device line and no ring bank", e);
+    if (bank->slot[e] < 0)
+      return set_error(MOE_ERR_RING, "expert %d has no device line and is not in the bank", e);
+    *offloaded = true;
+  }
+  return MOE_OK;
+}
+
+#define MOE_HIP(call)                                                                      \
+  do {                                                                                     \
+    hipError_t e_ = (call);                                                                \
+    if (e_ != hipSuccess)                                                                  \
+      return set_error(MOE_ERR_HIP, "%s: %s", #call, hipGetErrorString(e_));               \
+  } while (0)
+
+moe_status route_impl(const moe_layer* L, const void* x, int64_t T, int64_t chunk,
+                      int32_t* ids, float* weights, int32_t* chunk_counts, float* logits,
+                      hipStream_t s) {
+  const moe_shape& sh = L->shape;
+  MOE_HIP(launch_router_gemm(sh.dtype, x, L->w_router, L->router_bias, T, sh.d, sh.n_experts,
+                             logits, s));
+  MOE_HIP(launch_topk(logits, T, sh.n_experts, sh.top_k, ids, weights, s));
+  MOE_HIP(launch_chunk_hist(ids, T, sh.top_k, sh.n_experts, chunk, chunk_counts, s));
+  return MOE_OK;
+}
+
+// Routed GEMMs of a chunk whose experts come partly from the ring: the chunk's used
+// offloaded experts, in ascending id, are cut into waves of at most n_lines/2 experts; wave w
+// covers the expert-id range [lo_w, hi_w) (resident experts in that range run with it). Wave
+// w+1 is staged on the copy stream before wave w's GEMMs are enqueued, so copies overlap
+// compute; each wave waits for its lines' `ready` events and then records their `release`.
+moe_status ring_waves(const moe_layer* L, const void* x, int64_t t0, int64_t n,
+                      const int32_t* counts_host, char* ws, const WsLayout& W, hipStream_t s,
+                      hipStream_t cs) {
+  const moe_shape& sh = L->shape;
+  const int E = sh.n_experts, k = sh.top_k;
+  moe_ring* R = L->ring;
+  std::vector<int32_t> cnt(E);
+  if (counts_host) {
+    memcpy(cnt.data(), counts_host, sizeof(int32_t) * E);
+  } else {
+    MOE_HIP(hipMemcpyAsync(cnt.data(), ws + W.counts, sizeof(int32_t) * E,
+                           hipMemcpyDeviceToHost, s));
+    MOE_HIP(hipStreamSynchronize(s));
+  }
+  int64_t total = 0;
+  for (int e = 0; e < E; ++e) {
+    if (cnt[e] < 0) return set_error(MOE_ERR_INVALID, "negative count for expert %d", e);
+    total += cnt[e];
+  }
+  if (total != n * k)
+    return set_error(MOE_ERR_INVALID, "expert counts sum to %lld, chunk has %lld slots",
+                     static_cast<long long>(total), static_cast<long long>(n * k));
+  std::vector<int64_t> mt_begin(E + 1, 0);
+  for (int e = 0; e < E; ++e) mt_begin[e + 1] = mt_begin[e] + mtiles_of(cnt[e]);
+
+  std::vector<int32_t> used;
+  for (int e = 0; e < E; ++e)
+    if (!L->expert_lines[e] && cnt[e] > 0) used.push_back(e);
+  const int per_wave = std::max(1, R->n_lines / 2);
+  const int nw = std::max<int>(1, (static_cast<int>(used.size()) + per_wave - 1) / per_wave);
+  std::vector<std::vector<int32_t>> wexp(nw), wlines(nw);
+  std::vector<int32_t> lo(nw), hi(nw);
+  for (int w = 0; w < nw; ++w) {
+    const size_t b = static_cast<size_t>(w) * per_wave;
+    const size_t e = std::min(used.size(), b + per_wave);
+    for (size_t i = b; i < e; ++i) wexp[w].push_back(used[i]);
+    wlines[w].resize(wexp[w].size());
+    lo[w] = w == 0 ? 0 : hi[w - 1];
+    hi[w] = (w + 1 < nw) ? used[static_cast<size_t>(w + 1) * per_wave] : E;
+  }
+
+  const void** wtab = reinterpret_cast<const void**>(ws + W.wtab);
+  GemmGroups g{reinterpret_cast<const MTile*>(ws + W.mtiles),
+               reinterpret_cast<const int32_t*>(ws + W.meta) + kMetaMTiles,
+               reinterpret_cast<const int32_t*>(ws + W.offsets),
+               reinterpret_cast<const int32_t*>(ws + W.counts), wtab, 0, 0};
+  const int32_t* row_tok = reinterpret_cast<const int32_t*>(ws + W.row_tok);
+  const int32_t* row_slot = reinterpret_cast<const int32_t*>(ws + W.row_slot);
+  char* h = ws + W.h;
+  float* y = reinterpret_cast<float*>(ws + W.y);
+
+  int staged = 0;
+  moe_status st = MOE_OK;
+  auto release_held = [&](int from) {          // unwind: give back lines of unfinished waves
+    for (int w = from; w < staged; ++w)
+      (void)ring_release(R, wlines[w].data(), static_cast<int32_t>(wlines[w].size()), s);
+  };
+  for (int w = 0; w < nw; ++w) {
+    while (staged < nw && staged <= w + 1) {   // this wave, and the next one if lines allow
+      st = ring_stage(R, L->layer_id, wexp[staged].data(),
+                      static_cast<int32_t>(wexp[staged].size()), cs, wlines[staged].data());
+      if (st == MOE_ERR_RING && staged > w) { st = MOE_OK; break; }   // retry after release
+      if (st != MOE_OK) { release_held(w); return st; }
+      ++staged;
+    }
+    const int32_t nl = static_cast<int32_t>(wlines[w].size());
+    std::vector<const void*> ptrs(nl);
+    for (int i = 0; i < nl; ++i) ptrs[i] = moe_ring_line_ptr(R, wlines[w][i]);
+    st = ring_wait_ready(R, wlines[w].data(), nl, s);
+    hipError_t err = hipSuccess;
+    if (st == MOE_OK) err = launch_upload_pairs(wtab, wexp[w].data(), ptrs.data(), nl, s);
+    g.tile_lo = static_cast<int>(mt_begin[lo[w]]);
+    g.tile_cap = static_cast<int>(mt_begin[hi[w]] - mt_begin[lo[w]]);
+    if (st == MOE_OK && err == hipSuccess)
+      err = launch_gu_routed(sh.dtype, x, t0, sh.d, sh.inter, g, row_tok, h, s);
+    if (st == MOE_OK && err == hipSuccess)
+      err = launch_down_routed(sh.dtype, h, sh.d, sh.inter, g, row_slot, y, s);
+    if (st == MOE_OK && err != hipSuccess)
+      st = set_error(MOE_ERR_HIP, "wave %d launch: %s", w, hipGetErrorString(err));
+    moe_status rst = ring_release(R, wlines[w].data(), nl, s);
+    if (st == MOE_OK) st = rst;
+    if (st != MOE_OK) { release_held(w + 1); return st; }
+    R->stats.waves++;
+  }
+  return MOE_OK;
+}
+
+moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const int32_t* ids,
+                      const float* weights, int64_t t0, int64_t n, const int32_t* counts_host,
+                      void* out, void* ws_v, size_t ws_bytes, hipStream_t s, hipStream_t cs) {
+  const moe_shape& sh = L->shape;
+  const int E = sh.n_experts, k = sh.top_k;
+  WsLayout W;
+  ws_layout(sh, n, &W);
+  if (ws_bytes < W.total)
+    return set_error(MOE_ERR_WORKSPACE, "workspace %zu bytes, %zu needed for %lld rows",
+                     ws_bytes, W.total, static_cast<long long>(n));
+  char* ws = static_cast<char*>(ws_v);
+  const void** wtab = reinterpret_cast<const void**>(ws + W.wtab);
+  MOE_HIP(launch_upload_ptrs(wtab, L->expert_lines, 0, E, s));
+  MOE_HIP(launch_bucket(ids + t0 * k, n, k, E, ws, W, s));
+  float* sbuf = sh.inter_shared ? reinterpret_cast<float*>(ws + W.s) : nullptr;
+  if (sh.inter_shared) {       // the shared expert needs no staging: enqueue it first
+    MOE_HIP(launch_gu_dense(sh.dtype, x, t0, n, sh.d, sh.inter_shared, L->w_gu_shared,
+                            ws + W.h_shared, s));
+    MOE_HIP(launch_down_dense(sh.dtype, ws + W.h_shared, n, sh.d, sh.inter_shared,
+                              L->w_down_shared, sbuf, s));
+  }
+  float* y = reinterpret_cast<float*>(ws + W.y);
+  if (!offloaded) {
+    GemmGroups g{reinterpret_cast<const MTile*>(ws + W.mtiles),
+                 reinterpret_cast<const int32_t*>(ws + W.meta) + kMetaMTiles,
+                 reinterpret_cast<const int32_t*>(ws + W.offsets),
+                 reinterpret_cast<const int32_t*>(ws + W.counts), wtab, 0,
+                 static_cast<int>(n * k / kBM + std::min<int64_t>(E, n * k))};
+    MOE_HIP(launch_gu_routed(sh.dtype, x, t0, sh.d, sh.inter, g,
+                             reinterpret_cast<const int32_t*>(ws + W.row_tok), ws + W.h, s));
+    MOE_HIP(launch_down_routed(sh.dtype, ws + W.h, sh.d, sh.inter, g,
+                               reinterpret_cast<const int32_t*>(ws + W.row_slot), y, s));
+  } else {
+    moe_status st = ring_waves(L, x, t0, n, counts_host, ws, W, s, cs ? cs : s);
+    if (st != MOE_OK) return st;
+  }
+  MOE_HIP(launch_combine(sh.dtype, y, sbuf, weights, t0, n, k, sh.d, out, s));
+  return MOE_OK;
+}
+
+moe_status check_rows(int64_t T, const moe_shape& sh) {
+  if (T < 0) return set_error(MOE_ERR_INVALID, "T=%lld", static_cast<long long>(T));
+  if (T > (int64_t{1} << 31) / sh.top_k - 1)
+    return set_error(MOE_ERR_INVALID, "T=%lld too large (T*k must fit int32)",
+                     static_cast<long long>(T));
+  return MOE_OK;
+}
+
+}  // namespace
+
+bool ws_layout(const moe_shape& sh, int64_t max_n, WsLayout* L) {
+  if (max_n < 1) max_n = 1;
+  const int64_t E = sh.n_experts, k = sh.top_k, d = sh.d, I = sh.inter, Is = sh.inter_shared;
+  const size_t elt = elt_bytes(sh.dtype);
+  const int64_t rows = max_n * k;
+  const int64_t nb = (max_n + kTokBlock - 1) / kTokBlock;
+  const int64_t max_mt = rows / kBM + std::min<int64_t>(E, rows);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += align_up(bytes);
+    return o;
+  };
+  L->wtab = take(sizeof(void*) * E);
+  L->blk_counts = take(sizeof(int32_t) * nb * E);
+  L->blk_base = take(sizeof(int32_t) * nb * E);
+  L->counts = take(sizeof(int32_t) * E);
+  L->offsets = take(sizeof(int32_t) * (E + 1));
+  L->meta = take(sizeof(int32_t) * kMetaWords);
+  L->mtiles = take(sizeof(MTile) * max_mt);
+  L->row_tok = take(sizeof(int32_t) * rows);
+  L->row_slot = take(sizeof(int32_t) * rows);
+  L->h = take(elt * rows * I);
+  L->h_shared = take(elt * max_n * Is);
+  L->y = take(sizeof(float) * rows * d);
+  L->s = take(Is ? sizeof(float) * max_n * d : 0);
+  L->total = off;
+  L->max_n = max_n;
+  L->max_rows = rows;
+  L->max_mtiles = max_mt;
+  L->n_blocks = nb;
+  return true;
+}
+
+}  // namespace moe
+
+using moe::set_error;
+
+extern "C" {
+
+int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "MOE_OK";
+    case MOE_ERR_INVALID: return "MOE_ERR_INVALID";
+    case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+    case MOE_ERR_RING: return "MOE_ERR_RING";
+    case MOE_ERR_HIP: return "MOE_ERR_HIP";
+    case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+const char* moe_last_error(void) { return moe::last_error_text(); }
+
+size_t moe_workspace_bytes(const moe_shape* shape, int64_t max_chunk_tokens) {
+  if (moe::check_shape(shape) != MOE_OK || max_chunk_tokens < 0) return 0;
+  if (max_chunk_tokens > (int64_t{1} << 31) / shape->top_k - 1) return 0;
+  moe::WsLayout L;
+  moe::ws_layout(*shape, max_chunk_tokens, &L);
+  return L.total;
+}
+
+moe_status moe_workspace_offsets(const moe_shape* shape, int64_t n, moe_ws_offsets* out) {
+  moe::clear_error();
+  moe_status st = moe::check_shape(shape);
+  if (st != MOE_OK) return st;
+  if (!out || n < 0 || n > (int64_t{1} << 31) / shape->top_k - 1)
+    return set_error(MOE_ERR_INVALID, "bad arguments");
+  moe::WsLayout L;
+  moe::ws_layout(*shape, n, &L);
+  out->counts = L.counts;
+  out->offsets = L.offsets;
+  out->row_tok = L.row_tok;
+  out->row_slot = L.row_slot;
+  out->total = L.total;
+  return MOE_OK;
+}
+
+moe_status moe_prefill_route(const moe_layer* layer, const void* x, int64_t T, int64_t chunk,
+                             int32_t* ids, float* weights, int32_t* chunk_counts, float* logits,
+                             void* stream) {
+  moe::clear_error();
+  moe_status st = moe::check_layer(layer);
+  if (st != MOE_OK) return st;
+  if ((st = moe::check_rows(T, layer->shape)) != MOE_OK) return st;
+  if (chunk < 1) return set_error(MOE_ERR_INVALID, "chunk=%lld", static_cast<long long>(chunk));
+  if (T == 0) return MOE_OK;
+  if (!x || !ids || !weights || !chunk_counts || !logits)
+    return set_error(MOE_ERR_INVALID, "NULL tensor argument");
+  if (!moe::aligned(x, 16) || !moe::aligned(ids, 4) || !moe::aligned(weights, 4) ||
+      !moe::aligned(chunk_counts, 4) || !moe::aligned(logits, 4))
+    return set_error(MOE_ERR_INVALID, "misaligned tensor argument");
+  return moe::route_impl(layer, x, T, chunk, ids, weights, chunk_counts, logits,
+                         static_cast<hipStream_t>(stream));
+}
+
+moe_status moe_prefill_chunk(const moe_layer* layer, const void* x, const int32_t* ids,
+                             const float* weights, int64_t T, int64_t t0, int64_t n,
+                             const int32_t* counts_host, void* out, void* ws, size_t ws_bytes,
+                             void* stream, void* copy_stream) {
+  moe::clear_error();
+  moe_status st = moe::check_layer(layer);
+  if (st != MOE_OK) return st;
+  if ((st = moe::check_rows(T, layer->shape)) != MOE_OK) return st;
+  if (t0 < 0 || n < 0 || t0 + n > T)
+    return set_error(MOE_ERR_INVALID, "rows [%lld, %lld) outside [0, %lld)",
+                     static_cast<long long>(t0), static_cast<long long>(t0 + n),
+                     static_cast<long long>(T));
+  bool offloaded = false;
+  if ((st = moe::check_experts(layer, &offloaded)) != MOE_OK) return st;
+  if (n == 0) return MOE_OK;
+  if (!x || !ids || !weights || !out || !ws)
+    return set_error(MOE_ERR_INVALID, "NULL tensor argument");
+  if (!moe::aligned(x, 16) || !moe::aligned(out, 16) || !moe::aligned(ids, 4) ||
+      !moe::aligned(weights, 4) || !moe::aligned(ws, 256))
+    return set_error(MOE_ERR_INVALID, "misaligned tensor argument (ws needs 256 bytes)");
+  return moe::chunk_impl(layer, offloaded, x, ids, weights, t0, n, counts_host, out, ws,
+                         ws_bytes, static_cast<hipStream_t>(stream),
+                         static_cast<hipStream_t>(copy_stream));
+}
+
+moe_status moe_prefill_layer(const moe_layer* layer, const void* x, int64_t T, int64_t chunk,
+                             int32_t* ids, float* weights, int32_t* chunk_counts, float* logits,
+                             void* out, void* ws, size_t ws_bytes, void* stream,
+                             void* copy_stream) {
+  moe::clear_error();
+  moe_status st = moe::check_layer(layer);
+  if (st != MOE_OK) return st;
+  if ((st = moe::check_rows(T, layer->shape)) != MOE_OK) return st;
+  if (chunk < 1) return set_error(MOE_ERR_INVALID, "chunk=%lld", static_cast<long long>(chunk));
+  bool offloaded = false;
+  if ((st = moe::check_experts(layer, &offloaded)) != MOE_OK) return st;
+  if (T == 0) return MOE_OK;
+  if (!x || !ids || !weights || !chunk_counts || !logits || !out || !ws)
+    return set_error(MOE_ERR_INVALID, "NULL tensor argument");
+  if (!moe::aligned(x, 16) || !moe::aligned(out, 16) || !moe::aligned(ids, 4) ||
+      !moe::aligned(weights, 4) || !moe::aligned(chunk_counts, 4) ||
+      !moe::aligned(logits, 4) || !moe::aligned(ws, 256))
+    return set_error(MOE_ERR_INVALID, "misaligned tensor argument (ws needs 256 bytes)");
+  const int64_t cmax = std::min(chunk, T);
+  const size_t need = moe_workspace_bytes(&layer->shape, cmax);
+  if (ws_bytes < need)
+    return set_error(MOE_ERR_WORKSPACE, "workspace %zu bytes, %zu needed for chunk %lld",
+                     ws_bytes, need, static_cast<long long>(cmax));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipStream_t cs = static_cast<hipStream_t>(copy_stream);
+  if ((st = moe::route_impl(layer, x, T, chunk, ids, weights, chunk_counts, logits, s)) !=
+      MOE_OK)
+    return st;
+  const int E = layer->shape.n_experts;
+  const int64_t n_chunks = (T + chunk - 1) / chunk;
+  std::vector<int32_t> hc;
+  if (offloaded) {             // one device-to-host copy of every chunk's expert counts
+    hc.resize(static_cast<size_t>(n_chunks) * E);
+    hipError_t err = hipMemcpyAsync(hc.data(), chunk_counts, hc.size() * sizeof(int32_t),
+                                    hipMemcpyDeviceToHost, s);
+    if (err == hipSuccess) err = hipStreamSynchronize(s);
+    if (err != hipSuccess)
+      return set_error(MOE_ERR_HIP, "chunk counts to host: %s", hipGetErrorString(err));
+  }
+  for (int64_t c = 0; c < n_chunks; ++c) {
+    const int64_t t0 = c * chunk;
+    const int64_t n = std::min(chunk, T - t0);
+    st = moe::chunk_impl(layer, offloaded, x, ids, weights, t0, n,
+                         offloaded ? hc.data() + c * E : nullptr, out, ws, ws_bytes, s, cs);
+    if (st != MOE_OK) return st;
+  }
+  return MOE_OK;
+}
+
+moe_status moe_add_rmsnorm(const void* x, const void* delta, int64_t T, int32_t d,
+                           int32_t dtype, float eps, void* x_out, void* normed, void* stream) {
+  moe::clear_error();
+  if (T < 0 || d < 1 || d > (1 << 20)) return set_error(MOE_ERR_INVALID, "T or d out of range");
+  if (dtype != MOE_BF16 && dtype != MOE_F32) return set_error(MOE_ERR_INVALID, "dtype");
+  if (!(eps >= 0.0f)) return set_error(MOE_ERR_INVALID, "eps must be >= 0");
+  if (T == 0) return MOE_OK;
+  if (!x || !normed || (delta && !x_out))
+    return set_error(MOE_ERR_INVALID, "NULL tensor argument");
+  MOE_HIP(moe::launch_add_rmsnorm(dtype, x, delta, T, d, eps, x_out, normed,
+                                  static_cast<hipStream_t>(stream)));
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,193 @@
+// Bucketing of one chunk's token-slots by expert, on the GPU: per-block histogram, one scan
+// kernel (block bases, expert offsets, M-tile list) and a stable permute. The pages build
+// these per-expert member lists on the CPU ("EXL3 on upstream", PR #1113, "Latest prefill
+// efficiency candidate"); here they never leave the device, so the resident path needs no
+// host synchronisation.
+//
+// Row order inside an expert is token order (a stable permute), so the member list of each
+// expert is unique and the whole bucketing is reproducible bit for bit.
+#include <algorithm>
+
+#include "device_common.h"
+#include "moe_internal.h"
+#include "profile.h"
+
+namespace moe {
+namespace {
+
+constexpr int kMaxE = 1024;
+
+// blk_counts[b][e] = slots of tokens [b*256, b*256+256) routed to e (LDS histogram).
+__global__ __launch_bounds__(kTokBlock) void block_hist_kernel(const int32_t* __restrict__ ids,
+                                                               int64_t n, int k, int E,
+                                                               int32_t* __restrict__ blk_counts) {
+  __shared__ int32_t hist[kMaxE];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kTokBlock) hist[e] = 0;
+  __syncthreads();
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokBlock + tid;
+  if (t < n)
+    for (int j = 0; j < k; ++j) atomicAdd(&hist[ids[t * k + j]], 1);
+  __syncthreads();
+  int32_t* out = blk_counts + static_cast<int64_t>(blockIdx.x) * E;
+  for (int e = tid; e < E; e += kTokBlock) out[e] = hist[e];
+}
+
+// One workgroup of 1024 threads; thread e owns expert e.
+//   blk_base[b][e] = slots of e in blocks before b; counts[e]; offsets = exclusive scan of
+//   counts; M-tiles: expert e contributes ceil(counts[e]/kBM) tiles (e, 0), (e, kBM), ... at
+//   position (exclusive scan of the tile counts); meta = {number of tiles, number of rows}.
+__global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ blk_counts,
+                                                    int nb, int E,
+                                                    int32_t* __restrict__ blk_base,
+                                                    int32_t* __restrict__ counts,
+                                                    int32_t* __restrict__ offsets,
+                                                    MTile* __restrict__ mtiles,
+                                                    int32_t* __restrict__ meta) {
+  __shared__ int32_t s_rows[kMaxE];
+  __shared__ int32_t s_tiles[kMaxE];
+  const int e = threadIdx.x;
+  int32_t run = 0;
+  if (e < E) {
+    for (int b = 0; b < nb; ++b) {
+      const int64_t i = static_cast<int64_t>(b) * E + e;
+      blk_base[i] = run;
+      run += blk_counts[i];
+    }
+    counts[e] = run;
+  }
+  const int32_t ntile = static_cast<int32_t>((run + kBM - 1) / kBM);
+  s_rows[e] = run;
+  s_tiles[e] = ntile;
+  __syncthreads();
+  for (int off = 1; off < kMaxE; off <<= 1) {    // inclusive Hillis-Steele scans
+    const int32_t a = e >= off ? s_rows[e - off] : 0;
+    const int32_t b = e >= off ? s_tiles[e - off] : 0;
+    __syncthreads();
+    s_rows[e] += a;
+    s_tiles[e] += b;
+    __syncthreads();
+  }
+  const int32_t row_off = s_rows[e] - run;
+  const int32_t tile_off = s_tiles[e] - ntile;
+  if (e < E) {
+    offsets[e] = row_off;
+    for (int i = 0; i < ntile; ++i) mtiles[tile_off + i] = MTile{e, i * kBM};
+  }
+  if (e == kMaxE - 1) {
+    offsets[E] = s_rows[e];
+    meta[kMetaMTiles] = s_tiles[e];
+    meta[kMetaRows] = s_rows[e];
+  }
+}
+
+// Stable permute. Block b (tokens [b*256, b*256+256)) marks, per expert, which of its tokens
+// chose that expert in a 256-bit LDS mask; a token's rank among the block's tokens of expert
+// e is the number of marked tokens before it. Row = offsets[e] + blk_base[b][e] + rank.
+__global__ __launch_bounds__(kTokBlock) void permute_kernel(const int32_t* __restrict__ ids,
+                                                            int64_t n, int k, int E,
+                                                            const int32_t* __restrict__ blk_base,
+                                                            const int32_t* __restrict__ offsets,
+                                                            int32_t* __restrict__ row_tok,
+                                                            int32_t* __restrict__ row_slot) {
+  __shared__ uint32_t mask[kMaxE * (kTokBlock / 32)];
+  const int tid = threadIdx.x;
+  for (int w = tid; w < E * (kTokBlock / 32); w += kTokBlock) mask[w] = 0u;
+  __syncthreads();
+  const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokBlock + tid;
+  const bool valid = t < n;
+  const int word = tid >> 5;
+  const uint32_t bit = 1u << (tid & 31);
+  if (valid)
+    for (int j = 0; j < k; ++j) atomicOr(&mask[ids[t * k + j] * (kTokBlock / 32) + word], bit);
+  __syncthreads();
+  if (!valid) return;
+  const int32_t* base = blk_base + static_cast<int64_t>(blockIdx.x) * E;
+  for (int j = 0; j < k; ++j) {
+    const int e = ids[t * k + j];
+    const uint32_t* m = mask + e * (kTokBlock / 32);
+    int rank = __popc(m[word] & (bit - 1u));
+    for (int w = 0; w < word; ++w) rank += __popc(m[w]);
+    const int64_t r = static_cast<int64_t>(offsets[e]) + base[e] + rank;
+    row_tok[r] = static_cast<int32_t>(t);
+    row_slot[r] = static_cast<int32_t>(t * k + j);
+  }
+}
+
+struct PtrPairs {                 // kernel-argument batch of table entries
+  int32_t n;
+  int32_t idx[128];
+  const void* ptr[128];
+};
+
+__global__ void upload_ptrs_kernel(const void** table, PtrPairs b) {
+  const int i = threadIdx.x;
+  if (i < b.n) table[b.idx[i]] = b.ptr[i];
+}
+
+}  // namespace
+
+hipError_t launch_upload_ptrs(const void** table, const void* const* src, int first, int n,
+                              hipStream_t s) {
+  ProfScope prof(MOE_STAGE_TABLE, s);
+  for (int i0 = 0; i0 < n; i0 += 128) {
+    PtrPairs b{};
+    b.n = std::min(128, n - i0);
+    for (int i = 0; i < b.n; ++i) {
+      b.idx[i] = first + i0 + i;
+      b.ptr[i] = src[i0 + i];
+    }
+    upload_ptrs_kernel<<<1, 128, 0, s>>>(table, b);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_upload_pairs(const void** table, const int32_t* idx, const void* const* ptr,
+                               int n, hipStream_t s) {
+  ProfScope prof(MOE_STAGE_TABLE, s);
+  for (int i0 = 0; i0 < n; i0 += 128) {
+    PtrPairs b{};
+    b.n = std::min(128, n - i0);
+    for (int i = 0; i < b.n; ++i) {
+      b.idx[i] = idx[i0 + i];
+      b.ptr[i] = ptr[i0 + i];
+    }
+    upload_ptrs_kernel<<<1, 128, 0, s>>>(table, b);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_bucket(const int32_t* ids_chunk, int64_t n, int k, int E, char* ws,
+                         const WsLayout& L, hipStream_t s) {
+  const int nb = static_cast<int>((n + kTokBlock - 1) / kTokBlock);
+  int32_t* blk_counts = reinterpret_cast<int32_t*>(ws + L.blk_counts);
+  int32_t* blk_base = reinterpret_cast<int32_t*>(ws + L.blk_base);
+  int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+  int32_t* meta = reinterpret_cast<int32_t*>(ws + L.meta);
+  MTile* mtiles = reinterpret_cast<MTile*>(ws + L.mtiles);
+  hipError_t err;
+  {
+    ProfScope prof(MOE_STAGE_HIST, s);
+    block_hist_kernel<<<nb, kTokBlock, 0, s>>>(ids_chunk, n, k, E, blk_counts);
+    err = hipGetLastError();
+  }
+  if (err != hipSuccess) return err;
+  {
+    ProfScope prof(MOE_STAGE_SCAN, s);
+    scan_kernel<<<1, 1024, 0, s>>>(blk_counts, nb, E, blk_base, counts, offsets, mtiles, meta);
+    err = hipGetLastError();
+  }
+  if (err != hipSuccess) return err;
+  ProfScope prof(MOE_STAGE_PERMUTE, s);
+  permute_kernel<<<nb, kTokBlock, 0, s>>>(ids_chunk, n, k, E, blk_base, offsets,
+                                          reinterpret_cast<int32_t*>(ws + L.row_tok),
+                                          reinterpret_cast<int32_t*>(ws + L.row_slot));
+  return hipGetLastError();
+}
+
+}  // namespace moe

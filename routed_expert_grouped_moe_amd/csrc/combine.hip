@@ -1,0 +1,134 @@
+// The combine (one fixed reduction order per token) and the RMSNorm + residual glue of a stack.
+#include <math.h>
+
+#include "device_common.h"
+#include "moe_internal.h"
+#include "profile.h"
+
+namespace moe {
+namespace {
+
+template <typename T> struct Pack4;
+template <> struct Pack4<uint16_t> {
+  static __device__ __forceinline__ void store(uint16_t* p, float4 v) {
+    uint2 w;
+    w.x = static_cast<uint32_t>(f32_to_bf16(v.x)) | (static_cast<uint32_t>(f32_to_bf16(v.y)) << 16);
+    w.y = static_cast<uint32_t>(f32_to_bf16(v.z)) | (static_cast<uint32_t>(f32_to_bf16(v.w)) << 16);
+    *reinterpret_cast<uint2*>(p) = w;
+  }
+  static __device__ __forceinline__ float4 load(const uint16_t* p) {
+    const uint2 w = *reinterpret_cast<const uint2*>(p);
+    return make_float4(bf16_to_f32(w.x & 0xffffu), bf16_to_f32(w.x >> 16),
+                       bf16_to_f32(w.y & 0xffffu), bf16_to_f32(w.y >> 16));
+  }
+};
+template <> struct Pack4<float> {
+  static __device__ __forceinline__ void store(float* p, float4 v) {
+    *reinterpret_cast<float4*>(p) = v;
+  }
+  static __device__ __forceinline__ float4 load(const float* p) {
+    return *reinterpret_cast<const float4*>(p);
+  }
+};
+
+// The canonical reduction of one token (the routed-expert reduction the exact deep prefill
+// page, "Flash Next EXL3: exact deep prefill", adopts so chunk size cannot change a sum):
+//   acc = 0; for each chosen expert in ascending id: acc = fma(w_j, y_j, acc); acc += shared;
+//   out = round(acc)    (one rounding to the storage type, bf16 round-to-nearest-even)
+// y_j is the unweighted fp32 row expert j wrote for this token; the order never depends on
+// the chunk, the expert's row count or where the expert ran.
+template <typename T>
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
+                                                      const float* __restrict__ shared,
+                                                      const float* __restrict__ weights,
+                                                      int64_t t0, int k, int d,
+                                                      T* __restrict__ out) {
+  const int64_t t = blockIdx.x;                       // token within the chunk
+  const float* wt = weights + (t0 + t) * k;
+  const float* yt = y + t * k * static_cast<int64_t>(d);
+  for (int c = threadIdx.x * 4; c < d; c += 1024) {
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+      const float wj = wt[j];
+      const float4 v = *reinterpret_cast<const float4*>(yt + static_cast<int64_t>(j) * d + c);
+      acc.x = fmaf(wj, v.x, acc.x);
+      acc.y = fmaf(wj, v.y, acc.y);
+      acc.z = fmaf(wj, v.z, acc.z);
+      acc.w = fmaf(wj, v.w, acc.w);
+    }
+    if (shared) {
+      const float4 s = *reinterpret_cast<const float4*>(shared + t * d + c);
+      acc.x += s.x;
+      acc.y += s.y;
+      acc.z += s.z;
+      acc.w += s.w;
+    }
+    Pack4<T>::store(out + (t0 + t) * d + c, acc);
+  }
+}
+
+// x_new = round(x + delta) (when delta is given); normed = round(x_new / sqrt(mean(x_new^2) +
+// eps)). Each thread sums squares of columns tid, tid + 256, ... in order, then a fixed
+// halving tree over the 256 partial sums: the same bits on every run.
+template <typename T>
+__global__ __launch_bounds__(256) void add_rmsnorm_kernel(const T* __restrict__ x,
+                                                          const T* __restrict__ delta, int d,
+                                                          float eps, T* x_out,
+                                                          T* __restrict__ normed) {
+  __shared__ float red[256];
+  const int tid = threadIdx.x;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * d;
+  float ss = 0.f;
+  for (int c = tid; c < d; c += 256) {
+    float v = Elt<T>::load(x[row + c]);
+    if (delta) {
+      const T r = Elt<T>::store(v + Elt<T>::load(delta[row + c]));
+      x_out[row + c] = r;
+      v = Elt<T>::load(r);
+    }
+    ss = fmaf(v, v, ss);
+  }
+  red[tid] = ss;
+  __syncthreads();
+  for (int s = 128; s > 0; s >>= 1) {
+    if (tid < s) red[tid] += red[tid + s];
+    __syncthreads();
+  }
+  const float inv = 1.0f / sqrtf(red[0] / static_cast<float>(d) + eps);
+  for (int c = tid; c < d; c += 256) {
+    const float v = Elt<T>::load(delta ? x_out[row + c] : x[row + c]);
+    normed[row + c] = Elt<T>::store(v * inv);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_combine(int dtype, const float* y, const float* shared, const float* weights,
+                          int64_t t0, int64_t n, int k, int d, void* out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  ProfScope prof(MOE_STAGE_COMBINE, s);
+  if (dtype == MOE_BF16)
+    combine_kernel<uint16_t><<<static_cast<unsigned>(n), 256, 0, s>>>(
+        y, shared, weights, t0, k, d, static_cast<uint16_t*>(out));
+  else
+    combine_kernel<float><<<static_cast<unsigned>(n), 256, 0, s>>>(
+        y, shared, weights, t0, k, d, static_cast<float*>(out));
+  return hipGetLastError();
+}
+
+hipError_t launch_add_rmsnorm(int dtype, const void* x, const void* delta, int64_t T, int d,
+                              float eps, void* x_out, void* normed, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  ProfScope prof(MOE_STAGE_RMSNORM, s);
+  if (dtype == MOE_BF16)
+    add_rmsnorm_kernel<uint16_t><<<static_cast<unsigned>(T), 256, 0, s>>>(
+        static_cast<const uint16_t*>(x), static_cast<const uint16_t*>(delta), d, eps,
+        static_cast<uint16_t*>(x_out), static_cast<uint16_t*>(normed));
+  else
+    add_rmsnorm_kernel<float><<<static_cast<unsigned>(T), 256, 0, s>>>(
+        static_cast<const float*>(x), static_cast<const float*>(delta), d, eps,
+        static_cast<float*>(x_out), static_cast<float*>(normed));
+  return hipGetLastError();
+}
+
+}  // namespace moe

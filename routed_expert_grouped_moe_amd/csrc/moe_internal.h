@@ -1,0 +1,90 @@
+// Internal declarations shared by the HIP translation units of libmoeprefill.
+// Not part of the ABI: the exported surface is include/moe_prefill.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe_prefill.h"
+
+#define MOE_HIDDEN __attribute__((visibility("hidden")))
+
+namespace moe {
+
+// ------------------------------------------------------------------ GEMM tiling constants
+// One workgroup computes a 128 x 128 output tile with 4 waves (2 x 2, 64 x 64 each) on
+// 16x16 MFMA blocks; K advances 128 bytes per stage (64 bf16 or 32 fp32 elements).
+constexpr int kBM = 128;          // rows of a tile (token rows)
+constexpr int kBN = 128;          // columns of a tile (weight rows)
+constexpr int kGuHCols = 64;      // h columns per gate/up tile (64 gate + 64 up weight rows)
+constexpr int kThreads = 256;
+constexpr int kTokBlock = 256;    // tokens per block of the bucketing kernels
+
+// ------------------------------------------------------------------ device-side records
+struct MTile {                    // one M-tile of a routed expert: rows [m0, m0+kBM) of group g
+  int32_t group;
+  int32_t m0;
+};
+
+// Workspace layout for chunks of up to max_n tokens (all offsets 256-byte aligned).
+struct WsLayout {
+  size_t wtab, blk_counts, blk_base, counts, offsets, meta, mtiles, row_tok, row_slot;
+  size_t h, h_shared, y, s, total;
+  int64_t max_n, max_rows, max_mtiles, n_blocks;
+};
+MOE_HIDDEN bool ws_layout(const moe_shape& sh, int64_t max_n, WsLayout* out);
+
+// meta words in the workspace
+enum { kMetaMTiles = 0, kMetaRows = 1, kMetaWords = 64 };
+
+// ------------------------------------------------------------------ launch wrappers
+// (each returns hipGetLastError() after its launches)
+MOE_HIDDEN hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s);
+
+MOE_HIDDEN hipError_t launch_router_gemm(int dtype, const void* x, const void* w_router,
+                                         const float* bias, int64_t T, int d, int E,
+                                         float* logits, hipStream_t s);
+MOE_HIDDEN hipError_t launch_topk(const float* logits, int64_t T, int E, int k, int32_t* ids,
+                                  float* weights, hipStream_t s);
+MOE_HIDDEN hipError_t launch_chunk_hist(const int32_t* ids, int64_t T, int k, int E,
+                                        int64_t chunk, int32_t* chunk_counts, hipStream_t s);
+
+MOE_HIDDEN hipError_t launch_upload_ptrs(const void** dst_table, const void* const* src,
+                                         int first, int n, hipStream_t s);
+MOE_HIDDEN hipError_t launch_upload_pairs(const void** table, const int32_t* idx,
+                                         const void* const* ptr, int n, hipStream_t s);
+MOE_HIDDEN hipError_t launch_bucket(const int32_t* ids_chunk, int64_t n, int k, int E,
+                                    char* ws, const WsLayout& L, hipStream_t s);
+
+struct GemmGroups {               // routed (grouped) problem description
+  const MTile* mtiles;
+  const int32_t* n_mtiles;        // device scalar
+  const int32_t* offsets;         // [E+1]
+  const int32_t* counts;          // [E]
+  const void* const* wtab;        // [E] expert line pointers
+  int tile_lo;                    // first M-tile of this launch
+  int tile_cap;                   // grid rows (M-tiles) of this launch
+};
+
+MOE_HIDDEN hipError_t launch_gu_routed(int dtype, const void* x, int64_t t0, int d, int I,
+                                       const GemmGroups& g, const int32_t* row_tok, void* h,
+                                       hipStream_t s);
+MOE_HIDDEN hipError_t launch_gu_dense(int dtype, const void* x, int64_t t0, int64_t n, int d,
+                                      int Is, const void* w_gu, void* h, hipStream_t s);
+MOE_HIDDEN hipError_t launch_down_routed(int dtype, const void* h, int d, int I,
+                                         const GemmGroups& g, const int32_t* row_slot,
+                                         float* y, hipStream_t s);
+MOE_HIDDEN hipError_t launch_down_dense(int dtype, const void* h, int64_t n, int d, int Is,
+                                        const void* w_down, float* out, hipStream_t s);
+MOE_HIDDEN hipError_t launch_combine(int dtype, const float* y, const float* shared,
+                                     const float* weights, int64_t t0, int64_t n, int k, int d,
+                                     void* out, hipStream_t s);
+MOE_HIDDEN hipError_t launch_add_rmsnorm(int dtype, const void* x, const void* delta,
+                                         int64_t T, int d, float eps, void* x_out,
+                                         void* normed, hipStream_t s);
+
+// number of M-tiles of a group with c rows
+inline int64_t mtiles_of(int64_t c) { return (c + kBM - 1) / kBM; }
+
+}  // namespace moe

@@ -1,0 +1,98 @@
+// Opt-in per-stage kernel timing with HIP events recorded on each launch's own stream.
+#include <mutex>
+#include <vector>
+
+#include "profile.h"
+#include "ring.h"
+
+namespace moe {
+namespace {
+
+struct Pending {
+  int stage;
+  hipEvent_t a, b;
+};
+
+std::mutex g_mu;
+bool g_on = false;
+std::vector<Pending> g_pending;
+std::vector<hipEvent_t> g_pool;
+double g_ms[16];
+int64_t g_n[16];
+
+hipEvent_t take_event() {   // caller holds g_mu
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+}  // namespace
+
+ProfScope::ProfScope(int stage, hipStream_t s) : stage_(stage), s_(s) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_on) return;
+  a_ = take_event();
+  if (a_ && hipEventRecord(a_, s_) != hipSuccess) {
+    g_pool.push_back(a_);
+    a_ = nullptr;
+  }
+}
+
+ProfScope::~ProfScope() {
+  if (!a_) return;
+  std::lock_guard<std::mutex> lk(g_mu);
+  hipEvent_t b = take_event();
+  if (b && hipEventRecord(b, s_) == hipSuccess) {
+    g_pending.push_back({stage_, a_, b});
+  } else {
+    g_pool.push_back(a_);
+    if (b) g_pool.push_back(b);
+  }
+}
+
+}  // namespace moe
+
+extern "C" {
+
+moe_status moe_profile_enable(int32_t on) {
+  std::lock_guard<std::mutex> lk(moe::g_mu);
+  moe::g_on = on != 0;
+  return MOE_OK;
+}
+
+moe_status moe_profile_read(moe_profile_t* out, int32_t reset) {
+  moe::clear_error();
+  if (!out) return moe::set_error(MOE_ERR_INVALID, "out is NULL");
+  std::lock_guard<std::mutex> lk(moe::g_mu);
+  moe_status st = MOE_OK;
+  for (const moe::Pending& p : moe::g_pending) {
+    float ms = 0.f;
+    hipError_t err = hipEventSynchronize(p.b);
+    if (err == hipSuccess) err = hipEventElapsedTime(&ms, p.a, p.b);
+    if (err != hipSuccess && st == MOE_OK)
+      st = moe::set_error(MOE_ERR_HIP, "profile events: %s", hipGetErrorString(err));
+    moe::g_ms[p.stage] += ms;
+    moe::g_n[p.stage] += 1;
+    moe::g_pool.push_back(p.a);
+    moe::g_pool.push_back(p.b);
+  }
+  moe::g_pending.clear();
+  out->version = 1;
+  out->n_stages = MOE_STAGE_COUNT;
+  for (int i = 0; i < 16; ++i) {
+    out->ms[i] = moe::g_ms[i];
+    out->launches[i] = moe::g_n[i];
+    if (reset) {
+      moe::g_ms[i] = 0.0;
+      moe::g_n[i] = 0;
+    }
+  }
+  return st;
+}
+
+}  // extern "C"

@@ -1,0 +1,63 @@
+// Host-side state of a ring of device expert lines (the opaque moe_ring of the ABI).
+#pragma once
+
+#include <unordered_map>
+#include <vector>
+
+#include "moe_internal.h"
+
+struct moe_ring {
+  struct Line {
+    int32_t layer = -1;           // (layer, expert) held, or -1
+    int32_t expert = -1;
+    uint64_t last_use = 0;        // LRU clock of the last staging that used the line
+    bool held = false;            // handed out by a staging call, not yet released
+    bool has_ready = false;       // `ready` has been recorded at least once
+    bool has_release = false;     // `release` has been recorded at least once
+    uint64_t release_seq = 0;     // release epoch (per ring, increasing in record order)
+    hipStream_t release_stream = nullptr;
+  };
+  struct Bank {
+    const char* base = nullptr;
+    std::vector<int32_t> slot;    // bank slot of each expert, -1 = resident
+  };
+
+  moe_shape shape{};
+  size_t line_bytes = 0;
+  char* lines = nullptr;
+  int32_t n_lines = 0;
+  std::vector<Line> line;
+  std::vector<hipEvent_t> ready, release;
+  std::unordered_map<int64_t, int32_t> where;   // (layer << 32 | expert) -> line
+  std::unordered_map<int32_t, Bank> banks;
+  uint64_t clock = 0;
+  uint64_t release_counter = 0;
+  // Release-epoch coalescing: the copy stream `coal_copy` has already waited for every
+  // release recorded on `coal_rel` up to epoch `waited_seq`, so older releases need no wait.
+  hipStream_t coal_rel = nullptr, coal_copy = nullptr;
+  uint64_t waited_seq = 0;
+  moe_ring_stats_t stats{};
+};
+
+namespace moe {
+
+inline int64_t ring_key(int32_t layer, int32_t expert) {
+  return (static_cast<int64_t>(layer) << 32) | static_cast<uint32_t>(expert);
+}
+
+// Implementations of the ABI calls, used by the chunk sequencer too (no argument checks
+// beyond the ring's own; set the thread's last error on failure).
+MOE_HIDDEN moe_status ring_stage(moe_ring* r, int32_t layer, const int32_t* experts, int32_t n,
+                                 hipStream_t copy_stream, int32_t* lines_out);
+MOE_HIDDEN moe_status ring_wait_ready(moe_ring* r, const int32_t* lines, int32_t n,
+                                      hipStream_t stream);
+MOE_HIDDEN moe_status ring_release(moe_ring* r, const int32_t* lines, int32_t n,
+                                   hipStream_t stream);
+
+// thread-local error text
+MOE_HIDDEN const char* last_error_text();
+MOE_HIDDEN void clear_error();
+MOE_HIDDEN moe_status set_error(moe_status s, const char* fmt, ...)
+    __attribute__((format(printf, 2, 3)));
+
+}  // namespace moe

@@ -1,0 +1,187 @@
+"""HIP path against the fp64 oracle (element by element) and against itself across chunk
+sizes, through the C ABI. Needs an MI355X."""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import oracle.moe_oracle as orc
+from tests.parity import as_f64, oracle_params, place, rel_err, routing_gates
+
+pytestmark = pytest.mark.gpu
+
+BF16_TOL = 2e-2     # max-abs error over output RMS, bf16 outputs
+F32_TOL = 1e-4      # same metric, fp32 storage and arithmetic
+
+
+@pytest.fixture(scope="module")
+def moe():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import routed_expert_grouped_moe_amd as m
+    m.moe_abi_version()
+    return m
+
+
+def bits(t):
+    """Bit patterns of a tensor (compares NaNs and signed zeros exactly)."""
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+def _run(moe, L, x, chunk, **kw):
+    r = moe.moe_prefill_layer(L, x, chunk, **kw)
+    torch.cuda.synchronize()
+    return r
+
+
+def _full_parity(moe, wl, tol, chunks=None):
+    """Whole-layer parity against the oracle plus bit-identity across chunk sizes."""
+    params, L = place(wl)
+    x = mi.make_x(wl, device="cuda")
+    chunks = chunks or wl.chunks
+    outs = {}
+    for c in chunks:
+        outs[c] = _run(moe, L, x, c)
+    base = outs[chunks[-1]]
+    for c in chunks:
+        assert torch.equal(bits(outs[c]["out"]), bits(base["out"])), f"chunk {c}"
+        assert torch.equal(outs[c]["ids"], base["ids"])
+    op = oracle_params(params, wl)
+    xh = mi.to_numpy_exact(x)
+    ref_logits = orc.router_logits(xh, op["w_router"], op["router_bias"])
+    ids_use, ties = routing_gates(base["logits"].cpu().numpy(), base["ids"].cpu().numpy(),
+                                  base["weights"].cpu().numpy(), ref_logits, wl.shape.top_k)
+    for c in chunks:
+        cc = outs[c]["chunk_counts"].cpu().numpy()
+        assert np.array_equal(cc, orc.chunk_counts(outs[c]["ids"].cpu().numpy(), c,
+                                                   wl.shape.n_experts)), f"counts, chunk {c}"
+    ref = orc.moe_layer(xh, op, ids=ids_use)["out"]
+    err = rel_err(as_f64(base["out"]), ref)
+    print(f"{wl.name}: rel err {err:.3e}, near-ties {ties}")
+    assert err <= tol, err
+    return err
+
+
+def test_tiny_fp32(moe):
+    _full_parity(moe, mi.WORKLOADS["tiny_fp32"], F32_TOL, chunks=(40, 7, 1))
+
+
+def test_small_bf16_many_chunks(moe):
+    wl = mi.custom_workload("small", T=300, d=128, E=16, k=4, inter=64, inter_shared=128,
+                            zipf_s=1.1, seed=3)
+    _full_parity(moe, wl, BF16_TOL, chunks=(1, 3, 7, 64, 129, 300))
+
+
+@pytest.mark.parametrize("case", [
+    dict(T=37, d=64, E=1, k=1, inter=64, inter_shared=64),        # a single expert
+    dict(T=50, d=128, E=8, k=8, inter=64, inter_shared=0),         # k = E, no shared expert
+    dict(T=1, d=256, E=32, k=3, inter=128, inter_shared=64),       # one token
+    dict(T=515, d=192, E=200, k=6, inter=192, inter_shared=192),   # E not a multiple of 64/128
+    dict(T=260, d=64, E=1024, k=2, inter=64, inter_shared=0),      # largest E
+])
+def test_edge_shapes(moe, case):
+    wl = mi.custom_workload("edge", seed=11, **case)
+    chunks = (max(1, case["T"] // 3), case["T"])
+    _full_parity(moe, wl, BF16_TOL, chunks=chunks)
+
+
+def test_member_lists_bit_exact(moe):
+    """The GPU's expert-major member lists equal the oracle's, integer for integer."""
+    wl = mi.custom_workload("lists", T=1000, d=128, E=16, k=4, inter=64, inter_shared=64,
+                            zipf_s=1.5, seed=5)
+    params, L = place(wl)
+    x = mi.make_x(wl, device="cuda")
+    sh = L.shape
+    r = moe.moe_prefill_route(L, x, 300)
+    out = torch.empty_like(x)
+    for t0, n in ((0, 300), (300, 300), (900, 100)):
+        ws = torch.empty(moe.moe_workspace_bytes(sh, n), dtype=torch.uint8, device="cuda")
+        moe.moe_prefill_chunk(L, x, r["ids"], r["weights"], t0, n, out, ws)
+        torch.cuda.synchronize()
+        off = moe.moe_workspace_offsets(sh, n)
+        w8 = ws.cpu().numpy()
+        as_i32 = lambda o, cnt: w8[o: o + 4 * cnt].view(np.int32)
+        counts, offsets, row_tok, row_slot = orc.member_lists(
+            r["ids"][t0:t0 + n].cpu().numpy(), sh.n_experts)
+        assert np.array_equal(as_i32(off["counts"], sh.n_experts), counts)
+        assert np.array_equal(as_i32(off["offsets"], sh.n_experts + 1), offsets)
+        assert np.array_equal(as_i32(off["row_tok"], n * sh.top_k), row_tok)
+        assert np.array_equal(as_i32(off["row_slot"], n * sh.top_k), row_slot)
+
+
+def test_repeatable_five_runs(moe):
+    wl = mi.custom_workload("rep", T=700, d=256, E=64, k=6, inter=128, inter_shared=256,
+                            zipf_s=1.1, seed=9)
+    params, L = place(wl)
+    x = mi.make_x(wl, device="cuda")
+    first = _run(moe, L, x, 256)
+    for _ in range(4):
+        again = _run(moe, L, x, 256)
+        assert torch.equal(bits(again["out"]), bits(first["out"]))
+        assert torch.equal(again["logits"], first["logits"])
+        assert torch.equal(again["weights"], first["weights"])
+
+
+def test_row_position_invariance(moe):
+    """A token's bytes do not depend on its position: permuting the prompt permutes the output."""
+    wl = mi.custom_workload("perm", T=333, d=128, E=16, k=4, inter=128, inter_shared=64, seed=4)
+    params, L = place(wl)
+    x = mi.make_x(wl, device="cuda")
+    perm = torch.randperm(wl.T, generator=torch.Generator().manual_seed(0)).cuda()
+    a = _run(moe, L, x, 100)["out"]
+    b = _run(moe, L, x[perm].contiguous(), 64)["out"]
+    assert torch.equal(bits(b), bits(a[perm]))
+
+
+def test_workspace_too_small_leaves_output(moe):
+    wl = mi.custom_workload("ws", T=64, d=128, E=8, k=2, inter=64, inter_shared=64)
+    params, L = place(wl)
+    x = mi.make_x(wl, device="cuda")
+    r = moe.moe_prefill_route(L, x, 64)
+    out = torch.full_like(x, 3.0)
+    ws = torch.empty(moe.moe_workspace_bytes(L.shape, 64) - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(moe.MoeError, match="MOE_ERR_WORKSPACE"):
+        moe.moe_prefill_chunk(L, x, r["ids"], r["weights"], 0, 64, out, ws)
+    torch.cuda.synchronize()
+    assert torch.all(out == 3.0)
+    # a smaller chunk fits the same workspace and gives the same bytes as the batched pass
+    full = _run(moe, L, x, 64)["out"]
+    for t0 in range(0, 64, 32):
+        moe.moe_prefill_chunk(L, x, r["ids"], r["weights"], t0, 32, out, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(out), bits(full))
+
+
+def test_layer_3001(moe):
+    """bf16 layer, T = 3,001, all experts resident: deep chunk 1,024 equals the batched pass
+    bit for bit, and both match the oracle."""
+    _full_parity(moe, mi.WORKLOADS["layer_3001"], BF16_TOL)
+
+
+def test_chunk_gate_4099(moe):
+    """Zipf(1.1)-skewed routing, T = 4,099: chunks 256 / 1,024 / 2,048 and the batched pass
+    give identical bytes."""
+    _full_parity(moe, mi.WORKLOADS["chunk_gate_4099"], BF16_TOL)
+
+
+def test_add_rmsnorm(moe):
+    g = torch.Generator(device="cuda").manual_seed(3)
+    x = torch.randn(77, 2048, device="cuda", generator=g).to(torch.bfloat16)
+    dlt = torch.randn(77, 2048, device="cuda", generator=g).to(torch.bfloat16)
+    xn, nrm = moe.moe_add_rmsnorm(x, dlt, 1e-6)
+    torch.cuda.synchronize()
+    # residual add: one rounding of the exact sum (torch's own bf16 rounding is the reference)
+    want = (x.double() + dlt.double()).to(torch.bfloat16)
+    assert torch.equal(xn.view(torch.int16), want.view(torch.int16))
+    # normed: fp32 arithmetic then one bf16 rounding, so each element is within half a bf16
+    # ulp (2^-9 relative) of the exact value, plus fp32 noise; 2^-8 relative bounds both
+    ref = orc.rmsnorm(as_f64(xn), 1e-6)
+    assert np.all(np.abs(as_f64(nrm) - ref) <= 2.0 ** -8 * np.abs(ref) + 1e-30)
+    # without delta: normalise only; in place form
+    _, n2 = moe.moe_add_rmsnorm(x, None, 1e-6)
+    ref2 = orc.rmsnorm(as_f64(x), 1e-6)
+    assert np.all(np.abs(as_f64(n2) - ref2) <= 2.0 ** -8 * np.abs(ref2) + 1e-30)
+    x2 = x.clone()
+    moe.moe_add_rmsnorm(x2, dlt, 1e-6, x_out=x2)
+    torch.cuda.synchronize()
+    assert torch.equal(x2.view(torch.int16), want.view(torch.int16))

@@ -80,6 +80,15 @@ def time_steps(fn, steps, warmup):
     return a.elapsed_time(b) / steps, wall
 
 
+def copy_probe(nbytes: int, runs: int) -> float:
+    """A plain copy kernel: out = in * 1 over nbytes of fp32 (reads and writes nbytes each)."""
+    import torch
+    a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    ms, _ = time_steps(lambda: torch.mul(a, 1.0, out=b), runs, 1)
+    return 2 * a.numel() * 4 / (ms / 1e3) / 1e9
+
+
 def cpu_baseline(params, wl, x, n_tokens):
     import numpy as np
     from threadpoolctl import threadpool_info
@@ -111,6 +120,9 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run a plain fp32 copy kernel (out = in * 1) over BYTES bytes "
+                         "5 times and print its bandwidth (calibrates HBM byte counters)")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -127,6 +139,11 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_probe:
+        gbps = copy_probe(args.copy_probe, 5)
+        print(json.dumps({"copy_probe_bytes": args.copy_probe, "runs": 5,
+                          "read_plus_write_gbps": round(gbps, 1)}), flush=True)
+        return
     wl = mi.WORKLOADS["offload_16022"]      # T = 16,022 inputs (seeded), placed resident here
     T = wl.T
     log(f"[bench] generating layer and {T} tokens on cuda:0")
@@ -211,6 +228,7 @@ def main():
         del br, Lr
         ring.close()
 
+    copy_gbps = copy_probe(1 << 30, 5)
     cpu = None
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline on {args.cpu_sample_tokens} tokens")
@@ -228,6 +246,7 @@ def main():
         "tflops": round(tflops, 2), "mfma_frac": round(tflops * 1e12 / PEAK_BF16, 4),
         "grouped_gemm_mfma_frac": round(gemm_flop / (gemm_ms / 1e3) / PEAK_BF16, 4),
         "wall_ms_per_step": round(wall_ms, 4), "ms_per_step_profiled": round(ms_prof, 4),
+        "hbm_copy_gbps_measured": round(copy_gbps, 1),
         "roofline": roof, "cpu_baseline": cpu, "kernels": kernels, "variants": variants,
     }
     print(json.dumps(line), flush=True)

@@ -126,8 +126,9 @@ moe_status ring_waves(const moe_layer* L, const void* x, int64_t t0, int64_t n,
   if (total != n * k)
     return set_error(MOE_ERR_INVALID, "expert counts sum to %lld, chunk has %lld slots",
                      static_cast<long long>(total), static_cast<long long>(n * k));
+  const int bm = routed_tile_rows(n, k, E);
   std::vector<int64_t> mt_begin(E + 1, 0);
-  for (int e = 0; e < E; ++e) mt_begin[e + 1] = mt_begin[e] + mtiles_of(cnt[e]);
+  for (int e = 0; e < E; ++e) mt_begin[e + 1] = mt_begin[e] + mtiles_of(cnt[e], bm);
 
   std::vector<int32_t> used;
   for (int e = 0; e < E; ++e)
@@ -149,7 +150,7 @@ moe_status ring_waves(const moe_layer* L, const void* x, int64_t t0, int64_t n,
   GemmGroups g{reinterpret_cast<const MTile*>(ws + W.mtiles),
                reinterpret_cast<const int32_t*>(ws + W.meta) + kMetaMTiles,
                reinterpret_cast<const int32_t*>(ws + W.offsets),
-               reinterpret_cast<const int32_t*>(ws + W.counts), wtab, 0, 0};
+               reinterpret_cast<const int32_t*>(ws + W.counts), wtab, 0, 0, bm};
   const int32_t* row_tok = reinterpret_cast<const int32_t*>(ws + W.row_tok);
   const int32_t* row_slot = reinterpret_cast<const int32_t*>(ws + W.row_slot);
   char* h = ws + W.h;
@@ -204,7 +205,8 @@ moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const i
   char* ws = static_cast<char*>(ws_v);
   const void** wtab = reinterpret_cast<const void**>(ws + W.wtab);
   MOE_HIP(launch_upload_ptrs(wtab, L->expert_lines, 0, E, s));
-  MOE_HIP(launch_bucket(ids + t0 * k, n, k, E, ws, W, s));
+  const int bm = routed_tile_rows(n, k, E);
+  MOE_HIP(launch_bucket(ids + t0 * k, n, k, E, bm, ws, W, s));
   float* sbuf = sh.inter_shared ? reinterpret_cast<float*>(ws + W.s) : nullptr;
   if (sh.inter_shared) {       // the shared expert needs no staging: enqueue it first
     MOE_HIP(launch_gu_dense(sh.dtype, x, t0, n, sh.d, sh.inter_shared, L->w_gu_shared,
@@ -218,7 +220,7 @@ moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const i
                  reinterpret_cast<const int32_t*>(ws + W.meta) + kMetaMTiles,
                  reinterpret_cast<const int32_t*>(ws + W.offsets),
                  reinterpret_cast<const int32_t*>(ws + W.counts), wtab, 0,
-                 static_cast<int>(n * k / kBM + std::min<int64_t>(E, n * k))};
+                 static_cast<int>(n * k / bm + std::min<int64_t>(E, n * k)), bm};
     MOE_HIP(launch_gu_routed(sh.dtype, x, t0, sh.d, sh.inter, g,
                              reinterpret_cast<const int32_t*>(ws + W.row_tok), ws + W.h, s));
     MOE_HIP(launch_down_routed(sh.dtype, ws + W.h, sh.d, sh.inter, g,
@@ -247,7 +249,7 @@ bool ws_layout(const moe_shape& sh, int64_t max_n, WsLayout* L) {
   const size_t elt = elt_bytes(sh.dtype);
   const int64_t rows = max_n * k;
   const int64_t nb = (max_n + kTokBlock - 1) / kTokBlock;
-  const int64_t max_mt = rows / kBM + std::min<int64_t>(E, rows);
+  const int64_t max_mt = rows / kMinTileRows + std::min<int64_t>(E, rows);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;

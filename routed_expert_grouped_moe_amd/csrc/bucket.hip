@@ -35,10 +35,10 @@ __global__ __launch_bounds__(kTokBlock) void block_hist_kernel(const int32_t* __
 
 // One workgroup of 1024 threads; thread e owns expert e.
 //   blk_base[b][e] = slots of e in blocks before b; counts[e]; offsets = exclusive scan of
-//   counts; M-tiles: expert e contributes ceil(counts[e]/kBM) tiles (e, 0), (e, kBM), ... at
+//   counts; M-tiles: expert e contributes ceil(counts[e]/bm) tiles (e, 0), (e, bm), ... at
 //   position (exclusive scan of the tile counts); meta = {number of tiles, number of rows}.
 __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ blk_counts,
-                                                    int nb, int E,
+                                                    int nb, int E, int bm,
                                                     int32_t* __restrict__ blk_base,
                                                     int32_t* __restrict__ counts,
                                                     int32_t* __restrict__ offsets,
@@ -56,7 +56,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
     }
     counts[e] = run;
   }
-  const int32_t ntile = static_cast<int32_t>((run + kBM - 1) / kBM);
+  const int32_t ntile = (run + bm - 1) / bm;
   s_rows[e] = run;
   s_tiles[e] = ntile;
   __syncthreads();
@@ -72,7 +72,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
   const int32_t tile_off = s_tiles[e] - ntile;
   if (e < E) {
     offsets[e] = row_off;
-    for (int i = 0; i < ntile; ++i) mtiles[tile_off + i] = MTile{e, i * kBM};
+    for (int i = 0; i < ntile; ++i) mtiles[tile_off + i] = MTile{e, i * bm};
   }
   if (e == kMaxE - 1) {
     offsets[E] = s_rows[e];
@@ -161,8 +161,8 @@ hipError_t launch_upload_pairs(const void** table, const int32_t* idx, const voi
   return hipSuccess;
 }
 
-hipError_t launch_bucket(const int32_t* ids_chunk, int64_t n, int k, int E, char* ws,
-                         const WsLayout& L, hipStream_t s) {
+hipError_t launch_bucket(const int32_t* ids_chunk, int64_t n, int k, int E, int tile_rows,
+                         char* ws, const WsLayout& L, hipStream_t s) {
   const int nb = static_cast<int>((n + kTokBlock - 1) / kTokBlock);
   int32_t* blk_counts = reinterpret_cast<int32_t*>(ws + L.blk_counts);
   int32_t* blk_base = reinterpret_cast<int32_t*>(ws + L.blk_base);
@@ -179,7 +179,8 @@ hipError_t launch_bucket(const int32_t* ids_chunk, int64_t n, int k, int E, char
   if (err != hipSuccess) return err;
   {
     ProfScope prof(MOE_STAGE_SCAN, s);
-    scan_kernel<<<1, 1024, 0, s>>>(blk_counts, nb, E, blk_base, counts, offsets, mtiles, meta);
+    scan_kernel<<<1, 1024, 0, s>>>(blk_counts, nb, E, tile_rows, blk_base, counts, offsets,
+                                   mtiles, meta);
     err = hipGetLastError();
   }
   if (err != hipSuccess) return err;

@@ -9,6 +9,15 @@ namespace moe {
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
+// 16-byte load through the global address space. Pointers read from memory (such as the
+// expert-line table) are generic to the compiler, which would otherwise emit flat loads; a
+// flat load also counts against the LDS wait counter, so waiting for LDS fragments would
+// wait for every outstanding prefetch as well.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x4_t load_global16(const char* p) {
+  return *(const __attribute__((address_space(1))) u32x4_t*)(p);
+}
+
 // bf16 is stored as its raw 16-bit pattern (the upper half of an IEEE binary32).
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);

@@ -1,18 +1,25 @@
 // GEMMs of the layer on CDNA4 matrix cores: the router, each expert's gate/up projection with
 // the fused silu(gate)*up epilogue, and each expert's down projection.
 //
-// Every GEMM here is X W^T with both operands K-contiguous (x rows and weight rows), tiled
-// 128 x 128 per workgroup, K staged through LDS 128 bytes per row at a time (double buffered,
-// one barrier per stage). The four waves of a workgroup each own a 64 x 64 block built from
-// 4 x 4 MFMA blocks of 16 x 16: v_mfma_f32_16x16x32_bf16 for bf16 storage and
-// v_mfma_f32_16x16x4_f32 for fp32 storage, fp32 accumulation in both.
+// Every GEMM here is X W^T with both operands K-contiguous (token rows and weight rows). A
+// workgroup computes a BM x BN tile; K advances 128 bytes per row and stage (64 bf16 or 32
+// fp32 elements) through two LDS stages filled by direct global->LDS loads
+// (global_load_lds_dwordx4: each lane's 16 bytes land at the instruction's LDS base plus
+// 16 x lane, so one instruction fills 8 rows of 128 bytes; the A rows of a routed tile are
+// gathered from the prompt by pointer, no permuted copy of x exists). Inside LDS, 16-byte
+// segment g of row r sits at segment g ^ (r & 7), so the 16 lanes that read one MFMA operand
+// (16 rows, same K segment) hit 16 different bank groups. Waves own 64-row slabs of the tile
+// and accumulate 16 x 16 MFMA blocks: v_mfma_f32_16x16x32_bf16 (bf16) or
+// v_mfma_f32_16x16x4_f32 (fp32), fp32 accumulation.
 //
-// Row invariance (what makes chunked prefill equal the batched pass bit for bit): every
-// output element is one token row against one weight row, accumulated over K in the same
-// stage order with the same instruction, whatever tile, group size or chunk the row falls
-// in. No split-K, no shape-dependent kernel choice, no atomics. This is the property the
-// exact deep prefill page ("Flash Next EXL3: exact deep prefill", opening section) asks of
-// its GU/down kernels: the same bytes at every chunk size.
+// Two tile shapes: big (256 x 256, 8 waves of 64 x 128) for large row counts and small
+// (64 x 256, 4 waves of 64 x 64) for few rows per expert. Which one runs never changes a bit:
+// every output element is one token row against one weight row, accumulated over K in the same
+// stage order with the same instruction and the same lane-to-K mapping in both. Together with
+// no split-K, no atomics and no shape-dependent arithmetic, that is what makes a token's bytes
+// independent of the chunk size, of its position and of its expert's row count -- the
+// property the exact deep prefill page ("Flash Next EXL3: exact deep prefill", opening section)
+// asks of its GU/down kernels.
 #include "device_common.h"
 #include "moe_internal.h"
 #include "profile.h"
@@ -20,134 +27,199 @@
 namespace moe {
 namespace {
 
-constexpr int kRowBytes = 128;                          // K bytes per row per stage
-constexpr int kLdsPitch = kRowBytes + 16;               // padded LDS row pitch
-constexpr int kStageBytes = (kBM + kBN) * kLdsPitch;    // A tile + B tile of one stage
-constexpr int kLdsBytes = 2 * kStageBytes;              // double buffer: 73,728 bytes
+constexpr int kRowBytes = 128;     // K bytes per row per stage
 
-template <typename T> struct Mma;
-
-// bf16: one stage = 64 K elements = 2 MFMA steps of 32. Lane l supplies row (l & 15) and the
-// 8 consecutive K elements starting at 8 * (l >> 4) of the step, for A and B alike.
-template <> struct Mma<uint16_t> {
-  static constexpr int kStageElems = kRowBytes / 2;
-  static __device__ __forceinline__ void stage(const char* la, const char* lb,
-                                               const int (&arow)[4], const int (&brow)[4],
-                                               int kq, f32x4_t (&acc)[4][4]) {
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8_t a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const bf16x8_t*>(la + arow[i] * kLdsPitch + ks * 64 + kq * 16);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[j] = *reinterpret_cast<const bf16x8_t*>(lb + brow[j] * kLdsPitch + ks * 64 + kq * 16);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-  }
+template <int BM_, int BN_, int WM_, int WN_>
+struct Tile {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int NW = WM * WN, NT = 64 * NW;
+  static constexpr int TM = BM / WM, TN = BN / WN;          // wave tile
+  static constexpr int FM = TM / 16, FN = TN / 16;          // 16 x 16 MFMA blocks per wave
+  static constexpr int ROWS = BM + BN;
+  static constexpr int STAGE = ROWS * kRowBytes;
+  static constexpr int LDS = 2 * STAGE;
+  static constexpr int LPW = ROWS / 8 / NW;                 // load instructions per wave per stage
+  static_assert(TM == 64, "waves own 64-row slabs");
+  static_assert(ROWS % (8 * NW) == 0, "whole load instructions per wave");
 };
+using BigTile = Tile<256, 256, 4, 2>;      // 8 waves, 64 x 128 each; 128 KB LDS, 1 workgroup/CU
+using SmallTile = Tile<64, 256, 1, 4>;     // 4 waves, 64 x 64 each; 80 KB LDS, 2 workgroups/CU
 
-// fp32: one stage = 32 K elements = 8 MFMA steps of 4; lane l supplies element (l >> 4).
-template <> struct Mma<float> {
-  static constexpr int kStageElems = kRowBytes / 4;
-  static __device__ __forceinline__ void stage(const char* la, const char* lb,
-                                               const int (&arow)[4], const int (&brow)[4],
-                                               int kq, f32x4_t (&acc)[4][4]) {
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      float a[4], b[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        a[i] = *reinterpret_cast<const float*>(la + arow[i] * kLdsPitch + (ks * 4 + kq) * 4);
-#pragma unroll
-      for (int j = 0; j < 4; ++j)
-        b[j] = *reinterpret_cast<const float*>(lb + brow[j] * kLdsPitch + (ks * 4 + kq) * 4);
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[j], acc[i][j], 0, 0, 0);
-    }
-  }
-};
-
-// Tile mainloop. Thread t stages rows (t >> 3) + 32 q (q = 0..3) of the A and B tiles, 16 bytes
-// at byte (t & 7) * 16 of each 128-byte stage; pa[q] / pb[q] point at those rows' first byte.
-// Rows past the end of A or B point at a valid row instead: an MFMA output element depends
-// only on its own A row and B column, so those rows and columns are computed and dropped.
-// kPairedGU: the B tile holds 64 gate rows then 64 matching up rows, and wave column wn takes
-// gate rows wn*32.. and up rows 64 + wn*32.., so that each lane holds gate and up of the same
-// output column (acc[i][j] and acc[i][j + 2], j = 0, 1).
-template <typename T, bool kPairedGU>
-__device__ __forceinline__ void mainloop(const char* const (&pa)[4], const char* const (&pb)[4],
-                                         int nk, char* lds, f32x4_t (&acc)[4][4]) {
-  const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1, kq = lane >> 4, l16 = lane & 15;
-  const int seg = tid & 7, srow = tid >> 3;
-  int arow[4], brow[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) arow[i] = wm * 64 + i * 16 + l16;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int b = kPairedGU ? ((j < 2) ? wn * 32 + j * 16 : 64 + wn * 32 + (j - 2) * 16)
-                            : wn * 64 + j * 16;
-    brow[j] = b + l16;
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  uint4 ra0, ra1, ra2, ra3, rb0, rb1, rb2, rb3;
-  const int st_off = srow * kLdsPitch + seg * 16;
-#define MOE_GLOAD(kb)                                                                     \
-  do {                                                                                    \
-    const int off_ = (kb) * kRowBytes + seg * 16;                                         \
-    ra0 = *reinterpret_cast<const uint4*>(pa[0] + off_);                              \
-    ra1 = *reinterpret_cast<const uint4*>(pa[1] + off_);                              \
-    ra2 = *reinterpret_cast<const uint4*>(pa[2] + off_);                              \
-    ra3 = *reinterpret_cast<const uint4*>(pa[3] + off_);                              \
-    rb0 = *reinterpret_cast<const uint4*>(pb[0] + off_);                              \
-    rb1 = *reinterpret_cast<const uint4*>(pb[1] + off_);                              \
-    rb2 = *reinterpret_cast<const uint4*>(pb[2] + off_);                              \
-    rb3 = *reinterpret_cast<const uint4*>(pb[3] + off_);                              \
-  } while (0)
-#define MOE_SSTORE(buf)                                                                   \
-  do {                                                                                    \
-    char* b_ = (buf) + st_off;                                                            \
-    *reinterpret_cast<uint4*>(b_ + 0 * 32 * kLdsPitch) = ra0;                             \
-    *reinterpret_cast<uint4*>(b_ + 1 * 32 * kLdsPitch) = ra1;                             \
-    *reinterpret_cast<uint4*>(b_ + 2 * 32 * kLdsPitch) = ra2;                             \
-    *reinterpret_cast<uint4*>(b_ + 3 * 32 * kLdsPitch) = ra3;                             \
-    *reinterpret_cast<uint4*>(b_ + (kBM + 0 * 32) * kLdsPitch) = rb0;                     \
-    *reinterpret_cast<uint4*>(b_ + (kBM + 1 * 32) * kLdsPitch) = rb1;                     \
-    *reinterpret_cast<uint4*>(b_ + (kBM + 2 * 32) * kLdsPitch) = rb2;                     \
-    *reinterpret_cast<uint4*>(b_ + (kBM + 3 * 32) * kLdsPitch) = rb3;                     \
-  } while (0)
-
-  MOE_GLOAD(0);
-  MOE_SSTORE(lds);
-  __syncthreads();
-  for (int kb = 0; kb < nk; ++kb) {
-    const char* cur = lds + (kb & 1) * kStageBytes;
-    const bool more = kb + 1 < nk;
-    if (more) MOE_GLOAD(kb + 1);
-    Mma<T>::stage(cur, cur + kBM * kLdsPitch, arow, brow, kq, acc);
-    if (more) MOE_SSTORE(lds + ((kb + 1) & 1) * kStageBytes);
-    __syncthreads();
-  }
-#undef MOE_GLOAD
-#undef MOE_SSTORE
+// s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding of the immediate).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Output coordinates of accumulator element acc[i][j][r] of this lane (non-paired layout):
-//   tile row = wm*64 + i*16 + 4*(lane >> 4) + r, tile column = wn*64 + j*16 + (lane & 15).
+template <typename T> struct Frag;
+
+// bf16: a stage holds 2 MFMA steps of 32 K elements. Lane l supplies row (l & 15) and the 8
+// consecutive K elements of 16-byte segment (4 * step + (l >> 4)), for A and B alike.
+template <> struct Frag<uint16_t> {
+  static constexpr int kSteps = 2;
+  typedef bf16x8_t V;
+  static __device__ __forceinline__ V load(const char* row, int step, int kq, int sw) {
+    return *reinterpret_cast<const V*>(row + (((step * 4 + kq) ^ sw) << 4));
+  }
+  static __device__ __forceinline__ f32x4_t mma(V a, V b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+// fp32: a stage holds 8 MFMA steps of 4 K elements; lane l supplies element (l >> 4) of the
+// step, i.e. 4-byte word (l >> 4) of 16-byte segment `step`.
+template <> struct Frag<float> {
+  static constexpr int kSteps = 8;
+  typedef float V;
+  static __device__ __forceinline__ V load(const char* row, int step, int kq, int sw) {
+    return *reinterpret_cast<const V*>(row + (((step ^ sw) << 4) | (kq << 2)));
+  }
+  static __device__ __forceinline__ f32x4_t mma(V a, V b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// Row this lane stages for load instruction q, and the segment of it that it loads (so that
+// after the swizzle the instruction's 1 KB block holds 8 whole rows).
+template <class TL>
+__device__ __forceinline__ int stage_row(int q) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  return (wave * TL::LPW + q) * 8 + (lane >> 3);
+}
+__device__ __forceinline__ int stage_seg() {
+  const int lane = threadIdx.x & 63;
+  return (lane & 7) ^ (lane >> 3);
+}
+
+// Mainloop. src[q]: this lane's global source (row start + 16 * stage_seg()) for load
+// instruction q; stage s reads 128 bytes further per stage. kPairedGU: the B half holds BN/2
+// gate rows then the BN/2 matching up rows; wave column wn takes gate blocks wn*TN/2.. and the
+// up blocks of the same columns, so acc[i][j] and acc[i][j + FN/2] are gate and up of one
+// output element. rows: valid rows of the tile; a wave whose 64-row slab holds none keeps
+// loading its share of the stages but skips its MFMAs (its outputs are never stored).
+template <typename T, class TL, bool kPairedGU>
+__device__ __forceinline__ void mainloop(const char* const (&src)[TL::LPW], int nk, char* lds,
+                                         f32x4_t (&acc)[TL::FM][TL::FN], int rows) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / TL::WN, wn = wave % TL::WN, kq = lane >> 4, l16 = lane & 15;
+  const bool busy = wm * TL::TM < rows;
+  const int sw = l16 & 7;
+  int arow[TL::FM], brow[TL::FN];
+#pragma unroll
+  for (int i = 0; i < TL::FM; ++i) arow[i] = (wm * TL::TM + i * 16 + l16) * kRowBytes;
+#pragma unroll
+  for (int j = 0; j < TL::FN; ++j) {
+    int b;
+    if (kPairedGU) {
+      constexpr int H = TL::FN / 2;
+      b = (j < H) ? wn * (TL::TN / 2) + j * 16 : TL::BN / 2 + wn * (TL::TN / 2) + (j - H) * 16;
+    } else {
+      b = wn * TL::TN + j * 16;
+    }
+    brow[j] = (TL::BM + b + l16) * kRowBytes;
+  }
+#pragma unroll
+  for (int i = 0; i < TL::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < TL::FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  char* const wave_base = lds + wave * TL::LPW * 1024;
+  auto issue = [&](int s) {
+    char* dst = wave_base + (s & 1) * TL::STAGE;
+#pragma unroll
+    for (int q = 0; q < TL::LPW; ++q)
+      __builtin_amdgcn_global_load_lds(
+          (const __attribute__((address_space(1))) void*)(src[q] + s * kRowBytes),
+          (__attribute__((address_space(3))) void*)(dst + q * 1024), 16, 0, 0);
+  };
+  issue(0);
+  for (int s = 0; s < nk; ++s) {
+    wait_vmcnt<0>();            // this wave's share of stage s has landed ...
+    __syncthreads();            // ... and everyone's; everyone also left stage s - 1
+    if (s + 1 < nk) issue(s + 1);
+    const char* buf = lds + (s & 1) * TL::STAGE;
+    if (!busy) continue;
+#pragma unroll
+    for (int ks = 0; ks < Frag<T>::kSteps; ++ks) {
+      typename Frag<T>::V a[TL::FM], b[TL::FN];
+#pragma unroll
+      for (int i = 0; i < TL::FM; ++i) a[i] = Frag<T>::load(buf + arow[i], ks, kq, sw);
+#pragma unroll
+      for (int j = 0; j < TL::FN; ++j) b[j] = Frag<T>::load(buf + brow[j], ks, kq, sw);
+#pragma unroll
+      for (int i = 0; i < TL::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < TL::FN; ++j) acc[i][j] = Frag<T>::mma(a[i], b[j], acc[i][j]);
+    }
+  }
+  __syncthreads();              // LDS free for the epilogue
+}
+
+// Accumulator element acc[i][j][r] of a lane sits at wave-tile row i*16 + 4*(lane >> 4) + r and
+// column j*16 + (lane & 15).
+
+// XCD-aware placement of a 1-D grid. Workgroups are handed to the 8 XCDs round-robin
+// (workgroup w runs on XCD w % 8), and each XCD has its own L2. Workgroup w takes tile
+// (w % 8) * q + w / 8 with q = ceil(n_tiles / 8): every XCD works through one contiguous
+// slice of the tile sequence, so the tiles that share weights or activation rows (neighbours
+// in the sequence) meet in the same L2. The grid is padded to a multiple of 8; surplus
+// workgroups have no tile.
+constexpr int kXcds = 8;
+__device__ __forceinline__ bool xcd_tile(int n_tiles, int* t) {
+  const int w = static_cast<int>(blockIdx.x);
+  const int q = (n_tiles + kXcds - 1) / kXcds;
+  const int j = w / kXcds;
+  const int tt = (w % kXcds) * q + j;
+  if (j >= q || tt >= n_tiles) return false;
+  *t = tt;
+  return true;
+}
+inline unsigned xcd_grid(int64_t n_tiles) {
+  return static_cast<unsigned>((n_tiles + kXcds - 1) / kXcds * kXcds);
+}
+
+// Output of one wave's slab through LDS in 16-row rounds: the lanes write their accumulator
+// values (transformed by `val`) into a per-wave staging area, then store whole rows with
+// 16-byte vectors. row_of(r) maps a slab row to its global output row (or -1 to skip),
+// OUT is the stored element type, cols = columns of the slab that exist (<= NCOL).
+template <class TL, typename OUT, int NCOL, class Val, class RowOf>
+__device__ __forceinline__ void store_slab(char* lds, Val val, RowOf row_of, OUT* out,
+                                           int64_t ld, int col0, int cols) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int RB = NCOL * static_cast<int>(sizeof(OUT));        // bytes per staged row
+  constexpr int CPR = RB / 16;                                      // 16-byte chunks per row
+  OUT* stg = reinterpret_cast<OUT*>(lds + wave * (16 * RB));
+  static_assert(16 * RB * TL::NW <= TL::LDS, "staging fits in LDS");
+#pragma unroll
+  for (int i = 0; i < TL::FM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int j = 0; j < NCOL / 16; ++j)
+        stg[(4 * (lane >> 4) + r) * NCOL + j * 16 + (lane & 15)] = val(i, j, r);
+    __builtin_amdgcn_wave_barrier();
+    constexpr int EPC = 16 / static_cast<int>(sizeof(OUT));       // elements per chunk
+    // 16-byte stores need 16-byte aligned rows; a chunk that would cross `cols` (or a row
+    // pitch that is not a multiple of 16 bytes) goes element by element
+    const bool vec = (ld % EPC) == 0 && (col0 % EPC) == 0 &&
+                     (reinterpret_cast<uintptr_t>(out) & 15) == 0;
+#pragma unroll
+    for (int c = lane; c < 16 * CPR; c += 64) {
+      const int row = c / CPR, ch = c % CPR;
+      const int64_t grow = row_of(i * 16 + row);
+      const int col = ch * EPC;
+      if (grow < 0 || col >= cols) continue;
+      const char* s = reinterpret_cast<const char*>(stg) + row * RB + ch * 16;
+      OUT* d = out + grow * ld + col0 + col;
+      if (vec && col + EPC <= cols) {
+        *reinterpret_cast<u32x4_t*>(d) = *reinterpret_cast<const u32x4_t*>(s);
+      } else {
+        for (int e = 0; e < EPC && col + e < cols; ++e) d[e] = reinterpret_cast<const OUT*>(s)[e];
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
 
 struct GuParams {
   const void* x;          // [T, d] prompt rows
@@ -158,61 +230,70 @@ struct GuParams {
   GemmGroups g;           // grouped: routed experts
   const int32_t* row_tok; // grouped: chunk-local token of each permuted row
   void* h;                // [rows, I] out
-  bool grouped;
 };
 
-template <typename T>
-__global__ __launch_bounds__(kThreads) void gu_kernel(GuParams p) {
-  __shared__ __align__(16) char lds[kLdsBytes];
-  const int tid = threadIdx.x;
-  const int n0h = blockIdx.x * kGuHCols;
+template <typename T, class TL, bool kGrouped>
+__global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(2)))
+void gu_kernel(GuParams p) {
+  __shared__ __attribute__((aligned(1024))) char lds[TL::LDS];
+  constexpr int HC = TL::BN / 2;                         // h columns per tile
+  const int NT = (p.I + HC - 1) / HC;
+  const int m_tiles = kGrouped ? max(0, min(p.g.tile_cap, *p.g.n_mtiles - p.g.tile_lo))
+                               : static_cast<int>((p.n + TL::BM - 1) / TL::BM);
+  int t;
+  if (!xcd_tile(m_tiles * NT, &t)) return;
+  const int mi = t / NT;
+  const int n0h = (t % NT) * HC;
   int64_t row0;
   int rows;
   const char* wbase;
-  if (p.grouped) {
-    const int ti = p.g.tile_lo + static_cast<int>(blockIdx.y);
-    if (ti >= *p.g.n_mtiles) return;
-    const MTile mt = p.g.mtiles[ti];
+  if (kGrouped) {
+    const MTile mt = p.g.mtiles[p.g.tile_lo + mi];
     row0 = static_cast<int64_t>(p.g.offsets[mt.group]) + mt.m0;
-    rows = min(kBM, p.g.counts[mt.group] - mt.m0);
+    rows = min(TL::BM, p.g.counts[mt.group] - mt.m0);
     wbase = static_cast<const char*>(p.g.wtab[mt.group]);
   } else {
-    row0 = static_cast<int64_t>(blockIdx.y) * kBM;
-    rows = static_cast<int>(min<int64_t>(kBM, p.n - row0));
+    row0 = static_cast<int64_t>(mi) * TL::BM;
+    rows = static_cast<int>(min<int64_t>(TL::BM, p.n - row0));
     wbase = static_cast<const char*>(p.w);
   }
   const bool missing = wbase == nullptr;   // offloaded expert that was not staged
   const size_t rowb = static_cast<size_t>(p.d) * sizeof(T);
-  const char* pa[4];
-  const char* pb[4];
+  const char* src[TL::LPW];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int trow = (tid >> 3) + 32 * q;
-    const int arow = trow < rows ? trow : 0;
-    const int64_t tok = p.grouped ? p.row_tok[row0 + arow] : row0 + arow;
-    pa[q] = static_cast<const char*>(p.x) + (p.t0 + tok) * rowb;
-    const int64_t wrow = (trow < 64) ? n0h + trow : p.I + n0h + (trow - 64);
-    pb[q] = wbase + wrow * rowb;
-  }
-  f32x4_t acc[4][4];
-  if (!missing) mainloop<T, true>(pa, pb, p.d / Mma<T>::kStageElems, lds, acc);
-
-  const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-  T* h = static_cast<T*>(p.h);
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int trow = wm * 64 + i * 16 + 4 * (lane >> 4) + r;
-      if (trow >= rows) continue;
-      T* hrow = h + (row0 + trow) * static_cast<int64_t>(p.I);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int col = n0h + wn * 32 + j * 16 + (lane & 15);
-        const float hv = missing ? __builtin_nanf("") : silu_f32(acc[i][j][r]) * acc[i][j + 2][r];
-        hrow[col] = Elt<T>::store(hv);
-      }
+  for (int q = 0; q < TL::LPW; ++q) {
+    const int r = stage_row<TL>(q);
+    const char* base;
+    if (r < TL::BM) {
+      const int ar = r < rows ? r : 0;     // rows past the end compute and are dropped
+      const int64_t tok = kGrouped ? p.row_tok[row0 + ar] : row0 + ar;
+      base = static_cast<const char*>(p.x) + (p.t0 + tok) * rowb;
+    } else {
+      const int br = r - TL::BM;
+      const int hc = n0h + (br < HC ? br : br - HC);
+      const int wrow = (hc < p.I ? hc : n0h) + (br < HC ? 0 : p.I);
+      base = (missing ? static_cast<const char*>(p.x) : wbase) + static_cast<int64_t>(wrow) * rowb;
     }
+    src[q] = base + 16 * stage_seg();
+  }
+  f32x4_t acc[TL::FM][TL::FN];
+  if (!missing)
+    mainloop<T, TL, true>(src, p.d / (kRowBytes / static_cast<int>(sizeof(T))), lds, acc, rows);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / TL::WN, wn = wave % TL::WN;
+  constexpr int H = TL::FN / 2;
+  auto val = [&](int i, int j, int r) -> T {
+    const float hv = missing ? __builtin_nanf("") : silu_f32(acc[i][j][r]) * acc[i][j + H][r];
+    return Elt<T>::store(hv);
+  };
+  const int slab0 = wm * TL::TM;
+  auto row_of = [&](int sr) -> int64_t {
+    return slab0 + sr < rows ? row0 + slab0 + sr : -1;
+  };
+  const int col0 = n0h + wn * (TL::TN / 2);
+  store_slab<TL, T, TL::TN / 2>(lds, val, row_of, static_cast<T*>(p.h), p.I, col0,
+                                min(TL::TN / 2, p.I - col0));
 }
 
 struct DownParams {
@@ -224,58 +305,69 @@ struct DownParams {
   int64_t line_down_off;  // grouped: element offset of W_down inside a line (2*I*d)
   const int32_t* row_slot;// grouped: output row (t*k + j) of each permuted row
   float* out;             // grouped: Y [n*k, d]; dense: S [n, d]
-  bool grouped;
 };
 
-template <typename T>
-__global__ __launch_bounds__(kThreads) void down_kernel(DownParams p) {
-  __shared__ __align__(16) char lds[kLdsBytes];
-  const int tid = threadIdx.x;
-  const int n0 = blockIdx.x * kBN;
+template <typename T, class TL, bool kGrouped>
+__global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(2)))
+void down_kernel(DownParams p) {
+  __shared__ __attribute__((aligned(1024))) char lds[TL::LDS];
+  const int NT = (p.d + TL::BN - 1) / TL::BN;
+  // a tile-list entry taller than this tile shape is worked as `sub` stacked tiles
+  const int sub = kGrouped ? p.g.tile_rows / TL::BM : 1;
+  const int m_tiles = kGrouped ? max(0, min(p.g.tile_cap, *p.g.n_mtiles - p.g.tile_lo)) * sub
+                               : static_cast<int>((p.n + TL::BM - 1) / TL::BM);
+  int t;
+  if (!xcd_tile(m_tiles * NT, &t)) return;
+  const int mi = t / NT;
+  const int n0 = (t % NT) * TL::BN;
   int64_t row0;
   int rows;
   const char* wbase;
-  if (p.grouped) {
-    const int ti = p.g.tile_lo + static_cast<int>(blockIdx.y);
-    if (ti >= *p.g.n_mtiles) return;
-    const MTile mt = p.g.mtiles[ti];
-    row0 = static_cast<int64_t>(p.g.offsets[mt.group]) + mt.m0;
-    rows = min(kBM, p.g.counts[mt.group] - mt.m0);
+  if (kGrouped) {
+    const MTile mt = p.g.mtiles[p.g.tile_lo + mi / sub];
+    const int m0 = mt.m0 + (mi % sub) * TL::BM;
+    rows = min(TL::BM, p.g.counts[mt.group] - m0);
+    if (rows <= 0) return;
+    row0 = static_cast<int64_t>(p.g.offsets[mt.group]) + m0;
     const char* line = static_cast<const char*>(p.g.wtab[mt.group]);
     wbase = line ? line + p.line_down_off * static_cast<int64_t>(sizeof(T)) : nullptr;
   } else {
-    row0 = static_cast<int64_t>(blockIdx.y) * kBM;
-    rows = static_cast<int>(min<int64_t>(kBM, p.n - row0));
+    row0 = static_cast<int64_t>(mi) * TL::BM;
+    rows = static_cast<int>(min<int64_t>(TL::BM, p.n - row0));
     wbase = static_cast<const char*>(p.w);
   }
   const bool missing = wbase == nullptr;
   const size_t rowb = static_cast<size_t>(p.K) * sizeof(T);
-  const char* pa[4];
-  const char* pb[4];
+  const char* src[TL::LPW];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int trow = (tid >> 3) + 32 * q;
-    pa[q] = static_cast<const char*>(p.h) + (row0 + (trow < rows ? trow : 0)) * rowb;
-    pb[q] = wbase + static_cast<int64_t>(n0 + trow < p.d ? n0 + trow : n0) * rowb;
-  }
-  f32x4_t acc[4][4];
-  if (!missing) mainloop<T, false>(pa, pb, p.K / Mma<T>::kStageElems, lds, acc);
-
-  const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int trow = wm * 64 + i * 16 + 4 * (lane >> 4) + r;
-      if (trow >= rows) continue;
-      const int64_t orow = p.grouped ? p.row_slot[row0 + trow] : row0 + trow;
-      float* o = p.out + orow * static_cast<int64_t>(p.d);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = n0 + wn * 64 + j * 16 + (lane & 15);
-        if (col < p.d) o[col] = missing ? __builtin_nanf("") : acc[i][j][r];
-      }
+  for (int q = 0; q < TL::LPW; ++q) {
+    const int r = stage_row<TL>(q);
+    const char* base;
+    if (r < TL::BM) {
+      base = static_cast<const char*>(p.h) + (row0 + (r < rows ? r : 0)) * rowb;
+    } else {
+      const int wr = n0 + r - TL::BM;
+      base = missing ? static_cast<const char*>(p.h)
+                     : wbase + static_cast<int64_t>(wr < p.d ? wr : n0) * rowb;
     }
+    src[q] = base + 16 * stage_seg();
+  }
+  f32x4_t acc[TL::FM][TL::FN];
+  if (!missing)
+    mainloop<T, TL, false>(src, p.K / (kRowBytes / static_cast<int>(sizeof(T))), lds, acc, rows);
+
+  const int wave = threadIdx.x >> 6;
+  const int wm = wave / TL::WN, wn = wave % TL::WN;
+  auto val = [&](int i, int j, int r) -> float {
+    return missing ? __builtin_nanf("") : acc[i][j][r];
+  };
+  const int slab0 = wm * TL::TM;
+  auto row_of = [&](int sr) -> int64_t {
+    if (slab0 + sr >= rows) return -1;
+    return kGrouped ? static_cast<int64_t>(p.row_slot[row0 + slab0 + sr]) : row0 + slab0 + sr;
+  };
+  const int col0 = n0 + wn * TL::TN;
+  store_slab<TL, float, TL::TN>(lds, val, row_of, p.out, p.d, col0, min(TL::TN, p.d - col0));
 }
 
 struct RouterParams {
@@ -287,53 +379,78 @@ struct RouterParams {
   int d, E;
 };
 
-template <typename T>
-__global__ __launch_bounds__(kThreads) void router_kernel(RouterParams p) {
-  __shared__ __align__(16) char lds[kLdsBytes];
-  const int tid = threadIdx.x;
-  const int n0 = blockIdx.x * kBN;
-  const int64_t row0 = static_cast<int64_t>(blockIdx.y) * kBM;
-  const int rows = static_cast<int>(min<int64_t>(kBM, p.T - row0));
+template <typename T, class TL>
+__global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(2)))
+void router_kernel(RouterParams p) {
+  __shared__ __attribute__((aligned(1024))) char lds[TL::LDS];
+  const int NT = (p.E + TL::BN - 1) / TL::BN;
+  int t;
+  if (!xcd_tile(static_cast<int>((p.T + TL::BM - 1) / TL::BM) * NT, &t)) return;
+  const int n0 = (t % NT) * TL::BN;
+  const int64_t row0 = static_cast<int64_t>(t / NT) * TL::BM;
+  const int rows = static_cast<int>(min<int64_t>(TL::BM, p.T - row0));
   const size_t rowb = static_cast<size_t>(p.d) * sizeof(T);
-  const char* pa[4];
-  const char* pb[4];
+  const char* src[TL::LPW];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int trow = (tid >> 3) + 32 * q;
-    pa[q] = static_cast<const char*>(p.x) + (row0 + (trow < rows ? trow : 0)) * rowb;
-    pb[q] = static_cast<const char*>(p.w) +
-            static_cast<int64_t>(n0 + trow < p.E ? n0 + trow : n0) * rowb;
-  }
-  f32x4_t acc[4][4];
-  mainloop<T, false>(pa, pb, p.d / Mma<T>::kStageElems, lds, acc);
-
-  const int lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int trow = wm * 64 + i * 16 + 4 * (lane >> 4) + r;
-      if (trow >= rows) continue;
-      float* o = p.logits + (row0 + trow) * static_cast<int64_t>(p.E);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int col = n0 + wn * 64 + j * 16 + (lane & 15);
-        if (col < p.E) o[col] = acc[i][j][r] + (p.bias ? p.bias[col] : 0.0f);
-      }
+  for (int q = 0; q < TL::LPW; ++q) {
+    const int r = stage_row<TL>(q);
+    const char* base;
+    if (r < TL::BM) {
+      base = static_cast<const char*>(p.x) + (row0 + (r < rows ? r : 0)) * rowb;
+    } else {
+      const int wr = n0 + r - TL::BM;
+      base = static_cast<const char*>(p.w) + static_cast<int64_t>(wr < p.E ? wr : n0) * rowb;
     }
+    src[q] = base + 16 * stage_seg();
+  }
+  f32x4_t acc[TL::FM][TL::FN];
+  mainloop<T, TL, false>(src, p.d / (kRowBytes / static_cast<int>(sizeof(T))), lds, acc, rows);
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / TL::WN, wn = wave % TL::WN;
+  const int col0 = n0 + wn * TL::TN;
+  auto val = [&](int i, int j, int r) -> float {
+    const int col = col0 + j * 16 + (lane & 15);
+    return acc[i][j][r] + ((p.bias && col < p.E) ? p.bias[col] : 0.0f);
+  };
+  const int slab0 = wm * TL::TM;
+  auto row_of = [&](int sr) -> int64_t { return slab0 + sr < rows ? row0 + slab0 + sr : -1; };
+  store_slab<TL, float, TL::TN>(lds, val, row_of, p.logits, p.E, col0, min(TL::TN, p.E - col0));
+}
+
+// Big tiles when they still give the chip at least two workgroups per CU, else small ones.
+inline bool use_big_dense(int64_t n, int64_t n_tiles_big) {
+  return n >= BigTile::BM && ((n + BigTile::BM - 1) / BigTile::BM) * n_tiles_big >= 512;
 }
 
 }  // namespace
+
+int routed_tile_rows(int64_t n, int k, int E) {
+  return (n * k >= static_cast<int64_t>(E) * 128) ? BigTile::BM : SmallTile::BM;
+}
 
 hipError_t launch_router_gemm(int dtype, const void* x, const void* w_router, const float* bias,
                               int64_t T, int d, int E, float* logits, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   ProfScope prof(MOE_STAGE_ROUTER, s);
   RouterParams p{x, w_router, bias, logits, T, d, E};
-  dim3 grid((E + kBN - 1) / kBN, static_cast<unsigned>((T + kBM - 1) / kBM));
-  if (dtype == MOE_BF16) router_kernel<uint16_t><<<grid, kThreads, 0, s>>>(p);
-  else router_kernel<float><<<grid, kThreads, 0, s>>>(p);
+  if (use_big_dense(T, (E + BigTile::BN - 1) / BigTile::BN)) {
+    const unsigned grid = xcd_grid((T + BigTile::BM - 1) / BigTile::BM * ((E + BigTile::BN - 1) / BigTile::BN));
+    if (dtype == MOE_BF16) router_kernel<uint16_t, BigTile><<<grid, BigTile::NT, 0, s>>>(p);
+    else router_kernel<float, BigTile><<<grid, BigTile::NT, 0, s>>>(p);
+  } else {
+    const unsigned grid = xcd_grid((T + SmallTile::BM - 1) / SmallTile::BM * ((E + SmallTile::BN - 1) / SmallTile::BN));
+    if (dtype == MOE_BF16) router_kernel<uint16_t, SmallTile><<<grid, SmallTile::NT, 0, s>>>(p);
+    else router_kernel<float, SmallTile><<<grid, SmallTile::NT, 0, s>>>(p);
+  }
   return hipGetLastError();
+}
+
+template <class TL>
+static void gu_routed(int dtype, const GuParams& p, const GemmGroups& g, int I, hipStream_t s) {
+  const unsigned grid = xcd_grid(static_cast<int64_t>(g.tile_cap) * ((I + TL::BN / 2 - 1) / (TL::BN / 2)));
+  if (dtype == MOE_BF16) gu_kernel<uint16_t, TL, true><<<grid, TL::NT, 0, s>>>(p);
+  else gu_kernel<float, TL, true><<<grid, TL::NT, 0, s>>>(p);
 }
 
 hipError_t launch_gu_routed(int dtype, const void* x, int64_t t0, int d, int I,
@@ -342,10 +459,9 @@ hipError_t launch_gu_routed(int dtype, const void* x, int64_t t0, int d, int I,
   ProfScope prof(MOE_STAGE_GU_ROUTED, s);
   GuParams p{};
   p.x = x; p.t0 = t0; p.n = 0; p.d = d; p.I = I; p.w = nullptr; p.g = g;
-  p.row_tok = row_tok; p.h = h; p.grouped = true;
-  dim3 grid(I / kGuHCols, g.tile_cap);
-  if (dtype == MOE_BF16) gu_kernel<uint16_t><<<grid, kThreads, 0, s>>>(p);
-  else gu_kernel<float><<<grid, kThreads, 0, s>>>(p);
+  p.row_tok = row_tok; p.h = h;
+  if (g.tile_rows == BigTile::BM) gu_routed<BigTile>(dtype, p, g, I, s);
+  else gu_routed<SmallTile>(dtype, p, g, I, s);
   return hipGetLastError();
 }
 
@@ -354,12 +470,27 @@ hipError_t launch_gu_dense(int dtype, const void* x, int64_t t0, int64_t n, int 
   if (n <= 0 || Is <= 0) return hipSuccess;
   ProfScope prof(MOE_STAGE_GU_SHARED, s);
   GuParams p{};
-  p.x = x; p.t0 = t0; p.n = n; p.d = d; p.I = Is; p.w = w_gu; p.row_tok = nullptr;
-  p.h = h; p.grouped = false;
-  dim3 grid(Is / kGuHCols, static_cast<unsigned>((n + kBM - 1) / kBM));
-  if (dtype == MOE_BF16) gu_kernel<uint16_t><<<grid, kThreads, 0, s>>>(p);
-  else gu_kernel<float><<<grid, kThreads, 0, s>>>(p);
+  p.x = x; p.t0 = t0; p.n = n; p.d = d; p.I = Is; p.w = w_gu; p.row_tok = nullptr; p.h = h;
+  const int64_t nt_big = (Is + BigTile::BN / 2 - 1) / (BigTile::BN / 2);
+  if (use_big_dense(n, nt_big)) {
+    const unsigned grid = xcd_grid((n + BigTile::BM - 1) / BigTile::BM * nt_big);
+    if (dtype == MOE_BF16) gu_kernel<uint16_t, BigTile, false><<<grid, BigTile::NT, 0, s>>>(p);
+    else gu_kernel<float, BigTile, false><<<grid, BigTile::NT, 0, s>>>(p);
+  } else {
+    const unsigned grid = xcd_grid((n + SmallTile::BM - 1) / SmallTile::BM *
+                                   ((Is + SmallTile::BN / 2 - 1) / (SmallTile::BN / 2)));
+    if (dtype == MOE_BF16) gu_kernel<uint16_t, SmallTile, false><<<grid, SmallTile::NT, 0, s>>>(p);
+    else gu_kernel<float, SmallTile, false><<<grid, SmallTile::NT, 0, s>>>(p);
+  }
   return hipGetLastError();
+}
+
+template <class TL>
+static void down_routed(int dtype, const DownParams& p, const GemmGroups& g, int d, hipStream_t s) {
+  const unsigned grid = xcd_grid(static_cast<int64_t>(g.tile_cap) * (g.tile_rows / TL::BM) *
+                                 ((d + TL::BN - 1) / TL::BN));
+  if (dtype == MOE_BF16) down_kernel<uint16_t, TL, true><<<grid, TL::NT, 0, s>>>(p);
+  else down_kernel<float, TL, true><<<grid, TL::NT, 0, s>>>(p);
 }
 
 hipError_t launch_down_routed(int dtype, const void* h, int d, int I, const GemmGroups& g,
@@ -368,10 +499,9 @@ hipError_t launch_down_routed(int dtype, const void* h, int d, int I, const Gemm
   ProfScope prof(MOE_STAGE_DOWN_ROUTED, s);
   DownParams p{};
   p.h = h; p.n = 0; p.d = d; p.K = I; p.w = nullptr; p.g = g;
-  p.line_down_off = 2LL * I * d; p.row_slot = row_slot; p.out = y; p.grouped = true;
-  dim3 grid((d + kBN - 1) / kBN, g.tile_cap);
-  if (dtype == MOE_BF16) down_kernel<uint16_t><<<grid, kThreads, 0, s>>>(p);
-  else down_kernel<float><<<grid, kThreads, 0, s>>>(p);
+  p.line_down_off = 2LL * I * d; p.row_slot = row_slot; p.out = y;
+  if (g.tile_rows == BigTile::BM) down_routed<BigTile>(dtype, p, g, d, s);
+  else down_routed<SmallTile>(dtype, p, g, d, s);
   return hipGetLastError();
 }
 
@@ -381,10 +511,18 @@ hipError_t launch_down_dense(int dtype, const void* h, int64_t n, int d, int Is,
   ProfScope prof(MOE_STAGE_DOWN_SHARED, s);
   DownParams p{};
   p.h = h; p.n = n; p.d = d; p.K = Is; p.w = w_down; p.line_down_off = 0;
-  p.row_slot = nullptr; p.out = out; p.grouped = false;
-  dim3 grid((d + kBN - 1) / kBN, static_cast<unsigned>((n + kBM - 1) / kBM));
-  if (dtype == MOE_BF16) down_kernel<uint16_t><<<grid, kThreads, 0, s>>>(p);
-  else down_kernel<float><<<grid, kThreads, 0, s>>>(p);
+  p.row_slot = nullptr; p.out = out;
+  const int64_t nt_big = (d + BigTile::BN - 1) / BigTile::BN;
+  if (use_big_dense(n, nt_big)) {
+    const unsigned grid = xcd_grid((n + BigTile::BM - 1) / BigTile::BM * nt_big);
+    if (dtype == MOE_BF16) down_kernel<uint16_t, BigTile, false><<<grid, BigTile::NT, 0, s>>>(p);
+    else down_kernel<float, BigTile, false><<<grid, BigTile::NT, 0, s>>>(p);
+  } else {
+    const unsigned grid = xcd_grid((n + SmallTile::BM - 1) / SmallTile::BM *
+                                   ((d + SmallTile::BN - 1) / SmallTile::BN));
+    if (dtype == MOE_BF16) down_kernel<uint16_t, SmallTile, false><<<grid, SmallTile::NT, 0, s>>>(p);
+    else down_kernel<float, SmallTile, false><<<grid, SmallTile::NT, 0, s>>>(p);
+  }
   return hipGetLastError();
 }
 

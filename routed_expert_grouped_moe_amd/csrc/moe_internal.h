@@ -12,17 +12,12 @@
 
 namespace moe {
 
-// ------------------------------------------------------------------ GEMM tiling constants
-// One workgroup computes a 128 x 128 output tile with 4 waves (2 x 2, 64 x 64 each) on
-// 16x16 MFMA blocks; K advances 128 bytes per stage (64 bf16 or 32 fp32 elements).
-constexpr int kBM = 128;          // rows of a tile (token rows)
-constexpr int kBN = 128;          // columns of a tile (weight rows)
-constexpr int kGuHCols = 64;      // h columns per gate/up tile (64 gate + 64 up weight rows)
-constexpr int kThreads = 256;
+// ------------------------------------------------------------------ tiling constants
+constexpr int kMinTileRows = 64;  // smallest M-tile height of the routed GEMMs
 constexpr int kTokBlock = 256;    // tokens per block of the bucketing kernels
 
 // ------------------------------------------------------------------ device-side records
-struct MTile {                    // one M-tile of a routed expert: rows [m0, m0+kBM) of group g
+struct MTile {                    // one M-tile of a routed expert: rows [m0, m0 + tile rows)
   int32_t group;
   int32_t m0;
 };
@@ -55,7 +50,11 @@ MOE_HIDDEN hipError_t launch_upload_ptrs(const void** dst_table, const void* con
 MOE_HIDDEN hipError_t launch_upload_pairs(const void** table, const int32_t* idx,
                                          const void* const* ptr, int n, hipStream_t s);
 MOE_HIDDEN hipError_t launch_bucket(const int32_t* ids_chunk, int64_t n, int k, int E,
-                                    char* ws, const WsLayout& L, hipStream_t s);
+                                    int tile_rows, char* ws, const WsLayout& L, hipStream_t s);
+
+// M-tile height of the routed GEMMs for a chunk of n tokens (256 when experts average at least
+// 128 rows, else 64). The choice changes speed only, never a result bit.
+MOE_HIDDEN int routed_tile_rows(int64_t n, int k, int E);
 
 struct GemmGroups {               // routed (grouped) problem description
   const MTile* mtiles;
@@ -64,7 +63,8 @@ struct GemmGroups {               // routed (grouped) problem description
   const int32_t* counts;          // [E]
   const void* const* wtab;        // [E] expert line pointers
   int tile_lo;                    // first M-tile of this launch
-  int tile_cap;                   // grid rows (M-tiles) of this launch
+  int tile_cap;                   // M-tiles this launch may cover (upper bound)
+  int tile_rows;                  // M-tile height the tile list was built with
 };
 
 MOE_HIDDEN hipError_t launch_gu_routed(int dtype, const void* x, int64_t t0, int d, int I,
@@ -85,6 +85,6 @@ MOE_HIDDEN hipError_t launch_add_rmsnorm(int dtype, const void* x, const void* d
                                          void* normed, hipStream_t s);
 
 // number of M-tiles of a group with c rows
-inline int64_t mtiles_of(int64_t c) { return (c + kBM - 1) / kBM; }
+inline int64_t mtiles_of(int64_t c, int tile_rows) { return (c + tile_rows - 1) / tile_rows; }
 
 }  // namespace moe

@@ -20,7 +20,7 @@ __all__ = [
     "MOE_BF16", "MOE_F32", "MoeError", "Layer", "Ring", "make_shape", "moe_workspace_bytes",
     "moe_prefill_route", "moe_prefill_chunk", "moe_prefill_layer", "moe_stage_experts",
     "moe_add_rmsnorm", "moe_abi_version", "line_elems", "moe_workspace_offsets",
-    "layer_buffers", "moe_profile_enable", "moe_profile_read",
+    "layer_buffers", "moe_profile_enable", "moe_profile_read", "moe_prefill_stack",
 ]
 
 
@@ -300,6 +300,35 @@ def moe_prefill_layer(layer: Layer, x, chunk: int, workspace=None, out=None, str
                                   _stream(copy_stream) if copy_stream is not None else None),
           "moe_prefill_layer")
     return r
+
+
+def moe_prefill_stack(layers: Sequence[Layer], x, chunk: int, eps: float, stream=None,
+                      copy_stream=None, keep_inputs: bool = False) -> dict:
+    """A stack of layers joined by RMSNorm and a residual add, every step in the library:
+    h_0 = rmsnorm(x); x_{l+1} = x_l + layer_l(h_l); h_{l+1} = rmsnorm(x_{l+1}).
+    Returns {"out": final residual stream}; with keep_inputs also per-layer lists "x" (x_l),
+    "inputs" (h_l), "outs" (layer_l(h_l)), "ids", "weights", "logits"."""
+    if not layers:
+        raise ValueError("empty stack")
+    T = x.shape[0]
+    xs = x.clone()
+    normed = torch.empty_like(x)
+    moe_add_rmsnorm(xs, None, eps, normed=normed, stream=stream)
+    bufs = layer_buffers(layers[0], T, chunk, x.device)
+    keys = ("x", "inputs", "outs", "ids", "weights", "logits")
+    res = {key: [] for key in keys}
+    for L in layers:
+        if keep_inputs:
+            res["x"].append(xs.clone())
+            res["inputs"].append(normed.clone())
+        r = moe_prefill_layer(L, normed, chunk, stream=stream, copy_stream=copy_stream, bufs=bufs)
+        if keep_inputs:
+            for key, src in (("outs", "out"), ("ids", "ids"), ("weights", "weights"),
+                             ("logits", "logits")):
+                res[key].append(r[src].clone())
+        moe_add_rmsnorm(xs, r["out"], eps, x_out=xs, normed=normed, stream=stream)
+    res["out"] = xs
+    return res
 
 
 def moe_profile_enable(on: bool = True) -> None:

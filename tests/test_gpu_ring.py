@@ -1,0 +1,179 @@
+"""Staging ring of expert lines (pinned host bank -> HBM on a side stream): the output of a
+layer whose experts stream through the ring equals the all-resident output bit for bit, the
+staging bookkeeping (hits, misses, bytes) is what the plan implies, and the error paths leave
+everything unchanged. Needs an MI355X."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+import oracle.moe_oracle as orc
+from tests.parity import as_f64, oracle_params, place, rel_err, routing_gates
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def moe():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import routed_expert_grouped_moe_amd as m
+    return m
+
+
+def bits(t):
+    return t.view(torch.int16) if t.dtype == torch.bfloat16 else t.view(torch.int32)
+
+
+@pytest.mark.parametrize("n_lines,offload,chunk", [
+    (4, "half", 64), (1, "all", 100), (2, "all", 300), (3, "odd", 37), (64, "all", 300),
+])
+def test_ring_equals_resident(moe, n_lines, offload, chunk):
+    wl = mi.custom_workload("ring", T=300, d=128, E=32, k=4, inter=64, inter_shared=128,
+                            zipf_s=1.1, seed=21)
+    E = wl.shape.n_experts
+    off = {"half": range(E // 2, E), "all": range(E), "odd": range(1, E, 2)}[offload]
+    params, L_res = place(wl)
+    x = mi.make_x(wl, device="cuda")
+    ref = moe.moe_prefill_layer(L_res, x, chunk)
+    ring = moe.Ring(L_res.shape, n_lines)
+    _, L_ring = place(wl, offloaded=off, ring=ring, params=params)
+    cs = torch.cuda.Stream()
+    got = moe.moe_prefill_layer(L_ring, x, chunk, copy_stream=cs)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(got["out"]), bits(ref["out"]))
+    st = ring.stats()
+    # every (chunk, used offloaded expert) pair is either a hit or a copy
+    cc = ref["chunk_counts"].cpu().numpy()
+    offset = np.zeros(E, bool)
+    offset[list(off)] = True
+    needed = int(((cc > 0) & offset[None, :]).sum())
+    assert st["hits"] + st["misses"] == needed
+    assert st["bytes_h2d"] == st["misses"] * ring.line_bytes
+    assert st["misses"] >= min(needed, len(set(np.nonzero(cc.sum(0) * offset)[0])))
+    ring.close()
+
+
+def test_ring_reuses_lines_across_calls(moe):
+    """A second run finds every expert still in its line when the ring holds them all."""
+    wl = mi.custom_workload("reuse", T=128, d=128, E=16, k=2, inter=64, inter_shared=64, seed=2)
+    params, L_res = place(wl)
+    ring = moe.Ring(L_res.shape, 16)
+    _, L = place(wl, offloaded=range(16), ring=ring, params=params)
+    x = mi.make_x(wl, device="cuda")
+    a = moe.moe_prefill_layer(L, x, 128)
+    s1 = ring.stats()
+    b = moe.moe_prefill_layer(L, x, 128)
+    torch.cuda.synchronize()
+    s2 = ring.stats()
+    assert torch.equal(bits(a["out"]), bits(b["out"]))
+    assert s2["misses"] == s1["misses"] and s2["hits"] - s1["hits"] == s1["misses"]
+    ring.invalidate()
+    moe.moe_prefill_layer(L, x, 128)
+    torch.cuda.synchronize()
+    assert ring.stats()["misses"] == 2 * s1["misses"]
+    ring.close()
+
+
+def test_stage_api_direct(moe):
+    """moe_stage_experts copies exactly the bank's line into the ring line it returns."""
+    wl = mi.custom_workload("stage", T=8, d=64, E=8, k=2, inter=64, inter_shared=0, seed=3)
+    params, L_res = place(wl)
+    ring = moe.Ring(L_res.shape, 3)
+    place(wl, offloaded=range(8), ring=ring, params=params)
+    cs = torch.cuda.Stream()
+    lines = moe.moe_stage_experts(ring, 0, [5, 2], copy_stream=cs)
+    assert len(set(lines)) == 2
+    ring.wait_ready(lines)
+    le = moe.line_elems(L_res.shape)
+    view = ring.lines.view(torch.bfloat16).view(3, le)
+    torch.cuda.synchronize()
+    assert torch.equal(view[lines[0]], params["lines"][5])
+    assert torch.equal(view[lines[1]], params["lines"][2])
+    # 3 lines, 2 held: staging two more misses fails and changes nothing
+    with pytest.raises(moe.MoeError, match="MOE_ERR_RING"):
+        moe.moe_stage_experts(ring, 0, [0, 1], copy_stream=cs)
+    assert ring.stats()["misses"] == 2
+    # a hit needs no free line
+    assert moe.moe_stage_experts(ring, 0, [5], copy_stream=cs) == [lines[0]]
+    ring.release(lines)
+    ring.release([lines[0]])
+    l3 = moe.moe_stage_experts(ring, 0, [0, 1], copy_stream=cs)
+    ring.wait_ready(l3)
+    torch.cuda.synchronize()
+    assert torch.equal(view[l3[0]], params["lines"][0])
+    assert torch.equal(view[l3[1]], params["lines"][1])
+    with pytest.raises(moe.MoeError, match="MOE_ERR_INVALID"):
+        moe.moe_stage_experts(ring, 0, [3, 3], copy_stream=cs)      # duplicate
+    with pytest.raises(moe.MoeError, match="MOE_ERR_RING"):
+        moe.moe_stage_experts(ring, 7, [1], copy_stream=cs)          # no bank for layer 7
+    ring.release(l3)
+    ring.close()
+
+
+def test_missing_bank_is_an_error(moe):
+    wl = mi.custom_workload("nobank", T=16, d=64, E=8, k=2, inter=64, inter_shared=0, seed=4)
+    params, L_res = place(wl)
+    x = mi.make_x(wl, device="cuda")
+    ring = moe.Ring(L_res.shape, 2)
+    lines = [params["lines"][e].cuda() for e in range(8)]
+    lines[3] = None
+    L = moe.Layer(L_res.shape, params["w_router"], None, lines, ring=ring, layer_id=4)
+    with pytest.raises(moe.MoeError, match="MOE_ERR_RING"):
+        moe.moe_prefill_layer(L, x, 16)
+    ring.close()
+
+
+def test_ring_create_unwinds_on_failure(moe):
+    """A failure while creating the ring's events returns MOE_ERR_HIP and leaves nothing
+    behind (checked in a child process, since the failure is injected by an environment
+    variable read at creation)."""
+    code = r"""
+import ctypes, torch, sys
+sys.path.insert(0, sys.argv[1])
+import routed_expert_grouped_moe_amd as moe
+sh = moe.make_shape(64, 8, 2, 64, 0)
+try:
+    moe.Ring(sh, 4)
+    print("created")
+except moe.MoeError as e:
+    print("failed", e.status)
+"""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    for n, want in (("3", "failed 4"), ("8", "failed 4"), ("0", "created")):
+        env = dict(os.environ, MOE_TEST_FAIL_EVENT_CREATE=n)
+        out = subprocess.run([sys.executable, "-c", code, root], env=env, capture_output=True,
+                             text=True, timeout=120)
+        assert want in out.stdout, (n, out.stdout, out.stderr[-500:])
+
+
+def test_offload_16022_ring64(moe):
+    """T = 16,022, every expert in a pinned bank, 64-line ring, chunk 2,048 (as specified):
+    bit-identical to the all-resident batched pass, and sampled rows match the oracle."""
+    wl = mi.WORKLOADS["offload_16022"]
+    print(f"[ring] {wl.name}: T={wl.T} E={wl.shape.n_experts} lines={wl.ring_lines}", flush=True)
+    params, L_res = place(wl)
+    x = mi.make_x(wl, device="cuda")
+    ref = moe.moe_prefill_layer(L_res, x, wl.T)
+    ring = moe.Ring(L_res.shape, wl.ring_lines)
+    _, L = place(wl, offloaded=range(wl.shape.n_experts), ring=ring, params=params)
+    got = moe.moe_prefill_layer(L, x, 2048, copy_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    assert torch.equal(bits(got["out"]), bits(ref["out"]))
+    st = ring.stats()
+    assert st["bytes_h2d"] == st["misses"] * ring.line_bytes and st["waves"] >= 8
+    # sampled oracle rows (the layer is per token)
+    rows = np.unique(np.concatenate([np.arange(0, wl.T, 499), [wl.T - 1]]))
+    op = oracle_params(params, wl)
+    xs = mi.to_numpy_exact(x)[rows]
+    ref_logits = orc.router_logits(xs, op["w_router"], op["router_bias"])
+    ids_use, _ = routing_gates(got["logits"].cpu().numpy()[rows], got["ids"].cpu().numpy()[rows],
+                               got["weights"].cpu().numpy()[rows], ref_logits, wl.shape.top_k)
+    err = rel_err(as_f64(got["out"])[rows], orc.moe_layer(xs, op, ids=ids_use)["out"])
+    print(f"[ring] sampled rel err {err:.3e}")
+    assert err <= 2e-2
+    ring.close()

@@ -80,6 +80,30 @@ def time_steps(fn, steps, warmup):
     return a.elapsed_time(b) / steps, wall
 
 
+def kernel_source_sha() -> str:
+    import hashlib
+    p = os.path.join(ROOT, "routed_expert_grouped_moe_amd", "csrc", "gemm.hip")
+    with open(p, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or None when the
+    summary is missing or was taken on a different kernel source."""
+    p = os.path.join(ROOT, "profiles", "hbm_traffic_T16022_batched.md")
+    if not os.path.exists(p):
+        return None
+    text = open(p).read()
+    start = text.find("```json")
+    if start < 0:
+        return None
+    blob = json.loads(text[start + 7: text.find("```", start + 7)])
+    if blob.get("source_sha256") != kernel_source_sha():
+        return None
+    k = blob.get("kernels", {}).get(kernel)
+    return None if k is None else int(k["traffic_bytes_per_launch"])
+
+
 def copy_probe(nbytes: int, runs: int) -> float:
     """A plain copy kernel: out = in * 1 over nbytes of fp32 (reads and writes nbytes each)."""
     import torch
@@ -195,12 +219,12 @@ def main():
     if t_hbm >= t_mfma:
         ach = (b / n_l) / avg_s / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": 8000.0,
-                "unit": "GB/s", "frac": round(ach / 8000.0, 4), "traffic": None,
+                "unit": "GB/s", "frac": round(ach / 8000.0, 4), "traffic": measured_traffic(dom),
                 "bytes_per_launch": int(b / n_l), "avg_launch_us": round(avg_s * 1e6, 2)}
     else:
         ach = (f / n_l) / avg_s / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": 2500.0,
-                "unit": "TFLOP/s", "frac": round(ach / 2500.0, 4), "traffic": None,
+                "unit": "TFLOP/s", "frac": round(ach / 2500.0, 4), "traffic": measured_traffic(dom),
                 "flops_per_launch": int(f / n_l), "avg_launch_us": round(avg_s * 1e6, 2)}
 
     variants = {}

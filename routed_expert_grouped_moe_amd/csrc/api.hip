@@ -3,6 +3,7 @@
 #include <string.h>
 
 #include <algorithm>
+#include <unordered_map>
 #include <vector>
 
 #include "ring.h"
@@ -80,6 +81,52 @@ moe_status check_experts(const moe_layer* L, bool* offloaded) {
   }
   return MOE_OK;
 }
+
+// A side stream for work that may run beside the caller's stream, with a fork event (the
+// side stream waits for everything the caller enqueued before it) and a done event (the
+// caller's stream waits for the side work). One set per host thread and device, created on
+// first use and kept for the life of the thread; default priority.
+struct SideStream {
+  hipStream_t stream = nullptr;
+  hipEvent_t fork_ev = nullptr;
+  hipEvent_t done_ev = nullptr;
+
+  hipError_t acquire() {
+    struct Entry {
+      hipStream_t s = nullptr;
+      hipEvent_t f = nullptr, d = nullptr;
+    };
+    thread_local std::unordered_map<int, Entry> cache;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    Entry& en = cache[dev];
+    if (!en.s) {
+      e = hipStreamCreateWithFlags(&en.s, hipStreamNonBlocking);
+      if (e != hipSuccess) { en.s = nullptr; return e; }
+    }
+    if (!en.f) {
+      e = hipEventCreateWithFlags(&en.f, hipEventDisableTiming);
+      if (e != hipSuccess) { en.f = nullptr; return e; }
+    }
+    if (!en.d) {
+      e = hipEventCreateWithFlags(&en.d, hipEventDisableTiming);
+      if (e != hipSuccess) { en.d = nullptr; return e; }
+    }
+    stream = en.s;
+    fork_ev = en.f;
+    done_ev = en.d;
+    return hipSuccess;
+  }
+  hipError_t fork(hipStream_t s) {
+    hipError_t e = acquire();
+    if (e == hipSuccess) e = hipEventRecord(fork_ev, s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(stream, fork_ev, 0);
+    return e;
+  }
+  hipError_t record_done() { return hipEventRecord(done_ev, stream); }
+  hipError_t join(hipStream_t s) { return hipStreamWaitEvent(s, done_ev, 0); }
+};
 
 #define MOE_HIP(call)                                                                      \
   do {                                                                                     \
@@ -204,16 +251,27 @@ moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const i
                      ws_bytes, W.total, static_cast<long long>(n));
   char* ws = static_cast<char*>(ws_v);
   const void** wtab = reinterpret_cast<const void**>(ws + W.wtab);
+  float* sbuf = sh.inter_shared ? reinterpret_cast<float*>(ws + W.s) : nullptr;
+  // The shared expert depends only on x. With every expert resident it runs in order on
+  // the caller's stream: its GEMMs and the routed ones each fill the chip, and running them
+  // side by side measured slower than in sequence. With a ring it runs on a side stream
+  // (joined before the combine), filling the time the routed GEMMs wait for copies.
+  SideStream side;
+  hipStream_t ss = offloaded ? nullptr : s;
+  if (sh.inter_shared) {
+    if (offloaded) {
+      MOE_HIP(side.fork(s));
+      ss = side.stream;
+    }
+    MOE_HIP(launch_gu_dense(sh.dtype, x, t0, n, sh.d, sh.inter_shared, L->w_gu_shared,
+                            ws + W.h_shared, ss));
+    MOE_HIP(launch_down_dense(sh.dtype, ws + W.h_shared, n, sh.d, sh.inter_shared,
+                              L->w_down_shared, sbuf, ss));
+    if (offloaded) MOE_HIP(side.record_done());
+  }
   MOE_HIP(launch_upload_ptrs(wtab, L->expert_lines, 0, E, s));
   const int bm = routed_tile_rows(n, k, E);
   MOE_HIP(launch_bucket(ids + t0 * k, n, k, E, bm, ws, W, s));
-  float* sbuf = sh.inter_shared ? reinterpret_cast<float*>(ws + W.s) : nullptr;
-  if (sh.inter_shared) {       // the shared expert needs no staging: enqueue it first
-    MOE_HIP(launch_gu_dense(sh.dtype, x, t0, n, sh.d, sh.inter_shared, L->w_gu_shared,
-                            ws + W.h_shared, s));
-    MOE_HIP(launch_down_dense(sh.dtype, ws + W.h_shared, n, sh.d, sh.inter_shared,
-                              L->w_down_shared, sbuf, s));
-  }
   float* y = reinterpret_cast<float*>(ws + W.y);
   if (!offloaded) {
     GemmGroups g{reinterpret_cast<const MTile*>(ws + W.mtiles),
@@ -227,6 +285,8 @@ moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const i
                                reinterpret_cast<const int32_t*>(ws + W.row_slot), y, s));
   } else {
     moe_status st = ring_waves(L, x, t0, n, counts_host, ws, W, s, cs ? cs : s);
+    // Join even on failure, so the caller's stream never runs ahead of the side work.
+    if (sh.inter_shared) MOE_HIP(side.join(s));
     if (st != MOE_OK) return st;
   }
   MOE_HIP(launch_combine(sh.dtype, y, sbuf, weights, t0, n, k, sh.d, out, s));

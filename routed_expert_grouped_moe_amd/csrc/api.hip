@@ -128,6 +128,16 @@ struct SideStream {
   hipError_t join(hipStream_t s) { return hipStreamWaitEvent(s, done_ev, 0); }
 };
 
+// True when line e is at lines[0] + e * stride for every e (one block of E lines).
+bool uniform_lines(const void* const* lines, int E, int64_t* stride) {
+  const uintptr_t b = reinterpret_cast<uintptr_t>(lines[0]);
+  const uintptr_t st = E > 1 ? reinterpret_cast<uintptr_t>(lines[1]) - b : 0;
+  for (int e = 0; e < E; ++e)
+    if (reinterpret_cast<uintptr_t>(lines[e]) != b + static_cast<uintptr_t>(e) * st) return false;
+  *stride = static_cast<int64_t>(st);
+  return true;
+}
+
 #define MOE_HIP(call)                                                                      \
   do {                                                                                     \
     hipError_t e_ = (call);                                                                \
@@ -197,7 +207,7 @@ moe_status ring_waves(const moe_layer* L, const void* x, int64_t t0, int64_t n,
   GemmGroups g{reinterpret_cast<const MTile*>(ws + W.mtiles),
                reinterpret_cast<const int32_t*>(ws + W.meta) + kMetaMTiles,
                reinterpret_cast<const int32_t*>(ws + W.offsets),
-               reinterpret_cast<const int32_t*>(ws + W.counts), wtab, 0, 0, bm};
+               reinterpret_cast<const int32_t*>(ws + W.counts), wtab, nullptr, 0, 0, 0, bm};
   const int32_t* row_tok = reinterpret_cast<const int32_t*>(ws + W.row_tok);
   const int32_t* row_slot = reinterpret_cast<const int32_t*>(ws + W.row_slot);
   char* h = ws + W.h;
@@ -269,7 +279,11 @@ moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const i
                               L->w_down_shared, sbuf, ss));
     if (offloaded) MOE_HIP(side.record_done());
   }
-  MOE_HIP(launch_upload_ptrs(wtab, L->expert_lines, 0, E, s));
+  // Resident lines at a uniform stride (one block of E lines) need no table; otherwise the
+  // table is uploaded to the workspace (offloaded entries are filled per wave).
+  int64_t stride = 0;
+  const bool uniform = !offloaded && uniform_lines(L->expert_lines, E, &stride);
+  if (!uniform) MOE_HIP(launch_upload_ptrs(wtab, L->expert_lines, 0, E, s));
   const int bm = routed_tile_rows(n, k, E);
   MOE_HIP(launch_bucket(ids + t0 * k, n, k, E, bm, ws, W, s));
   float* y = reinterpret_cast<float*>(ws + W.y);
@@ -277,7 +291,8 @@ moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const i
     GemmGroups g{reinterpret_cast<const MTile*>(ws + W.mtiles),
                  reinterpret_cast<const int32_t*>(ws + W.meta) + kMetaMTiles,
                  reinterpret_cast<const int32_t*>(ws + W.offsets),
-                 reinterpret_cast<const int32_t*>(ws + W.counts), wtab, 0,
+                 reinterpret_cast<const int32_t*>(ws + W.counts), wtab,
+                 uniform ? static_cast<const char*>(L->expert_lines[0]) : nullptr, stride, 0,
                  static_cast<int>(n * k / bm + std::min<int64_t>(E, n * k)), bm};
     MOE_HIP(launch_gu_routed(sh.dtype, x, t0, sh.d, sh.inter, g,
                              reinterpret_cast<const int32_t*>(ws + W.row_tok), ws + W.h, s));

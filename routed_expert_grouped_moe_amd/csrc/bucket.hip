@@ -49,10 +49,18 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
   const int e = threadIdx.x;
   int32_t run = 0;
   if (e < E) {
-    for (int b = 0; b < nb; ++b) {
-      const int64_t i = static_cast<int64_t>(b) * E + e;
-      blk_base[i] = run;
-      run += blk_counts[i];
+    constexpr int kBatch = 16;           // loads of a batch are issued before their sums
+    for (int b0 = 0; b0 < nb; b0 += kBatch) {
+      int32_t c[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        c[j] = b0 + j < nb ? blk_counts[static_cast<int64_t>(b0 + j) * E + e] : 0;
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j)
+        if (b0 + j < nb) {
+          blk_base[static_cast<int64_t>(b0 + j) * E + e] = run;
+          run += c[j];
+        }
     }
     counts[e] = run;
   }

@@ -37,33 +37,79 @@ template <> struct Pack4<float> {
 //   out = round(acc)    (one rounding to the storage type, bf16 round-to-nearest-even)
 // y_j is the unweighted fp32 row expert j wrote for this token; the order never depends on
 // the chunk, the expert's row count or where the expert ran.
+//
+// Y is read once: non-temporal loads keep it from displacing cached data.
+__device__ __forceinline__ float4 load_stream(const float* p) {
+  const f32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(p));
+  return make_float4(v[0], v[1], v[2], v[3]);
+}
+
+// A thread owns 4-column groups c and c + 1024 (d = 2048 is one pass) and issues the loads of
+// 8 expert rows before their FMAs, which run in the same ascending order.
 template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ y,
                                                       const float* __restrict__ shared,
                                                       const float* __restrict__ weights,
                                                       int64_t t0, int k, int d,
                                                       T* __restrict__ out) {
+  constexpr int U = 2, J = 8;
   const int64_t t = blockIdx.x;                       // token within the chunk
   const float* wt = weights + (t0 + t) * k;
   const float* yt = y + t * k * static_cast<int64_t>(d);
-  for (int c = threadIdx.x * 4; c < d; c += 1024) {
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
+  for (int c0 = threadIdx.x * 4; c0 < d; c0 += 1024 * U) {
+    float4 acc[U];
+    bool on[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      on[u] = c0 + 1024 * u < d;
+    }
+    int j = 0;
+    for (; j + J <= k; j += J) {
+      float4 v[J][U];
+#pragma unroll
+      for (int i = 0; i < J; ++i)
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+          if (on[u])
+            v[i][u] = load_stream(yt + static_cast<int64_t>(j + i) * d + c0 + 1024 * u);
+#pragma unroll
+      for (int i = 0; i < J; ++i) {
+        const float wj = wt[j + i];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          acc[u].x = fmaf(wj, v[i][u].x, acc[u].x);
+          acc[u].y = fmaf(wj, v[i][u].y, acc[u].y);
+          acc[u].z = fmaf(wj, v[i][u].z, acc[u].z);
+          acc[u].w = fmaf(wj, v[i][u].w, acc[u].w);
+        }
+      }
+    }
+    for (; j < k; ++j) {
       const float wj = wt[j];
-      const float4 v = *reinterpret_cast<const float4*>(yt + static_cast<int64_t>(j) * d + c);
-      acc.x = fmaf(wj, v.x, acc.x);
-      acc.y = fmaf(wj, v.y, acc.y);
-      acc.z = fmaf(wj, v.z, acc.z);
-      acc.w = fmaf(wj, v.w, acc.w);
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+        if (on[u]) {
+          const float4 v = load_stream(yt + static_cast<int64_t>(j) * d + c0 + 1024 * u);
+          acc[u].x = fmaf(wj, v.x, acc[u].x);
+          acc[u].y = fmaf(wj, v.y, acc[u].y);
+          acc[u].z = fmaf(wj, v.z, acc[u].z);
+          acc[u].w = fmaf(wj, v.w, acc[u].w);
+        }
     }
-    if (shared) {
-      const float4 s = *reinterpret_cast<const float4*>(shared + t * d + c);
-      acc.x += s.x;
-      acc.y += s.y;
-      acc.z += s.z;
-      acc.w += s.w;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (!on[u]) continue;
+      const int c = c0 + 1024 * u;
+      if (shared) {
+        const float4 s = *reinterpret_cast<const float4*>(shared + t * d + c);
+        acc[u].x += s.x;
+        acc[u].y += s.y;
+        acc[u].z += s.z;
+        acc[u].w += s.w;
+      }
+      Pack4<T>::store(out + (t0 + t) * d + c, acc[u]);
     }
-    Pack4<T>::store(out + (t0 + t) * d + c, acc);
   }
 }
 

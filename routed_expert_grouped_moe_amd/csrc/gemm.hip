@@ -232,6 +232,12 @@ struct GuParams {
   void* h;                // [rows, I] out
 };
 
+// Start of expert e's line: from the uniform layout when there is one, else from the table.
+__device__ __forceinline__ const char* line_of(const GemmGroups& g, int e) {
+  return g.lines0 ? g.lines0 + static_cast<int64_t>(e) * g.line_stride
+                  : static_cast<const char*>(g.wtab[e]);
+}
+
 template <typename T, class TL, bool kGrouped>
 __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(2)))
 void gu_kernel(GuParams p) {
@@ -251,7 +257,7 @@ void gu_kernel(GuParams p) {
     const MTile mt = p.g.mtiles[p.g.tile_lo + mi];
     row0 = static_cast<int64_t>(p.g.offsets[mt.group]) + mt.m0;
     rows = min(TL::BM, p.g.counts[mt.group] - mt.m0);
-    wbase = static_cast<const char*>(p.g.wtab[mt.group]);
+    wbase = line_of(p.g, mt.group);
   } else {
     row0 = static_cast<int64_t>(mi) * TL::BM;
     rows = static_cast<int>(min<int64_t>(TL::BM, p.n - row0));
@@ -329,7 +335,7 @@ void down_kernel(DownParams p) {
     rows = min(TL::BM, p.g.counts[mt.group] - m0);
     if (rows <= 0) return;
     row0 = static_cast<int64_t>(p.g.offsets[mt.group]) + m0;
-    const char* line = static_cast<const char*>(p.g.wtab[mt.group]);
+    const char* line = line_of(p.g, mt.group);
     wbase = line ? line + p.line_down_off * static_cast<int64_t>(sizeof(T)) : nullptr;
   } else {
     row0 = static_cast<int64_t>(mi) * TL::BM;

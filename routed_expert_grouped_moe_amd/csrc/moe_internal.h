@@ -61,7 +61,9 @@ struct GemmGroups {               // routed (grouped) problem description
   const int32_t* n_mtiles;        // device scalar
   const int32_t* offsets;         // [E+1]
   const int32_t* counts;          // [E]
-  const void* const* wtab;        // [E] expert line pointers
+  const void* const* wtab;        // [E] expert line pointers (used when lines0 is NULL)
+  const char* lines0;             // else line e starts at lines0 + e * line_stride
+  int64_t line_stride;            // bytes
   int tile_lo;                    // first M-tile of this launch
   int tile_cap;                   // M-tiles this launch may cover (upper bound)
   int tile_rows;                  // M-tile height the tile list was built with

@@ -85,6 +85,48 @@ def test_edge_shapes(moe, case):
     _full_parity(moe, wl, BF16_TOL, chunks=chunks)
 
 
+def test_topk_ties_and_special_values(moe):
+    """Top-k on logits with exact ties (duplicated router rows), NaN and -inf (from the bias),
+    an all-NaN token and a zero token, with E = 130 (ragged lane slices). The ids equal the
+    oracle's selection on the GPU's own logits with NaN read as -inf (lower id first among
+    equal values); the weights match the oracle's to fp32 rounding."""
+    wl = mi.custom_workload("topk", T=200, d=64, E=130, k=5, inter=64, inter_shared=0,
+                            zipf_s=1.1, seed=21)
+    p = mi.make_layer(wl, 0, device="cuda")
+    w, b = p["w_router"], p["router_bias"]
+    w[10:20] = w[10].clone()
+    w[100:130] = w[3].clone()
+    b.zero_()
+    b[50] = float("nan")
+    b[51] = float("-inf")
+    b[60] = 30.0
+    params, L = place(wl, params=p)
+    x = mi.make_x(wl, device="cuda")
+    x[7] = float("nan")
+    x[8] = 0
+    r = moe.moe_prefill_route(L, x, 64)
+    torch.cuda.synchronize()
+    logits = r["logits"].cpu().numpy().astype(np.float64)
+    lg = np.where(np.isnan(logits), -np.inf, logits)
+    ids = r["ids"].cpu().numpy()
+    assert np.array_equal(ids, orc.select_topk(lg, wl.shape.top_k))
+    assert list(ids[7]) == [0, 1, 2, 3, 4]          # every logit NaN: five lowest ids
+    assert list(ids[8]) == [0, 1, 2, 3, 60]         # logits = bias: 30, then ties at 0
+    assert np.all(np.isin(ids, [50, 51], invert=True)[np.arange(wl.T) != 7])
+    ok = ~np.isnan(logits).all(axis=1)
+    wts = r["weights"].cpu().numpy()
+    w_ref = orc.topk_weights(lg[ok], ids[ok])
+    assert np.max(np.abs(w_ref - wts[ok])) <= 2e-6
+    assert np.array_equal(r["chunk_counts"].cpu().numpy(),
+                          orc.chunk_counts(ids, 64, wl.shape.n_experts))
+    # chunk 1: a 256-token block spans more (chunk, expert) bins than its LDS histogram holds
+    r1 = moe.moe_prefill_route(L, x, 1)
+    torch.cuda.synchronize()
+    assert np.array_equal(r1["ids"].cpu().numpy(), ids)
+    assert np.array_equal(r1["chunk_counts"].cpu().numpy(),
+                          orc.chunk_counts(ids, 1, wl.shape.n_experts))
+
+
 def test_member_lists_bit_exact(moe):
     """The GPU's expert-major member lists equal the oracle's, integer for integer."""
     wl = mi.custom_workload("lists", T=1000, d=128, E=16, k=4, inter=64, inter_shared=64,

@@ -14,8 +14,10 @@ the fused SiLU epilogue, and the combine.
 Prints one JSON line (stdout). Per-kernel times come from HIP events that the library records
 around each of its launches on the launch's own stream, over a second pass of the same K
 steps (the headline time comes from a pass without those events). Also reported: the same
-layer at deep chunk 2,048, the layer with all experts streamed from a pinned host bank
-through a 64-line ring at chunk 2,048, and the fp64 CPU oracle on a bounded sample.
+layer at deep chunks 2,048 / 4,096 / 8,192, the layer with all experts streamed from a pinned
+host bank through a 64-line ring at chunk 2,048 (with the measured host-link rate and the
+share of compute hidden under the copies), an 8-layer stack (T = 32,700, Zipf routing, half
+the experts through one 128-line ring), and the fp64 CPU oracle on a bounded sample.
 """
 from __future__ import annotations
 
@@ -64,20 +66,84 @@ def algorithmic(stage: str, T: int, sh, counts):
 
 
 def time_steps(fn, steps, warmup):
+    """(mean ms per step over the K steps, wall ms per step, per-step ms list). HIP events on
+    the current stream bracket the K steps, and each step separately."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     w0 = time.perf_counter()
-    a.record()
-    for _ in range(steps):
+    ev[0].record()
+    for i in range(steps):
         fn()
-    b.record()
+        ev[i + 1].record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - w0) * 1e3 / steps
-    return a.elapsed_time(b) / steps, wall
+    per = [ev[i].elapsed_time(ev[i + 1]) for i in range(steps)]
+    return ev[0].elapsed_time(ev[steps]) / steps, wall, per
+
+
+def spread(per):
+    import numpy as np
+    a = np.asarray(per)
+    return {"median": round(float(np.median(a)), 4), "min": round(float(a.min()), 4),
+            "max": round(float(a.max()), 4)}
+
+
+def h2d_probe(nbytes: int, runs: int) -> float:
+    """Pinned host -> HBM copy rate (GB/s) of one nbytes transfer on a side stream."""
+    import torch
+    src = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    s = torch.cuda.Stream()
+    best = float("inf")
+    for _ in range(runs):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(s):
+            dst.copy_(src, non_blocking=True)
+        s.synchronize()
+        best = min(best, time.perf_counter() - t0)
+    return nbytes / best / 1e9
+
+
+def stack_variant(steps: int):
+    """The 8-layer stack (T = 32,700, Zipf(1.5) routing, RMSNorm + residual between layers,
+    experts 256..511 of every layer in pinned banks streamed through one 128-line ring,
+    chunk 2,048): one untimed pass, then `steps` timed passes."""
+    import torch
+
+    import moe_inputs as mi
+    import routed_expert_grouped_moe_amd as moe
+    from tests.parity import place
+    wl = mi.WORKLOADS["stack_32700"]
+    E = wl.shape.n_experts
+    off = range(E - wl.n_offloaded, E)
+    ring, layers = None, []
+    for layer in range(wl.n_layers):
+        p = mi.make_layer(wl, layer, device="cuda")
+        if ring is None:
+            from tests.parity import moe_shape
+            ring = moe.Ring(moe_shape(wl), wl.ring_lines)
+        layers.append(place(wl, layer=layer, offloaded=off, ring=ring, params=p)[1])
+        del p
+    x = mi.make_x(wl, device="cuda")
+    cs = torch.cuda.Stream()
+    run = lambda: moe.moe_prefill_stack(layers, x, 2048, wl.rmsnorm_eps, copy_stream=cs)
+    run()
+    torch.cuda.synchronize()
+    ring.reset_stats()
+    _, wall, per = time_steps(run, steps, 0)
+    st = ring.stats()
+    ring.close()
+    looks = st["hits"] + st["misses"]
+    return {"workload": f"stack_{wl.n_layers}x_T{wl.T}_zipf1.5_ring{wl.ring_lines}_chunk2048",
+            "tokens_per_s": round(wl.T / (wall / 1e3), 1), "ms_per_pass": round(wall, 1),
+            "pass_ms": spread(per), "ring_hit_rate": round(st["hits"] / max(1, looks), 4),
+            "ring_lookups_per_pass": looks // steps,
+            "h2d_gb_per_pass": round(st["bytes_h2d"] / steps / 1e9, 2),
+            "h2d_gbps": round(st["bytes_h2d"] / steps / (wall / 1e3) / 1e9, 2)}
 
 
 def kernel_source_sha() -> str:
@@ -109,7 +175,7 @@ def copy_probe(nbytes: int, runs: int) -> float:
     import torch
     a = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
-    ms, _ = time_steps(lambda: torch.mul(a, 1.0, out=b), runs, 1)
+    ms, _, _ = time_steps(lambda: torch.mul(a, 1.0, out=b), runs, 1)
     return 2 * a.numel() * 4 / (ms / 1e3) / 1e9
 
 
@@ -144,6 +210,8 @@ def main():
     ap.add_argument("--cpu-sample-tokens", type=int, default=384)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
+    ap.add_argument("--no-stack", action="store_true",
+                    help="skip the 8-layer T=32,700 stack variant (about a minute)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain fp32 copy kernel (out = in * 1) over BYTES bytes "
                          "5 times and print its bandwidth (calibrates HBM byte counters)")
@@ -179,12 +247,12 @@ def main():
     bufs = moe.layer_buffers(L, T, T)
     step = lambda: moe.moe_prefill_layer(L, x, T, bufs=bufs)
     log(f"[bench] batched pass: warmup {args.warmup}, steps {args.steps}")
-    ms, wall_ms = time_steps(step, args.steps, args.warmup)
+    ms, wall_ms, per_step = time_steps(step, args.steps, args.warmup)
     counts = bufs["chunk_counts"][0].cpu().numpy()
 
     moe.moe_profile_read(reset=True)
     moe.moe_profile_enable(True)
-    ms_prof, _ = time_steps(step, args.steps, 0)
+    ms_prof, _, _ = time_steps(step, args.steps, 0)
     moe.moe_profile_enable(False)
     prof = moe.moe_profile_read(reset=True)
 
@@ -229,28 +297,46 @@ def main():
 
     variants = {}
     if not args.no_variants:
-        b2 = moe.layer_buffers(L, T, 2048)
-        v_ms, _ = time_steps(lambda: moe.moe_prefill_layer(L, x, 2048, bufs=b2), max(3, args.steps // 2), 2)
-        ok = torch.equal(b2["out"].view(torch.int16), bufs["out"].view(torch.int16))
-        variants["resident_chunk2048"] = {"tokens_per_s": round(T / (v_ms / 1e3), 1),
-                                          "ms_per_step": round(v_ms, 3),
-                                          "bit_identical_to_batched": bool(ok)}
-        del b2
+        for c in (2048, 4096, 8192):
+            b2 = moe.layer_buffers(L, T, c)
+            v_ms, _, v_per = time_steps(lambda: moe.moe_prefill_layer(L, x, c, bufs=b2),
+                                        max(3, args.steps // 2), 2)
+            ok = torch.equal(b2["out"].view(torch.int16), bufs["out"].view(torch.int16))
+            variants[f"resident_chunk{c}"] = {"tokens_per_s": round(T / (v_ms / 1e3), 1),
+                                              "ms_per_step": round(v_ms, 3), "step_ms": spread(v_per),
+                                              "bit_identical_to_batched": bool(ok)}
+            del b2
         log("[bench] ring variant: all 512 experts in a pinned bank, 64 lines, chunk 2048")
         ring = moe.Ring(sh, 64)
         _, Lr = place(wl, offloaded=range(sh.n_experts), ring=ring, params=params)
         br = moe.layer_buffers(Lr, T, 2048)
         cs = torch.cuda.Stream()
-        r_ms, r_wall = time_steps(lambda: moe.moe_prefill_layer(Lr, x, 2048, bufs=br, copy_stream=cs), 3, 1)
+        ring_step = lambda: moe.moe_prefill_layer(Lr, x, 2048, bufs=br, copy_stream=cs)
+        ring_step()
+        torch.cuda.synchronize()
+        ring.reset_stats()
+        r_ms, r_wall, r_per = time_steps(ring_step, 3, 0)
         ok = torch.equal(br["out"].view(torch.int16), bufs["out"].view(torch.int16))
         st = ring.stats()
+        per_step_bytes = st["bytes_h2d"] / 3
+        link = h2d_probe(1 << 30, 3)
+        t_copy = per_step_bytes / (link * 1e9) * 1e3                  # ms, copies alone
+        t_gemm = variants["resident_chunk2048"]["ms_per_step"]        # ms, compute alone
+        hidden = (t_copy + t_gemm - r_wall) / t_gemm
         variants["offload_ring64_chunk2048"] = {
             "tokens_per_s": round(T / (r_wall / 1e3), 1), "ms_per_step": round(r_wall, 2),
-            "h2d_gb_per_step": round(st["bytes_h2d"] / 4 / 1e9, 3),
-            "h2d_gbps": round(st["bytes_h2d"] / 4 / (r_wall / 1e3) / 1e9, 2),
+            "step_ms": spread(r_per),
+            "h2d_gb_per_step": round(per_step_bytes / 1e9, 3),
+            "h2d_gbps": round(per_step_bytes / (r_wall / 1e3) / 1e9, 2),
+            "h2d_link_gbps_measured": round(link, 2),
+            "compute_hidden_under_copies_frac": round(max(0.0, min(1.0, hidden)), 3),
             "bit_identical_to_batched": bool(ok)}
         del br, Lr
         ring.close()
+        if not args.no_stack:
+            log("[bench] stack variant: 8 layers, T=32,700, 128-line ring")
+            variants["stack"] = stack_variant(1)
+            torch.cuda.empty_cache()
 
     copy_gbps = copy_probe(1 << 30, 5)
     cpu = None
@@ -261,6 +347,7 @@ def main():
     line = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,
         "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(ms, 4),
+        "step_ms": spread(per_step),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic: seeded Gaussian activations and random-init weights "
                 "(1/sqrt(fan_in)), router std 0.02, uniform routing",

@@ -158,9 +158,14 @@ moe_status route_impl(const moe_layer* L, const void* x, int64_t T, int64_t chun
 
 // Routed GEMMs of a chunk whose experts come partly from the ring: the chunk's used
 // offloaded experts, in ascending id, are cut into waves of at most n_lines/2 experts; wave w
-// covers the expert-id range [lo_w, hi_w) (resident experts in that range run with it). Wave
-// w+1 is staged on the copy stream before wave w's GEMMs are enqueued, so copies overlap
-// compute; each wave waits for its lines' `ready` events and then records their `release`.
+// covers the expert-id range [lo_w, hi_w) (resident experts in that range run with it). The
+// waves run in ascending order on even passes of the ring and descending on odd ones
+// (boustrophedon): the lines the last pass left behind are the first ones this pass asks for.
+// The wave after the current one is staged on the copy stream before the current wave's GEMMs
+// are enqueued, so copies overlap compute; each wave waits for its lines' `ready` events and
+// then records their `release`. Misses evict lines this pass will not ask for again first.
+// The order of the waves never changes a result bit: each expert's rows are computed alone
+// and the combine sums in ascending expert id.
 moe_status ring_waves(const moe_layer* L, const void* x, int64_t t0, int64_t n,
                       const int32_t* counts_host, char* ws, const WsLayout& W, hipStream_t s,
                       hipStream_t cs) {
@@ -194,14 +199,19 @@ moe_status ring_waves(const moe_layer* L, const void* x, int64_t t0, int64_t n,
   const int nw = std::max<int>(1, (static_cast<int>(used.size()) + per_wave - 1) / per_wave);
   std::vector<std::vector<int32_t>> wexp(nw), wlines(nw);
   std::vector<int32_t> lo(nw), hi(nw);
+  const bool down = (R->sweeps++ & 1) != 0;
   for (int w = 0; w < nw; ++w) {
     const size_t b = static_cast<size_t>(w) * per_wave;
     const size_t e = std::min(used.size(), b + per_wave);
     for (size_t i = b; i < e; ++i) wexp[w].push_back(used[i]);
+    if (down) std::reverse(wexp[w].begin(), wexp[w].end());
     wlines[w].resize(wexp[w].size());
     lo[w] = w == 0 ? 0 : hi[w - 1];
     hi[w] = (w + 1 < nw) ? used[static_cast<size_t>(w + 1) * per_wave] : E;
   }
+  auto wave_at = [&](int i) { return down ? nw - 1 - i : i; };   // processing order
+  std::vector<char> later(E, 0);
+  for (int e : used) later[e] = 1;
 
   const void** wtab = reinterpret_cast<const void**>(ws + W.wtab);
   GemmGroups g{reinterpret_cast<const MTile*>(ws + W.mtiles),
@@ -213,18 +223,23 @@ moe_status ring_waves(const moe_layer* L, const void* x, int64_t t0, int64_t n,
   char* h = ws + W.h;
   float* y = reinterpret_cast<float*>(ws + W.y);
 
-  int staged = 0;
+  int staged = 0;                              // waves staged, in processing order
   moe_status st = MOE_OK;
   auto release_held = [&](int from) {          // unwind: give back lines of unfinished waves
-    for (int w = from; w < staged; ++w)
+    for (int i = from; i < staged; ++i) {
+      const int w = wave_at(i);
       (void)ring_release(R, wlines[w].data(), static_cast<int32_t>(wlines[w].size()), s);
+    }
   };
-  for (int w = 0; w < nw; ++w) {
-    while (staged < nw && staged <= w + 1) {   // this wave, and the next one if lines allow
-      st = ring_stage(R, L->layer_id, wexp[staged].data(),
-                      static_cast<int32_t>(wexp[staged].size()), cs, wlines[staged].data());
-      if (st == MOE_ERR_RING && staged > w) { st = MOE_OK; break; }   // retry after release
-      if (st != MOE_OK) { release_held(w); return st; }
+  for (int i = 0; i < nw; ++i) {
+    const int w = wave_at(i);
+    while (staged < nw && staged <= i + 1) {   // this wave, and the next one if lines allow
+      const int ws_ = wave_at(staged);
+      for (int e : wexp[ws_]) later[e] = 0;
+      st = ring_stage(R, L->layer_id, wexp[ws_].data(), static_cast<int32_t>(wexp[ws_].size()),
+                      cs, wlines[ws_].data(), &later);
+      if (st == MOE_ERR_RING && staged > i) { st = MOE_OK; break; }   // retry after release
+      if (st != MOE_OK) { release_held(i); return st; }
       ++staged;
     }
     const int32_t nl = static_cast<int32_t>(wlines[w].size());
@@ -243,7 +258,7 @@ moe_status ring_waves(const moe_layer* L, const void* x, int64_t t0, int64_t n,
       st = set_error(MOE_ERR_HIP, "wave %d launch: %s", w, hipGetErrorString(err));
     moe_status rst = ring_release(R, wlines[w].data(), nl, s);
     if (st == MOE_OK) st = rst;
-    if (st != MOE_OK) { release_held(w + 1); return st; }
+    if (st != MOE_OK) { release_held(i + 1); return st; }
     R->stats.waves++;
   }
   return MOE_OK;

@@ -424,9 +424,10 @@ void router_kernel(RouterParams p) {
   store_slab<TL, float, TL::TN>(lds, val, row_of, p.logits, p.E, col0, min(TL::TN, p.E - col0));
 }
 
-// Big tiles when they still give the chip at least two workgroups per CU, else small ones.
+// Big tiles when they still give the chip about two workgroups per CU (384 of them: 1.5 per
+// CU), else small ones.
 inline bool use_big_dense(int64_t n, int64_t n_tiles_big) {
-  return n >= BigTile::BM && ((n + BigTile::BM - 1) / BigTile::BM) * n_tiles_big >= 512;
+  return n >= BigTile::BM && ((n + BigTile::BM - 1) / BigTile::BM) * n_tiles_big >= 384;
 }
 
 }  // namespace

@@ -31,6 +31,7 @@ struct moe_ring {
   std::unordered_map<int64_t, int32_t> where;   // (layer << 32 | expert) -> line
   std::unordered_map<int32_t, Bank> banks;
   uint64_t clock = 0;
+  uint64_t sweeps = 0;            // chunk passes planned; odd passes walk experts downward
   uint64_t release_counter = 0;
   // Release-epoch coalescing: the copy stream `coal_copy` has already waited for every
   // release recorded on `coal_rel` up to epoch `waited_seq`, so older releases need no wait.
@@ -47,8 +48,13 @@ inline int64_t ring_key(int32_t layer, int32_t expert) {
 
 // Implementations of the ABI calls, used by the chunk sequencer too (no argument checks
 // beyond the ring's own; set the thread's last error on failure).
+// later (optional, indexed by expert of `layer`): experts that further stagings of the same
+// pass will ask for. A miss then evicts, least recently used first, a line that holds none of
+// them when there is one (a near-Belady choice for the known rest of the pass), else the least
+// recently used line.
 MOE_HIDDEN moe_status ring_stage(moe_ring* r, int32_t layer, const int32_t* experts, int32_t n,
-                                 hipStream_t copy_stream, int32_t* lines_out);
+                                 hipStream_t copy_stream, int32_t* lines_out,
+                                 const std::vector<char>* later = nullptr);
 MOE_HIDDEN moe_status ring_wait_ready(moe_ring* r, const int32_t* lines, int32_t n,
                                       hipStream_t stream);
 MOE_HIDDEN moe_status ring_release(moe_ring* r, const int32_t* lines, int32_t n,

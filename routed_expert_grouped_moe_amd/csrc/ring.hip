@@ -37,7 +37,7 @@ const char* last_error_text() { return g_last_error.c_str(); }
 void clear_error() { g_last_error.clear(); }
 
 moe_status ring_stage(moe_ring* r, int32_t layer, const int32_t* experts, int32_t n,
-                      hipStream_t cs, int32_t* lines_out) {
+                      hipStream_t cs, int32_t* lines_out, const std::vector<char>* later) {
   auto bit = r->banks.find(layer);
   if (bit == r->banks.end())
     return set_error(MOE_ERR_RING, "no bank bound for layer %d", layer);
@@ -79,12 +79,15 @@ moe_status ring_stage(moe_ring* r, int32_t layer, const int32_t* experts, int32_
   }
   for (int i = 0; i < n; ++i) {
     if (hit_line[i] >= 0) continue;
-    int victim = -1;
+    int victim = -1, victim_needed = -1;
     for (int l = 0; l < r->n_lines; ++l) {
       const moe_ring::Line& c = r->line[l];
       if (c.held) continue;
-      if (victim < 0 || c.last_use < r->line[victim].last_use) victim = l;
+      const bool needed = later && c.layer == layer && c.expert >= 0 && (*later)[c.expert];
+      int& v = needed ? victim_needed : victim;
+      if (v < 0 || c.last_use < r->line[v].last_use) v = l;
     }
+    if (victim < 0) victim = victim_needed;
     moe_ring::Line& ln = r->line[victim];
     if (ln.expert >= 0) r->where.erase(ring_key(ln.layer, ln.expert));
     ln.layer = -1;

@@ -79,6 +79,39 @@ def test_ring_reuses_lines_across_calls(moe):
     ring.close()
 
 
+def test_ring_passes_alternate_direction(moe):
+    """Chunk passes walk the offloaded experts up, then down, then up: the lines one pass leaves
+    behind are the first ones the next pass asks for, and misses evict lines the pass will
+    not need again first. The ring's hit and miss counts equal those of a host model of the
+    same plan (tests/ring_model.py), which also shows the gain over one fixed direction; the
+    output equals the all-resident layer bit for bit."""
+    from tests.ring_model import RingModel
+    wl = mi.custom_workload("sweep", T=600, d=64, E=24, k=4, inter=64, inter_shared=0, seed=12)
+    params, L_res = place(wl)
+    x = mi.make_x(wl, device="cuda")
+    ref = moe.moe_prefill_layer(L_res, x, 100)
+    ring = moe.Ring(L_res.shape, 8)
+    _, L = place(wl, offloaded=range(24), ring=ring, params=params)
+    got = moe.moe_prefill_layer(L, x, 100, copy_stream=torch.cuda.Stream())
+    torch.cuda.synchronize()
+    assert torch.equal(bits(got["out"]), bits(ref["out"]))
+    st = ring.stats()
+    model = RingModel(8)
+    cc = got["chunk_counts"].cpu().numpy()
+    for row in cc:
+        model.chunk(0, [int(e) for e in np.nonzero(row)[0]])
+    print(f"[ring] sweep: library hits {st['hits']} misses {st['misses']}; model "
+          f"{model.hits}/{model.misses}", flush=True)
+    assert (st["hits"], st["misses"]) == (model.hits, model.misses)
+    # one fixed direction with plain LRU (the model with every pass ascending)
+    lru = RingModel(8)
+    for row in cc:
+        lru.sweeps = 0
+        lru.chunk(0, [int(e) for e in np.nonzero(row)[0]])
+    assert model.misses < lru.misses
+    ring.close()
+
+
 def test_stage_api_direct(moe):
     """moe_stage_experts copies exactly the bank's line into the ring line it returns."""
     wl = mi.custom_workload("stage", T=8, d=64, E=8, k=2, inter=64, inter_shared=0, seed=3)

@@ -329,6 +329,8 @@ def main():
             "h2d_gb_per_step": round(per_step_bytes / 1e9, 3),
             "h2d_gbps": round(per_step_bytes / (r_wall / 1e3) / 1e9, 2),
             "h2d_link_gbps_measured": round(link, 2),
+            "ring_hit_rate": round(st["hits"] / max(1, st["hits"] + st["misses"]), 4),
+            "copy_waits_per_step": st["copy_waits"] // 3,
             "compute_hidden_under_copies_frac": round(max(0.0, min(1.0, hidden)), 3),
             "bit_identical_to_batched": bool(ok)}
         del br, Lr

@@ -142,7 +142,12 @@ moe_status moe_prefill_route(const moe_layer* layer, const void* x, int64_t T, i
  *                synchronisation).
  *   out          device [T, d] dtype; only rows t0..t0+n-1 are written
  *   ws, ws_bytes device workspace of at least moe_workspace_bytes(shape, n) bytes
- *   stream       compute stream; copy_stream: stream for ring copies (NULL = stream)
+ *   stream       compute stream; copy_stream: stream for ring copies (NULL = stream). The
+ *                copies of a wave alternate between copy_stream and one copy stream the ring
+ *                owns (default priority, created on first use, destroyed with the ring); each
+ *                line's `ready` event marks its own copy, and the compute stream waits on those.
+ * With a ring, the chunk's used offloaded experts are staged in waves that walk upward on
+ * even calls of the ring and downward on odd ones; no result bit depends on that order.
  * The batched pass is t0 = 0, n = T. n == 0 enqueues nothing. */
 moe_status moe_prefill_chunk(const moe_layer* layer, const void* x, const int32_t* ids,
                              const float* weights, int64_t T, int64_t t0, int64_t n,

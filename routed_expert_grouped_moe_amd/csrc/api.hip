@@ -237,7 +237,7 @@ moe_status ring_waves(const moe_layer* L, const void* x, int64_t t0, int64_t n,
       const int ws_ = wave_at(staged);
       for (int e : wexp[ws_]) later[e] = 0;
       st = ring_stage(R, L->layer_id, wexp[ws_].data(), static_cast<int32_t>(wexp[ws_].size()),
-                      cs, wlines[ws_].data(), &later);
+                      cs, wlines[ws_].data(), &later, /*two_streams=*/true);
       if (st == MOE_ERR_RING && staged > i) { st = MOE_OK; break; }   // retry after release
       if (st != MOE_OK) { release_held(i); return st; }
       ++staged;

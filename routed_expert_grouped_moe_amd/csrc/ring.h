@@ -33,10 +33,17 @@ struct moe_ring {
   uint64_t clock = 0;
   uint64_t sweeps = 0;            // chunk passes planned; odd passes walk experts downward
   uint64_t release_counter = 0;
-  // Release-epoch coalescing: the copy stream `coal_copy` has already waited for every
-  // release recorded on `coal_rel` up to epoch `waited_seq`, so older releases need no wait.
-  hipStream_t coal_rel = nullptr, coal_copy = nullptr;
-  uint64_t waited_seq = 0;
+  // Release-epoch coalescing, per copy stream: copy stream `copy` has already waited for
+  // every release recorded on `rel` up to epoch `seq`, so older releases need no wait.
+  struct Coal {
+    hipStream_t rel = nullptr, copy = nullptr;
+    uint64_t seq = 0;
+  };
+  Coal coal[2];
+  // Library-owned second copy stream (default priority, created on first use): the chunk
+  // sequencer alternates a wave's copies between it and the caller's copy stream, so one
+  // copy's per-transfer set-up overlaps the other's transfer.
+  hipStream_t copy2 = nullptr;
   moe_ring_stats_t stats{};
 };
 
@@ -48,13 +55,15 @@ inline int64_t ring_key(int32_t layer, int32_t expert) {
 
 // Implementations of the ABI calls, used by the chunk sequencer too (no argument checks
 // beyond the ring's own; set the thread's last error on failure).
+// two_streams: misses alternate between copy_stream and the ring's own second copy stream.
 // later (optional, indexed by expert of `layer`): experts that further stagings of the same
 // pass will ask for. A miss then evicts, least recently used first, a line that holds none of
 // them when there is one (a near-Belady choice for the known rest of the pass), else the least
 // recently used line.
 MOE_HIDDEN moe_status ring_stage(moe_ring* r, int32_t layer, const int32_t* experts, int32_t n,
                                  hipStream_t copy_stream, int32_t* lines_out,
-                                 const std::vector<char>* later = nullptr);
+                                 const std::vector<char>* later = nullptr,
+                                 bool two_streams = false);
 MOE_HIDDEN moe_status ring_wait_ready(moe_ring* r, const int32_t* lines, int32_t n,
                                       hipStream_t stream);
 MOE_HIDDEN moe_status ring_release(moe_ring* r, const int32_t* lines, int32_t n,

@@ -37,7 +37,8 @@ const char* last_error_text() { return g_last_error.c_str(); }
 void clear_error() { g_last_error.clear(); }
 
 moe_status ring_stage(moe_ring* r, int32_t layer, const int32_t* experts, int32_t n,
-                      hipStream_t cs, int32_t* lines_out, const std::vector<char>* later) {
+                      hipStream_t cs0, int32_t* lines_out, const std::vector<char>* later,
+                      bool two_streams) {
   auto bit = r->banks.find(layer);
   if (bit == r->banks.end())
     return set_error(MOE_ERR_RING, "no bank bound for layer %d", layer);
@@ -69,6 +70,15 @@ moe_status ring_stage(moe_ring* r, int32_t layer, const int32_t* experts, int32_
     return set_error(MOE_ERR_RING, "%d experts to copy but only %d lines free", misses,
                      free_lines);
 
+  if (two_streams && misses > 1 && !r->copy2) {
+    hipError_t err = hipStreamCreateWithFlags(&r->copy2, hipStreamNonBlocking);
+    if (err != hipSuccess) {
+      r->copy2 = nullptr;
+      return set_error(MOE_ERR_HIP, "hipStreamCreateWithFlags: %s", hipGetErrorString(err));
+    }
+  }
+  const bool split = two_streams && r->copy2 != nullptr;
+  int miss_no = 0;
   for (int i = 0; i < n; ++i) {            // hits first: they must not be chosen as victims
     if (hit_line[i] < 0) continue;
     moe_ring::Line& ln = r->line[hit_line[i]];
@@ -77,6 +87,14 @@ moe_status ring_stage(moe_ring* r, int32_t layer, const int32_t* experts, int32_
     r->stats.hits++;
     if (lines_out) lines_out[i] = hit_line[i];
   }
+  // Misses in three passes: choose every victim, then make each copy stream wait once per
+  // release stream for the newest release among its victims (releases recorded on one stream
+  // complete in order, so that wait covers the older ones), then issue the copies.
+  struct Planned {
+    int i, victim, sj;
+  };
+  std::vector<Planned> plan;
+  plan.reserve(misses);
   for (int i = 0; i < n; ++i) {
     if (hit_line[i] >= 0) continue;
     int victim = -1, victim_needed = -1;
@@ -92,40 +110,69 @@ moe_status ring_stage(moe_ring* r, int32_t layer, const int32_t* experts, int32_
     if (ln.expert >= 0) r->where.erase(ring_key(ln.layer, ln.expert));
     ln.layer = -1;
     ln.expert = -1;
-    if (ln.has_release) {
-      const bool covered = ln.release_stream == r->coal_rel && cs == r->coal_copy &&
-                           ln.release_seq <= r->waited_seq;
-      if (!covered) {
-        hipError_t err = hipStreamWaitEvent(cs, r->release[victim], 0);
-        if (err != hipSuccess)
-          return set_error(MOE_ERR_HIP, "hipStreamWaitEvent(release): %s", hipGetErrorString(err));
-        if (ln.release_stream != r->coal_rel || cs != r->coal_copy) {
-          r->coal_rel = ln.release_stream;
-          r->coal_copy = cs;
-          r->waited_seq = 0;
+    ln.held = true;
+    plan.push_back({i, victim, split ? (miss_no++ & 1) : 0});
+  }
+  // On a HIP error nothing this call took stays held: hit lines and filled victims keep their
+  // (valid) contents, victims not yet filled stay empty.
+  auto unwind = [&](size_t) {
+    for (int i = 0; i < n; ++i)
+      if (hit_line[i] >= 0) r->line[hit_line[i]].held = false;
+    for (const Planned& pl : plan) r->line[pl.victim].held = false;
+  };
+  for (int sj = 0; sj < 2; ++sj) {
+    hipStream_t cs = sj ? r->copy2 : cs0;
+    moe_ring::Coal& co = r->coal[sj];
+    std::vector<int> newest;                 // per release stream: victim of the newest release
+    for (const Planned& pl : plan) {
+      if (pl.sj != sj || !r->line[pl.victim].has_release) continue;
+      const moe_ring::Line& ln = r->line[pl.victim];
+      bool merged = false;
+      for (int& v : newest)
+        if (r->line[v].release_stream == ln.release_stream) {
+          if (ln.release_seq > r->line[v].release_seq) v = pl.victim;
+          merged = true;
         }
-        r->waited_seq = std::max(r->waited_seq, ln.release_seq);
-        r->stats.copy_waits++;
-      }
+      if (!merged) newest.push_back(pl.victim);
     }
-    const int e = experts[i];
+    for (int v : newest) {
+      const moe_ring::Line& ln = r->line[v];
+      if (ln.release_stream == co.rel && cs == co.copy && ln.release_seq <= co.seq) continue;
+      hipError_t err = hipStreamWaitEvent(cs, r->release[v], 0);
+      if (err != hipSuccess) {
+        unwind(0);
+        return set_error(MOE_ERR_HIP, "hipStreamWaitEvent(release): %s", hipGetErrorString(err));
+      }
+      if (ln.release_stream != co.rel || cs != co.copy) {
+        co.rel = ln.release_stream;
+        co.copy = cs;
+        co.seq = 0;
+      }
+      co.seq = std::max(co.seq, ln.release_seq);
+      r->stats.copy_waits++;
+    }
+  }
+  for (size_t q = 0; q < plan.size(); ++q) {
+    const Planned& pl = plan[q];
+    hipStream_t cs = pl.sj ? r->copy2 : cs0;
+    const int e = experts[pl.i];
     const char* src = bank.base + static_cast<size_t>(bank.slot[e]) * r->line_bytes;
-    char* dst = r->lines + static_cast<size_t>(victim) * r->line_bytes;
+    char* dst = r->lines + static_cast<size_t>(pl.victim) * r->line_bytes;
     hipError_t err = hipMemcpyAsync(dst, src, r->line_bytes, hipMemcpyHostToDevice, cs);
-    if (err != hipSuccess)
-      return set_error(MOE_ERR_HIP, "hipMemcpyAsync(line %d): %s", victim, hipGetErrorString(err));
-    err = hipEventRecord(r->ready[victim], cs);
-    if (err != hipSuccess)
-      return set_error(MOE_ERR_HIP, "hipEventRecord(ready): %s", hipGetErrorString(err));
+    if (err == hipSuccess) err = hipEventRecord(r->ready[pl.victim], cs);
+    if (err != hipSuccess) {
+      unwind(q);
+      return set_error(MOE_ERR_HIP, "copy into line %d: %s", pl.victim, hipGetErrorString(err));
+    }
+    moe_ring::Line& ln = r->line[pl.victim];
     ln.has_ready = true;
     ln.layer = layer;
     ln.expert = e;
-    ln.held = true;
     ln.last_use = ++r->clock;
-    r->where[ring_key(layer, e)] = victim;
+    r->where[ring_key(layer, e)] = pl.victim;
     r->stats.misses++;
     r->stats.bytes_h2d += static_cast<int64_t>(r->line_bytes);
-    if (lines_out) lines_out[i] = victim;
+    if (lines_out) lines_out[pl.i] = pl.victim;
   }
   return MOE_OK;
 }
@@ -303,6 +350,10 @@ void moe_ring_destroy(moe_ring* r) {
   }
   for (hipEvent_t e : r->ready) (void)hipEventDestroy(e);
   for (hipEvent_t e : r->release) (void)hipEventDestroy(e);
+  if (r->copy2) {
+    (void)hipStreamSynchronize(r->copy2);
+    (void)hipStreamDestroy(r->copy2);
+  }
   delete r;
 }
 

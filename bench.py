@@ -254,7 +254,8 @@ def main():
     moe.moe_profile_enable(True)
     ms_prof, _, _ = time_steps(step, args.steps, 0)
     moe.moe_profile_enable(False)
-    prof = moe.moe_profile_read(reset=True)
+    prof3 = moe.moe_profile_read(reset=True, clocks=True)
+    prof = {k: (v[0], v[1]) for k, v in prof3.items()}
 
     flop_tok = 2 * sh.d * sh.n_experts + 6 * sh.d * sh.inter * sh.top_k + 6 * sh.d * sh.inter_shared
     tok_s = T / (ms / 1e3)
@@ -275,6 +276,8 @@ def main():
         if b:
             ent["gbps"] = round(b_l / (per_launch_ms / 1e3) / 1e9, 1)
             ent["hbm_frac"] = round(ent["gbps"] * 1e9 / PEAK_HBM, 4)
+        if prof3[stage][2] > 0:
+            ent["clock_mhz"] = round(prof3[stage][2], 0)
         kernels[stage] = ent
     gemm = ["gu_routed", "down_routed", "gu_shared", "down_shared"]
     gemm_ms = sum(prof[s][0] for s in gemm) / args.steps
@@ -288,12 +291,20 @@ def main():
         ach = (b / n_l) / avg_s / 1e9
         roof = {"kernel": dom, "bound": "hbm", "achieved": round(ach, 1), "peak": 8000.0,
                 "unit": "GB/s", "frac": round(ach / 8000.0, 4), "traffic": measured_traffic(dom),
-                "bytes_per_launch": int(b / n_l), "avg_launch_us": round(avg_s * 1e6, 2)}
+                "bytes_per_launch": int(b / n_l), "avg_launch_us": round(avg_s * 1e6, 2),
+                "flops_per_launch": int(f / n_l),
+                "mfma_frac": round((f / n_l) / avg_s / PEAK_BF16, 4)}
     else:
         ach = (f / n_l) / avg_s / 1e12
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": 2500.0,
                 "unit": "TFLOP/s", "frac": round(ach / 2500.0, 4), "traffic": measured_traffic(dom),
                 "flops_per_launch": int(f / n_l), "avg_launch_us": round(avg_s * 1e6, 2)}
+    clk = prof3[dom][2]
+    if clk > 0:
+        # the shader clock the kernel ran at (sampled in the kernel): the MFMA peak scales with
+        # it (2.5 PFLOP/s is quoted at 2.4 GHz)
+        roof["clock_mhz_sustained"] = round(clk, 0)
+        roof["mfma_peak_at_sustained_clock_tflops"] = round(2500.0 * clk / 2400.0, 1)
 
     variants = {}
     if not args.no_variants:

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 1
+#define MOE_ABI_VERSION 2
 
 typedef enum {
   MOE_OK = 0,
@@ -218,8 +218,10 @@ void moe_ring_destroy(moe_ring* ring);
 
 /* Per-kernel timing with HIP events. While enabled, every launch the library enqueues is
  * bracketed by two timing events recorded on the launch's own stream; moe_profile_read waits
- * for the recorded events and adds their elapsed times to per-stage totals. Process-wide and
- * thread-safe; off by default (then no events are recorded). */
+ * for the recorded events and adds their elapsed times to per-stage totals. The GEMM kernels
+ * also sample the shader clock (thread 0 of every workgroup, start to last store) into a small
+ * device buffer the library allocates on first use per device. Process-wide and thread-safe;
+ * off by default (then nothing is recorded). Version 2 of moe_profile_t adds clock_mhz. */
 enum {
   MOE_STAGE_ROUTER = 0,     /* router GEMM */
   MOE_STAGE_TOPK = 1,       /* top-k + weights */
@@ -242,6 +244,9 @@ typedef struct {
   int32_t n_stages;         /* MOE_STAGE_COUNT */
   double ms[16];            /* summed kernel time per stage, milliseconds */
   int64_t launches[16];     /* launches per stage */
+  double clock_mhz[16];     /* GEMM stages: mean shader clock over their workgroups' lifetimes,
+                               sampled with s_memtime against s_memrealtime (100 MHz); 0 when
+                               not sampled */
 } moe_profile_t;
 
 moe_status moe_profile_enable(int32_t on);

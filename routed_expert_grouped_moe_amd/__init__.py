@@ -335,11 +335,14 @@ def moe_profile_enable(on: bool = True) -> None:
     check(lib().moe_profile_enable(1 if on else 0), "moe_profile_enable")
 
 
-def moe_profile_read(reset: bool = True) -> dict:
-    """{stage: (milliseconds, launches)} of the kernels timed since the last reset."""
+def moe_profile_read(reset: bool = True, clocks: bool = False) -> dict:
+    """{stage: (milliseconds, launches)} of the kernels timed since the last reset; with
+    clocks, {stage: (milliseconds, launches, mean shader clock MHz or 0)}."""
     from ._abi import STAGES, MoeProfile
     p = MoeProfile()
     check(lib().moe_profile_read(ctypes.byref(p), 1 if reset else 0), "moe_profile_read")
+    if clocks:
+        return {name: (p.ms[i], p.launches[i], p.clock_mhz[i]) for i, name in enumerate(STAGES)}
     return {name: (p.ms[i], p.launches[i]) for i, name in enumerate(STAGES)}
 
 

@@ -34,7 +34,7 @@ class MoeWsOffsets(ctypes.Structure):
 
 class MoeProfile(ctypes.Structure):
     _fields_ = [("version", c_i32), ("n_stages", c_i32), ("ms", ctypes.c_double * 16),
-                ("launches", c_i64 * 16)]
+                ("launches", c_i64 * 16), ("clock_mhz", ctypes.c_double * 16)]
 
 
 STAGES = ["router", "topk", "chunk_counts", "table", "hist", "scan", "permute", "gu_shared",
@@ -78,6 +78,9 @@ SIGNATURES = {
 _lib = None
 
 
+ABI_VERSION = 2     # MOE_ABI_VERSION of include/moe_prefill.h
+
+
 def lib():
     """The loaded libmoeprefill.so (raises if it has not been built)."""
     global _lib
@@ -91,6 +94,9 @@ def lib():
             f = getattr(L, name)
             f.restype = res
             f.argtypes = args
+        if L.moe_abi_version() != ABI_VERSION:
+            raise RuntimeError(f"{LIB_PATH} has ABI version {L.moe_abi_version()}, the binding "
+                               f"expects {ABI_VERSION}: rebuild the HIP library")
         _lib = L
     return _lib
 

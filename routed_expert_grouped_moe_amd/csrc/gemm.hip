@@ -230,6 +230,26 @@ struct GuParams {
   GemmGroups g;           // grouped: routed experts
   const int32_t* row_tok; // grouped: chunk-local token of each permuted row
   void* h;                // [rows, I] out
+  unsigned long long* clk;   // profiling clock counters of the stage, or NULL
+};
+
+// Clock sampling for the opt-in profiling: thread 0 of a workgroup notes the core clock and
+// the 100 MHz real-time counter at its start and adds the differences at its end.
+struct ClockSample {
+  unsigned long long* clk;
+  unsigned long long c0 = 0, r0 = 0;
+  __device__ explicit ClockSample(unsigned long long* p) : clk(threadIdx.x == 0 ? p : nullptr) {
+    if (clk) {
+      c0 = __builtin_amdgcn_s_memtime();
+      r0 = __builtin_amdgcn_s_memrealtime();
+    }
+  }
+  __device__ void finish() {
+    if (!clk) return;
+    const unsigned long long c1 = __builtin_amdgcn_s_memtime(), r1 = __builtin_amdgcn_s_memrealtime();
+    atomicAdd(clk, c1 - c0);
+    atomicAdd(clk + 1, r1 - r0);
+  }
 };
 
 // Start of expert e's line: from the uniform layout when there is one, else from the table.
@@ -248,6 +268,7 @@ void gu_kernel(GuParams p) {
                                : static_cast<int>((p.n + TL::BM - 1) / TL::BM);
   int t;
   if (!xcd_tile(m_tiles * NT, &t)) return;
+  ClockSample clock(p.clk);
   const int mi = t / NT;
   const int n0h = (t % NT) * HC;
   int64_t row0;
@@ -300,6 +321,7 @@ void gu_kernel(GuParams p) {
   const int col0 = n0h + wn * (TL::TN / 2);
   store_slab<TL, T, TL::TN / 2>(lds, val, row_of, static_cast<T*>(p.h), p.I, col0,
                                 min(TL::TN / 2, p.I - col0));
+  clock.finish();
 }
 
 struct DownParams {
@@ -311,6 +333,7 @@ struct DownParams {
   int64_t line_down_off;  // grouped: element offset of W_down inside a line (2*I*d)
   const int32_t* row_slot;// grouped: output row (t*k + j) of each permuted row
   float* out;             // grouped: Y [n*k, d]; dense: S [n, d]
+  unsigned long long* clk;   // profiling clock counters of the stage, or NULL
 };
 
 template <typename T, class TL, bool kGrouped>
@@ -324,6 +347,7 @@ void down_kernel(DownParams p) {
                                : static_cast<int>((p.n + TL::BM - 1) / TL::BM);
   int t;
   if (!xcd_tile(m_tiles * NT, &t)) return;
+  ClockSample clock(p.clk);
   const int mi = t / NT;
   const int n0 = (t % NT) * TL::BN;
   int64_t row0;
@@ -374,6 +398,7 @@ void down_kernel(DownParams p) {
   };
   const int col0 = n0 + wn * TL::TN;
   store_slab<TL, float, TL::TN>(lds, val, row_of, p.out, p.d, col0, min(TL::TN, p.d - col0));
+  clock.finish();
 }
 
 struct RouterParams {
@@ -383,6 +408,7 @@ struct RouterParams {
   float* logits;
   int64_t T;
   int d, E;
+  unsigned long long* clk;   // profiling clock counters of the stage, or NULL
 };
 
 template <typename T, class TL>
@@ -392,6 +418,7 @@ void router_kernel(RouterParams p) {
   const int NT = (p.E + TL::BN - 1) / TL::BN;
   int t;
   if (!xcd_tile(static_cast<int>((p.T + TL::BM - 1) / TL::BM) * NT, &t)) return;
+  ClockSample clock(p.clk);
   const int n0 = (t % NT) * TL::BN;
   const int64_t row0 = static_cast<int64_t>(t / NT) * TL::BM;
   const int rows = static_cast<int>(min<int64_t>(TL::BM, p.T - row0));
@@ -422,6 +449,7 @@ void router_kernel(RouterParams p) {
   const int slab0 = wm * TL::TM;
   auto row_of = [&](int sr) -> int64_t { return slab0 + sr < rows ? row0 + slab0 + sr : -1; };
   store_slab<TL, float, TL::TN>(lds, val, row_of, p.logits, p.E, col0, min(TL::TN, p.E - col0));
+  clock.finish();
 }
 
 // Big tiles when they still give the chip about two workgroups per CU (384 of them: 1.5 per
@@ -440,7 +468,7 @@ hipError_t launch_router_gemm(int dtype, const void* x, const void* w_router, co
                               int64_t T, int d, int E, float* logits, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   ProfScope prof(MOE_STAGE_ROUTER, s);
-  RouterParams p{x, w_router, bias, logits, T, d, E};
+  RouterParams p{x, w_router, bias, logits, T, d, E, prof_clock(MOE_STAGE_ROUTER)};
   if (use_big_dense(T, (E + BigTile::BN - 1) / BigTile::BN)) {
     const unsigned grid = xcd_grid((T + BigTile::BM - 1) / BigTile::BM * ((E + BigTile::BN - 1) / BigTile::BN));
     if (dtype == MOE_BF16) router_kernel<uint16_t, BigTile><<<grid, BigTile::NT, 0, s>>>(p);
@@ -466,7 +494,7 @@ hipError_t launch_gu_routed(int dtype, const void* x, int64_t t0, int d, int I,
   ProfScope prof(MOE_STAGE_GU_ROUTED, s);
   GuParams p{};
   p.x = x; p.t0 = t0; p.n = 0; p.d = d; p.I = I; p.w = nullptr; p.g = g;
-  p.row_tok = row_tok; p.h = h;
+  p.row_tok = row_tok; p.h = h; p.clk = prof_clock(MOE_STAGE_GU_ROUTED);
   if (g.tile_rows == BigTile::BM) gu_routed<BigTile>(dtype, p, g, I, s);
   else gu_routed<SmallTile>(dtype, p, g, I, s);
   return hipGetLastError();
@@ -478,6 +506,7 @@ hipError_t launch_gu_dense(int dtype, const void* x, int64_t t0, int64_t n, int 
   ProfScope prof(MOE_STAGE_GU_SHARED, s);
   GuParams p{};
   p.x = x; p.t0 = t0; p.n = n; p.d = d; p.I = Is; p.w = w_gu; p.row_tok = nullptr; p.h = h;
+  p.clk = prof_clock(MOE_STAGE_GU_SHARED);
   const int64_t nt_big = (Is + BigTile::BN / 2 - 1) / (BigTile::BN / 2);
   if (use_big_dense(n, nt_big)) {
     const unsigned grid = xcd_grid((n + BigTile::BM - 1) / BigTile::BM * nt_big);
@@ -507,6 +536,7 @@ hipError_t launch_down_routed(int dtype, const void* h, int d, int I, const Gemm
   DownParams p{};
   p.h = h; p.n = 0; p.d = d; p.K = I; p.w = nullptr; p.g = g;
   p.line_down_off = 2LL * I * d; p.row_slot = row_slot; p.out = y;
+  p.clk = prof_clock(MOE_STAGE_DOWN_ROUTED);
   if (g.tile_rows == BigTile::BM) down_routed<BigTile>(dtype, p, g, d, s);
   else down_routed<SmallTile>(dtype, p, g, d, s);
   return hipGetLastError();
@@ -518,7 +548,7 @@ hipError_t launch_down_dense(int dtype, const void* h, int64_t n, int d, int Is,
   ProfScope prof(MOE_STAGE_DOWN_SHARED, s);
   DownParams p{};
   p.h = h; p.n = n; p.d = d; p.K = Is; p.w = w_down; p.line_down_off = 0;
-  p.row_slot = nullptr; p.out = out;
+  p.row_slot = nullptr; p.out = out; p.clk = prof_clock(MOE_STAGE_DOWN_SHARED);
   const int64_t nt_big = (d + BigTile::BN - 1) / BigTile::BN;
   if (use_big_dense(n, nt_big)) {
     const unsigned grid = xcd_grid((n + BigTile::BM - 1) / BigTile::BM * nt_big);

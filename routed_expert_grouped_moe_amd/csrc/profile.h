@@ -18,4 +18,9 @@ class MOE_HIDDEN ProfScope {
   hipEvent_t a_ = nullptr;
 };
 
+// Device counters of the stage's sampled clocks while profiling is on (else NULL): [0] sums
+// core-clock ticks (s_memtime) and [1] real-time ticks (s_memrealtime, 100 MHz) that thread 0
+// of each workgroup of the stage's GEMM kernels spent between its start and its last store.
+MOE_HIDDEN unsigned long long* prof_clock(int stage);
+
 }  // namespace moe

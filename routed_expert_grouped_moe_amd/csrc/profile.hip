@@ -1,5 +1,6 @@
 // Opt-in per-stage kernel timing with HIP events recorded on each launch's own stream.
 #include <mutex>
+#include <unordered_map>
 #include <vector>
 
 #include "profile.h"
@@ -19,6 +20,8 @@ std::vector<Pending> g_pending;
 std::vector<hipEvent_t> g_pool;
 double g_ms[16];
 int64_t g_n[16];
+double g_clk[16], g_rt[16];                        // summed clock samples read back so far
+std::unordered_map<int, unsigned long long*> g_clk_dev;   // per device: [16][2] counters
 
 hipEvent_t take_event() {   // caller holds g_mu
   if (!g_pool.empty()) {
@@ -32,6 +35,26 @@ hipEvent_t take_event() {   // caller holds g_mu
 }
 
 }  // namespace
+
+unsigned long long* prof_clock(int stage) {
+  std::lock_guard<std::mutex> lk(g_mu);
+  if (!g_on || stage < 0 || stage >= 16) return nullptr;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  unsigned long long*& buf = g_clk_dev[dev];
+  if (!buf) {
+    if (hipMalloc(&buf, 16 * 2 * sizeof(unsigned long long)) != hipSuccess) {
+      buf = nullptr;
+      return nullptr;
+    }
+    if (hipMemset(buf, 0, 16 * 2 * sizeof(unsigned long long)) != hipSuccess) {
+      (void)hipFree(buf);
+      buf = nullptr;
+      return nullptr;
+    }
+  }
+  return buf + 2 * stage;
+}
 
 ProfScope::ProfScope(int stage, hipStream_t s) : stage_(stage), s_(s) {
   std::lock_guard<std::mutex> lk(g_mu);
@@ -82,14 +105,35 @@ moe_status moe_profile_read(moe_profile_t* out, int32_t reset) {
     moe::g_pool.push_back(p.b);
   }
   moe::g_pending.clear();
-  out->version = 1;
+  for (auto& kv : moe::g_clk_dev) {              // every launch read above has completed
+    if (!kv.second) continue;
+    unsigned long long h[32];
+    int cur = 0;
+    hipError_t err = hipGetDevice(&cur);
+    if (err == hipSuccess) err = hipSetDevice(kv.first);
+    if (err == hipSuccess) err = hipMemcpy(h, kv.second, sizeof(h), hipMemcpyDeviceToHost);
+    if (err == hipSuccess) err = hipMemset(kv.second, 0, sizeof(h));
+    (void)hipSetDevice(cur);
+    if (err != hipSuccess) {
+      if (st == MOE_OK) st = moe::set_error(MOE_ERR_HIP, "profile clocks: %s", hipGetErrorString(err));
+      continue;
+    }
+    for (int i = 0; i < 16; ++i) {
+      moe::g_clk[i] += static_cast<double>(h[2 * i]);
+      moe::g_rt[i] += static_cast<double>(h[2 * i + 1]);
+    }
+  }
+  out->version = 2;
   out->n_stages = MOE_STAGE_COUNT;
   for (int i = 0; i < 16; ++i) {
     out->ms[i] = moe::g_ms[i];
     out->launches[i] = moe::g_n[i];
+    out->clock_mhz[i] = moe::g_rt[i] > 0 ? moe::g_clk[i] / moe::g_rt[i] * 100.0 : 0.0;
     if (reset) {
       moe::g_ms[i] = 0.0;
       moe::g_n[i] = 0;
+      moe::g_clk[i] = 0.0;
+      moe::g_rt[i] = 0.0;
     }
   }
   return st;

@@ -85,6 +85,28 @@ def test_edge_shapes(moe, case):
     _full_parity(moe, wl, BF16_TOL, chunks=chunks)
 
 
+def test_big_tiles_with_partial_tiles(moe):
+    """A chunk averaging at least 128 rows per expert takes 256-row M-tiles; an expert's
+    remainder gets one more, partly filled tile. The seeded routing hits the cases (experts
+    with fewer than 64 rows, small remainders after full tiles, several full tiles plus a
+    large partial one). Oracle parity, and the bytes equal those of the all-64-row tiling that a
+    100-token chunk takes. (At this size the max-abs/RMS metric is crest-sensitive: rounding
+    the exact output once to bf16 already scores 1.15e-2 here, and 2.1e-2 -- above the bar --
+    for the same routing at d = 128, so the layer is taken at d = 256.)"""
+    wl = mi.custom_workload("tails", T=2000, d=256, E=16, k=4, inter=128, inter_shared=256,
+                            zipf_s=1.1, seed=15)
+    params, L = place(wl)
+    x = mi.make_x(wl, device="cuda")
+    r = moe.moe_prefill_route(L, x, wl.T)
+    torch.cuda.synchronize()
+    c = r["chunk_counts"][0].cpu().numpy()
+    assert wl.T * wl.shape.top_k >= wl.shape.n_experts * 128      # 256-row tiling
+    rem = c % 256
+    assert ((c > 0) & (c <= 64)).any()
+    assert ((c > 256) & (rem > 0) & (rem <= 64)).any() and ((c > 512) & (rem > 64)).any()
+    _full_parity(moe, wl, BF16_TOL, chunks=(100, wl.T))
+
+
 def test_topk_ties_and_special_values(moe):
     """Top-k on logits with exact ties (duplicated router rows), NaN and -inf (from the bias),
     an all-NaN token and a zero token, with E = 130 (ragged lane slices). The ids equal the
@@ -227,3 +249,26 @@ def test_add_rmsnorm(moe):
     moe.moe_add_rmsnorm(x2, dlt, 1e-6, x_out=x2)
     torch.cuda.synchronize()
     assert torch.equal(x2.view(torch.int16), want.view(torch.int16))
+
+
+def test_profile_times_and_clocks(moe):
+    """The opt-in profiling counts every GEMM launch and samples a plausible shader clock for
+    each GEMM stage; turning it off records nothing more."""
+    wl = mi.custom_workload("prof", T=700, d=256, E=64, k=6, inter=128, inter_shared=256,
+                            seed=9)
+    params, L = place(wl)
+    x = mi.make_x(wl, device="cuda")
+    moe.moe_profile_read(reset=True)
+    moe.moe_profile_enable(True)
+    try:
+        _run(moe, L, x, 256)
+    finally:
+        moe.moe_profile_enable(False)
+    prof = moe.moe_profile_read(reset=True, clocks=True)
+    for stage in ("router", "gu_routed", "down_routed", "gu_shared", "down_shared"):
+        ms, n, mhz = prof[stage]
+        assert n >= 1 and ms > 0, (stage, prof[stage])
+        assert 100 < mhz < 3500, (stage, mhz)
+    assert prof["combine"][1] == 3 and prof["combine"][2] == 0      # 3 chunks; not sampled
+    _run(moe, L, x, 256)
+    assert all(v[1] == 0 for v in moe.moe_profile_read(reset=True).values())

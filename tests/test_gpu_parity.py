@@ -222,6 +222,24 @@ def test_layer_3001(moe):
     _full_parity(moe, mi.WORKLOADS["layer_3001"], BF16_TOL)
 
 
+def test_row_path_equals_batched(moe):
+    """The single-row path (a chunk of one token, as a decoder would run it, on the same
+    kernels) gives each token the bytes of the batched pass, at the full layer size."""
+    wl = mi.WORKLOADS["layer_3001"]
+    params, L = place(wl)
+    x = mi.make_x(wl, device="cuda")
+    base = _run(moe, L, x, wl.T)
+    sh = L.shape
+    ws = torch.empty(moe.moe_workspace_bytes(sh, 1), dtype=torch.uint8, device="cuda")
+    out = torch.zeros_like(x)
+    rows = [0, 1, 1500, 2999, wl.T - 1]
+    for t in rows:
+        moe.moe_prefill_chunk(L, x, base["ids"], base["weights"], t, 1, out, ws)
+    torch.cuda.synchronize()
+    for t in rows:
+        assert torch.equal(bits(out[t]), bits(base["out"][t])), t
+
+
 def test_chunk_gate_4099(moe):
     """Zipf(1.1)-skewed routing, T = 4,099: chunks 256 / 1,024 / 2,048 and the batched pass
     give identical bytes."""

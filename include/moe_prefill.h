@@ -165,7 +165,9 @@ moe_status moe_prefill_layer(const moe_layer* layer, const void* x, int64_t T, i
 
 /* Ring of n_lines device expert lines, each line_bytes = 3*I*d*sizeof(dtype), in the
  * caller-owned buffer device_lines [n_lines * line_bytes] (256-byte aligned). Creates 2
- * events per line. On failure every partially created event is destroyed and *out = NULL. */
+ * events per line. On failure every partially created event is destroyed and *out = NULL.
+ * A ring belongs to the device that was current at creation; its calls (and chunk calls of
+ * layers bound to it) must come from one host thread at a time with that device current. */
 moe_status moe_ring_create(const moe_shape* shape, void* device_lines, int32_t n_lines,
                            moe_ring** out);
 
@@ -203,7 +205,8 @@ typedef struct {
   int64_t hits;               /* staged experts already present in a line */
   int64_t misses;             /* staged experts copied from a bank */
   int64_t bytes_h2d;          /* bytes copied host -> device */
-  int64_t copy_waits;         /* copy-stream waits on a line's release event */
+  int64_t copy_waits;         /* copy-stream waits on release events (a staging call waits
+                                 once per copy stream for the newest release it needs) */
   int64_t waves;              /* staging waves run by moe_prefill_chunk */
 } moe_ring_stats_t;
 
@@ -213,7 +216,8 @@ moe_status moe_ring_reset_stats(moe_ring* ring);
 /* Forget every cached line (next staging copies again). Does not wait for the GPU. */
 moe_status moe_ring_invalidate(moe_ring* ring);
 
-/* Wait for the ring's outstanding events, destroy them and free the ring. NULL-safe. */
+/* Wait for the ring's outstanding events and its own copy stream, destroy them and free the
+ * ring. NULL-safe. */
 void moe_ring_destroy(moe_ring* ring);
 
 /* Per-kernel timing with HIP events. While enabled, every launch the library enqueues is

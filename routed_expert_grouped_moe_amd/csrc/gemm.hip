@@ -182,7 +182,7 @@ inline unsigned xcd_grid(int64_t n_tiles) {
 // values (transformed by `val`) into a per-wave staging area, then store whole rows with
 // 16-byte vectors. row_of(r) maps a slab row to its global output row (or -1 to skip),
 // OUT is the stored element type, cols = columns of the slab that exist (<= NCOL).
-template <class TL, typename OUT, int NCOL, class Val, class RowOf>
+template <class TL, typename OUT, int NCOL, bool kStreamOut = false, class Val, class RowOf>
 __device__ __forceinline__ void store_slab(char* lds, Val val, RowOf row_of, OUT* out,
                                            int64_t ld, int col0, int cols) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -212,7 +212,11 @@ __device__ __forceinline__ void store_slab(char* lds, Val val, RowOf row_of, OUT
       const char* s = reinterpret_cast<const char*>(stg) + row * RB + ch * 16;
       OUT* d = out + grow * ld + col0 + col;
       if (vec && col + EPC <= cols) {
-        *reinterpret_cast<u32x4_t*>(d) = *reinterpret_cast<const u32x4_t*>(s);
+        if (kStreamOut)   // written once, read once by another kernel: keep it out of the caches
+          __builtin_nontemporal_store(*reinterpret_cast<const u32x4_t*>(s),
+                                      reinterpret_cast<u32x4_t*>(d));
+        else
+          *reinterpret_cast<u32x4_t*>(d) = *reinterpret_cast<const u32x4_t*>(s);
       } else {
         for (int e = 0; e < EPC && col + e < cols; ++e) d[e] = reinterpret_cast<const OUT*>(s)[e];
       }
@@ -397,7 +401,7 @@ void down_kernel(DownParams p) {
     return kGrouped ? static_cast<int64_t>(p.row_slot[row0 + slab0 + sr]) : row0 + slab0 + sr;
   };
   const int col0 = n0 + wn * TL::TN;
-  store_slab<TL, float, TL::TN>(lds, val, row_of, p.out, p.d, col0, min(TL::TN, p.d - col0));
+  store_slab<TL, float, TL::TN, true>(lds, val, row_of, p.out, p.d, col0, min(TL::TN, p.d - col0));
   clock.finish();
 }
 

@@ -207,7 +207,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-sample-tokens", type=int, default=384)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=2048,
+                    help="tokens of the headline workload the fp64 oracle runs (about 10 s)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-stack", action="store_true",

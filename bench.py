@@ -16,7 +16,8 @@ around each of its launches on the launch's own stream, over a second pass of th
 steps (the headline time comes from a pass without those events). Also reported: the same
 layer at deep chunks 2,048 / 4,096 / 8,192, the layer with all experts streamed from a pinned
 host bank through a 64-line ring at chunk 2,048 (with the measured host-link rate and the
-share of compute hidden under the copies), an 8-layer stack (T = 32,700, Zipf routing, half
+share of compute hidden under the copies), a decode-sized call (8 tokens) eager and as a
+replayed HIP graph, an 8-layer stack (T = 32,700, Zipf routing, half
 the experts through one 128-line ring), and the fp64 CPU oracle on a bounded sample.
 """
 from __future__ import annotations
@@ -106,6 +107,35 @@ def h2d_probe(nbytes: int, runs: int) -> float:
         s.synchronize()
         best = min(best, time.perf_counter() - t0)
     return nbytes / best / 1e9
+
+
+def small_call_variant(L, mi, wl, T: int = 8, steps: int = 50):
+    """A decode-sized call (T tokens of the headline layer, one chunk) eager and as a
+    replayed HIP graph of the same call: at this size launch overhead, not the GPU, bounds
+    the eager call."""
+    import torch
+
+    import routed_expert_grouped_moe_amd as moe
+    x = mi.make_x(wl, device="cuda")[:T].contiguous()
+    bufs = moe.layer_buffers(L, T, T)
+    call = lambda: moe.moe_prefill_layer(L, x, T, bufs=bufs)
+    e_ms, e_wall, _ = time_steps(call, steps, 5)
+    ref = bufs["out"].clone()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        call()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    g_ms, g_wall, _ = time_steps(g.replay, steps, 5)
+    ok = torch.equal(bufs["out"].view(torch.int16), ref.view(torch.int16))
+    return {"tokens": T, "eager_ms_per_call": round(e_wall, 4),
+            "graph_ms_per_call": round(g_wall, 4),
+            "eager_gpu_ms": round(e_ms, 4), "graph_gpu_ms": round(g_ms, 4),
+            "graph_equals_eager": bool(ok)}
 
 
 def stack_variant(steps: int):
@@ -318,6 +348,7 @@ def main():
                                               "ms_per_step": round(v_ms, 3), "step_ms": spread(v_per),
                                               "bit_identical_to_batched": bool(ok)}
             del b2
+        variants["small_call_T8"] = small_call_variant(L, mi, wl)
         log("[bench] ring variant: all 512 experts in a pinned bank, 64 lines, chunk 2048")
         ring = moe.Ring(sh, 64)
         _, Lr = place(wl, offloaded=range(sh.n_experts), ring=ring, params=params)

@@ -290,3 +290,36 @@ def test_profile_times_and_clocks(moe):
     assert prof["combine"][1] == 3 and prof["combine"][2] == 0      # 3 chunks; not sampled
     _run(moe, L, x, 256)
     assert all(v[1] == 0 for v in moe.moe_profile_read(reset=True).values())
+
+
+def test_graph_capture_resident_layer(moe):
+    """With every expert resident a layer call enqueues kernels only (no allocation, host
+    synchronisation or memset), so the whole call (route + 5 chunks) can be captured in a HIP
+    graph. Replays, with eager work and synchronisation between them, give the eager bytes
+    every time."""
+    wl = mi.custom_workload("graph", T=600, d=256, E=32, k=4, inter=128, inter_shared=256,
+                            zipf_s=1.1, seed=17)
+    params, L = place(wl)
+    x = mi.make_x(wl, device="cuda")
+    chunk = 128
+    eager = _run(moe, L, x, chunk)
+    bufs = moe.layer_buffers(L, wl.T, chunk)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):                      # warm-up outside the capture
+        moe.moe_prefill_layer(L, x, chunk, bufs=bufs)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.moe_prefill_layer(L, x, chunk, bufs=bufs)
+    for _ in range(3):
+        for key in ("out", "logits"):
+            bufs[key].zero_()
+        bufs["ids"].fill_(-1)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(bits(bufs["out"]), bits(eager["out"]))
+        assert torch.equal(bufs["ids"], eager["ids"])
+        assert torch.equal(bufs["chunk_counts"], eager["chunk_counts"])

@@ -39,10 +39,11 @@ struct Tile {
   static constexpr int STAGE = ROWS * kRowBytes;
   static constexpr int LDS = 2 * STAGE;
   static constexpr int LPW = ROWS / 8 / NW;                 // load instructions per wave per stage
-  static_assert(TM == 64, "waves own 64-row slabs");
+  static_assert(TM % 16 == 0 && TN % 16 == 0, "whole 16 x 16 MFMA blocks per wave");
   static_assert(ROWS % (8 * NW) == 0, "whole load instructions per wave");
 };
 using BigTile = Tile<256, 256, 4, 2>;      // 8 waves, 64 x 128 each; 128 KB LDS, 1 workgroup/CU
+using TallTile = Tile<320, 256, 4, 2>;     // 8 waves, 80 x 128 each; 144 KB LDS, 1 workgroup/CU
 using SmallTile = Tile<64, 256, 1, 4>;     // 4 waves, 64 x 64 each; 80 KB LDS, 2 workgroups/CU
 
 // s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding of the immediate).
@@ -479,7 +480,11 @@ inline bool use_big_dense(int64_t n, int64_t n_tiles_big) {
 }  // namespace
 
 int routed_tile_rows(int64_t n, int k, int E) {
-  return (n * k >= static_cast<int64_t>(E) * 128) ? BigTile::BM : SmallTile::BM;
+  // a = mean rows per expert. With a in [192, 320) many experts hold just over 256 rows; a
+  // 320-row tile keeps them in one tile instead of a full tile plus a nearly empty one.
+  const int64_t rows = n * k, e = static_cast<int64_t>(E);
+  if (rows >= e * 192 && rows < e * 320) return TallTile::BM;
+  return rows >= e * 128 ? BigTile::BM : SmallTile::BM;
 }
 
 hipError_t launch_router_gemm(int dtype, const void* x, const void* w_router, const float* bias,
@@ -513,7 +518,8 @@ hipError_t launch_gu_routed(int dtype, const void* x, int64_t t0, int d, int I,
   GuParams p{};
   p.x = x; p.t0 = t0; p.n = 0; p.d = d; p.I = I; p.w = nullptr; p.g = g;
   p.row_tok = row_tok; p.h = h; p.clk = prof_clock(MOE_STAGE_GU_ROUTED);
-  if (g.tile_rows == BigTile::BM) gu_routed<BigTile>(dtype, p, g, I, s);
+  if (g.tile_rows == TallTile::BM) gu_routed<TallTile>(dtype, p, g, I, s);
+  else if (g.tile_rows == BigTile::BM) gu_routed<BigTile>(dtype, p, g, I, s);
   else gu_routed<SmallTile>(dtype, p, g, I, s);
   return hipGetLastError();
 }
@@ -555,7 +561,8 @@ hipError_t launch_down_routed(int dtype, const void* h, int d, int I, const Gemm
   p.h = h; p.n = 0; p.d = d; p.K = I; p.w = nullptr; p.g = g;
   p.line_down_off = 2LL * I * d; p.row_slot = row_slot; p.out = y;
   p.clk = prof_clock(MOE_STAGE_DOWN_ROUTED);
-  if (g.tile_rows == BigTile::BM) down_routed<BigTile>(dtype, p, g, d, s);
+  if (g.tile_rows == TallTile::BM) down_routed<TallTile>(dtype, p, g, d, s);
+  else if (g.tile_rows == BigTile::BM) down_routed<BigTile>(dtype, p, g, d, s);
   else down_routed<SmallTile>(dtype, p, g, d, s);
   return hipGetLastError();
 }

@@ -8,18 +8,21 @@
 // 16 x lane, so one instruction fills 8 rows of 128 bytes; the A rows of a routed tile are
 // gathered from the prompt by pointer, no permuted copy of x exists). Inside LDS, 16-byte
 // segment g of row r sits at segment g ^ (r & 7), so the 16 lanes that read one MFMA operand
-// (16 rows, same K segment) hit 16 different bank groups. Waves own 64-row slabs of the tile
-// and accumulate 16 x 16 MFMA blocks: v_mfma_f32_16x16x32_bf16 (bf16) or
-// v_mfma_f32_16x16x4_f32 (fp32), fp32 accumulation.
+// (16 rows, same K segment) hit 16 different bank groups. A wave row-group owns every WM-th
+// 16-row block of the tile and accumulates 16 x 16 MFMA blocks: v_mfma_f32_16x16x32_bf16
+// (bf16) or v_mfma_f32_16x16x4_f32 (fp32), fp32 accumulation.
 //
-// Two tile shapes: big (256 x 256, 8 waves of 64 x 128) for large row counts and small
-// (64 x 256, 4 waves of 64 x 64) for few rows per expert. Which one runs never changes a bit:
-// every output element is one token row against one weight row, accumulated over K in the same
-// stage order with the same instruction and the same lane-to-K mapping in both. Together with
+// Three tile shapes: tall (320 x 256, 8 waves of 80 x 128) and big (256 x 256, 8 waves of
+// 64 x 128) for large row counts, small (64 x 256, 4 waves of 64 x 64) for few rows per
+// expert. Which one runs never changes a bit: every output element is one token row against
+// one weight row, accumulated over K in the same stage order with the same instruction and the
+// same lane-to-K mapping in all of them. Together with
 // no split-K, no atomics and no shape-dependent arithmetic, that is what makes a token's bytes
 // independent of the chunk size, of its position and of its expert's row count -- the
 // property the exact deep prefill page ("Flash Next EXL3: exact deep prefill", opening section)
 // asks of its GU/down kernels.
+#include <type_traits>
+
 #include "device_common.h"
 #include "moe_internal.h"
 #include "profile.h"
@@ -45,6 +48,20 @@ struct Tile {
 using BigTile = Tile<256, 256, 4, 2>;      // 8 waves, 64 x 128 each; 128 KB LDS, 1 workgroup/CU
 using TallTile = Tile<320, 256, 4, 2>;     // 8 waves, 80 x 128 each; 144 KB LDS, 1 workgroup/CU
 using SmallTile = Tile<64, 256, 1, 4>;     // 4 waves, 64 x 64 each; 80 KB LDS, 2 workgroups/CU
+
+// Wave rows: wave row-group wm owns the tile's 16-row blocks wm, wm + WM, wm + 2 WM, ...
+// (block i of the wave starts at tile row (i * WM + wm) * 16). Interleaving keeps the work of
+// a partly filled tile spread over all SIMDs; blocks past the tile's valid rows are skipped.
+template <class TL>
+__device__ __forceinline__ int block_row(int i, int wm) {
+  return (i * TL::WM + wm) * 16;
+}
+// Number of this wave's blocks that hold valid rows (they are a prefix of its blocks).
+template <class TL>
+__device__ __forceinline__ int busy_blocks(int rows, int wm) {
+  const int r16 = (rows + 15) / 16;
+  return r16 > wm ? min(TL::FM, (r16 - wm + TL::WM - 1) / TL::WM) : 0;
+}
 
 // s_waitcnt vmcnt(N) leaving the other counters alone (gfx9 encoding of the immediate).
 template <int N>
@@ -96,18 +113,19 @@ __device__ __forceinline__ int stage_seg() {
 // instruction q; stage s reads 128 bytes further per stage. kPairedGU: the B half holds BN/2
 // gate rows then the BN/2 matching up rows; wave column wn takes gate blocks wn*TN/2.. and the
 // up blocks of the same columns, so acc[i][j] and acc[i][j + FN/2] are gate and up of one
-// output element. rows: valid rows of the tile; a wave whose 64-row slab holds none keeps
-// loading its share of the stages but skips its MFMAs (its outputs are never stored).
+// output element. rows: valid rows of the tile; a wave keeps loading its share of the stages
+// but skips the fragment reads and MFMAs of its blocks past `rows` (their outputs are never
+// stored).
 template <typename T, class TL, bool kPairedGU>
 __device__ __forceinline__ void mainloop(const char* const (&src)[TL::LPW], int nk, char* lds,
                                          f32x4_t (&acc)[TL::FM][TL::FN], int rows) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / TL::WN, wn = wave % TL::WN, kq = lane >> 4, l16 = lane & 15;
-  const bool busy = wm * TL::TM < rows;
+  const int nbusy = busy_blocks<TL>(rows, wm);
   const int sw = l16 & 7;
   int arow[TL::FM], brow[TL::FN];
 #pragma unroll
-  for (int i = 0; i < TL::FM; ++i) arow[i] = (wm * TL::TM + i * 16 + l16) * kRowBytes;
+  for (int i = 0; i < TL::FM; ++i) arow[i] = (block_row<TL>(i, wm) + l16) * kRowBytes;
 #pragma unroll
   for (int j = 0; j < TL::FN; ++j) {
     int b;
@@ -147,31 +165,55 @@ __device__ __forceinline__ void mainloop(const char* const (&src)[TL::LPW], int 
 #pragma clang diagnostic pop
     }
   };
-  issue(0);
-  for (int s = 0; s < nk; ++s) {
-    wait_vmcnt<0>();            // this wave's share of stage s has landed ...
-    __syncthreads();            // ... and everyone's; everyone also left stage s - 1
-    if (s + 1 < nk) issue(s + 1);
-    const char* buf = lds + (s & 1) * TL::STAGE;
-    if (!busy) continue;
+  // Two copies of the stage loop: every block valid (straight-line fragment reads, then the
+  // MFMAs), or a partly valid wave that skips the blocks past `rows` (uniform branches).
+  auto run = [&](auto guarded) {
+    issue(0);
+    for (int s = 0; s < nk; ++s) {
+      wait_vmcnt<0>();            // this wave's share of stage s has landed ...
+      __syncthreads();            // ... and everyone's; everyone also left stage s - 1
+      if (s + 1 < nk) issue(s + 1);
+      const char* buf = lds + (s & 1) * TL::STAGE;
+      if constexpr (!decltype(guarded)::value) {
 #pragma unroll
-    for (int ks = 0; ks < Frag<T>::kSteps; ++ks) {
-      typename Frag<T>::V a[TL::FM], b[TL::FN];
+        for (int ks = 0; ks < Frag<T>::kSteps; ++ks) {
+          typename Frag<T>::V a[TL::FM], b[TL::FN];
 #pragma unroll
-      for (int i = 0; i < TL::FM; ++i) a[i] = Frag<T>::load(buf + arow[i], ks, kq, sw);
+          for (int i = 0; i < TL::FM; ++i) a[i] = Frag<T>::load(buf + arow[i], ks, kq, sw);
 #pragma unroll
-      for (int j = 0; j < TL::FN; ++j) b[j] = Frag<T>::load(buf + brow[j], ks, kq, sw);
+          for (int j = 0; j < TL::FN; ++j) b[j] = Frag<T>::load(buf + brow[j], ks, kq, sw);
 #pragma unroll
-      for (int i = 0; i < TL::FM; ++i)
+          for (int i = 0; i < TL::FM; ++i)
 #pragma unroll
-        for (int j = 0; j < TL::FN; ++j) acc[i][j] = Frag<T>::mma(a[i], b[j], acc[i][j]);
+            for (int j = 0; j < TL::FN; ++j) acc[i][j] = Frag<T>::mma(a[i], b[j], acc[i][j]);
+        }
+      } else if (nbusy > 0) {
+#pragma unroll
+        for (int ks = 0; ks < Frag<T>::kSteps; ++ks) {
+          typename Frag<T>::V b[TL::FN];
+#pragma unroll
+          for (int j = 0; j < TL::FN; ++j) b[j] = Frag<T>::load(buf + brow[j], ks, kq, sw);
+#pragma unroll
+          for (int i = 0; i < TL::FM; ++i) {
+            if (i < nbusy) {
+              const typename Frag<T>::V a = Frag<T>::load(buf + arow[i], ks, kq, sw);
+#pragma unroll
+              for (int j = 0; j < TL::FN; ++j) acc[i][j] = Frag<T>::mma(a, b[j], acc[i][j]);
+            }
+          }
+        }
+      }
     }
-  }
+  };
+  if (nbusy == TL::FM)
+    run(std::false_type{});
+  else
+    run(std::true_type{});
   __syncthreads();              // LDS free for the epilogue
 }
 
-// Accumulator element acc[i][j][r] of a lane sits at wave-tile row i*16 + 4*(lane >> 4) + r and
-// column j*16 + (lane & 15).
+// Accumulator element acc[i][j][r] of a lane sits at row 4*(lane >> 4) + r of the wave's block
+// i (tile row block_row(i, wm) + 4*(lane >> 4) + r) and at wave column j*16 + (lane & 15).
 
 // XCD-aware placement of a 1-D grid. Workgroups are handed to the 8 XCDs round-robin
 // (workgroup w runs on XCD w % 8), and each XCD has its own L2. Workgroup w takes tile
@@ -193,9 +235,10 @@ inline unsigned xcd_grid(int64_t n_tiles) {
   return static_cast<unsigned>((n_tiles + kXcds - 1) / kXcds * kXcds);
 }
 
-// Output of one wave's slab through LDS in 16-row rounds: the lanes write their accumulator
+// Output of one wave's blocks through LDS in 16-row rounds: the lanes write their accumulator
 // values (transformed by `val`) into a per-wave staging area, then store whole rows with
-// 16-byte vectors. row_of(r) maps a slab row to its global output row (or -1 to skip),
+// 16-byte vectors. row_of(16*i + r) maps row r of the wave's block i to its global output row
+// (or -1 to skip),
 // OUT is the stored element type, cols = columns of the slab that exist (<= NCOL).
 template <class TL, typename OUT, int NCOL, bool kStreamOut = false, class Val, class RowOf>
 __device__ __forceinline__ void store_slab(char* lds, Val val, RowOf row_of, OUT* out,
@@ -333,9 +376,9 @@ void gu_kernel(GuParams p) {
     const float hv = missing ? __builtin_nanf("") : silu_f32(acc[i][j][r]) * acc[i][j + H][r];
     return Elt<T>::store(hv);
   };
-  const int slab0 = wm * TL::TM;
-  auto row_of = [&](int sr) -> int64_t {
-    return slab0 + sr < rows ? row0 + slab0 + sr : -1;
+  auto row_of = [&](int sr) -> int64_t {      // sr = block * 16 + row in block
+    const int tr = block_row<TL>(sr >> 4, wm) + (sr & 15);
+    return tr < rows ? row0 + tr : -1;
   };
   const int col0 = n0h + wn * (TL::TN / 2);
   store_slab<TL, T, TL::TN / 2>(lds, val, row_of, static_cast<T*>(p.h), p.I, col0,
@@ -410,10 +453,10 @@ void down_kernel(DownParams p) {
   auto val = [&](int i, int j, int r) -> float {
     return missing ? __builtin_nanf("") : acc[i][j][r];
   };
-  const int slab0 = wm * TL::TM;
-  auto row_of = [&](int sr) -> int64_t {
-    if (slab0 + sr >= rows) return -1;
-    return kGrouped ? static_cast<int64_t>(p.row_slot[row0 + slab0 + sr]) : row0 + slab0 + sr;
+  auto row_of = [&](int sr) -> int64_t {      // sr = block * 16 + row in block
+    const int tr = block_row<TL>(sr >> 4, wm) + (sr & 15);
+    if (tr >= rows) return -1;
+    return kGrouped ? static_cast<int64_t>(p.row_slot[row0 + tr]) : row0 + tr;
   };
   const int col0 = n0 + wn * TL::TN;
   store_slab<TL, float, TL::TN, true>(lds, val, row_of, p.out, p.d, col0, min(TL::TN, p.d - col0));
@@ -465,8 +508,10 @@ void router_kernel(RouterParams p) {
     const int col = col0 + j * 16 + (lane & 15);
     return acc[i][j][r] + ((p.bias && col < p.E) ? p.bias[col] : 0.0f);
   };
-  const int slab0 = wm * TL::TM;
-  auto row_of = [&](int sr) -> int64_t { return slab0 + sr < rows ? row0 + slab0 + sr : -1; };
+  auto row_of = [&](int sr) -> int64_t {      // sr = block * 16 + row in block
+    const int tr = block_row<TL>(sr >> 4, wm) + (sr & 15);
+    return tr < rows ? row0 + tr : -1;
+  };
   store_slab<TL, float, TL::TN>(lds, val, row_of, p.logits, p.E, col0, min(TL::TN, p.E - col0));
   clock.finish();
 }

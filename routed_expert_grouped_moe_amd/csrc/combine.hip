@@ -12,8 +12,8 @@ template <typename T> struct Pack4;
 template <> struct Pack4<uint16_t> {
   static __device__ __forceinline__ void store(uint16_t* p, float4 v) {
     uint2 w;
-    w.x = static_cast<uint32_t>(f32_to_bf16(v.x)) | (static_cast<uint32_t>(f32_to_bf16(v.y)) << 16);
-    w.y = static_cast<uint32_t>(f32_to_bf16(v.z)) | (static_cast<uint32_t>(f32_to_bf16(v.w)) << 16);
+    w.x = f32x2_to_bf16x2(v.x, v.y);
+    w.y = f32x2_to_bf16x2(v.z, v.w);
     *reinterpret_cast<uint2*>(p) = w;
   }
   static __device__ __forceinline__ float4 load(const uint16_t* p) {

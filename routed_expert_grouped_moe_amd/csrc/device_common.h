@@ -23,12 +23,16 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
-// fp32 -> bf16, round to nearest, ties to even; NaN stays a (quiet) NaN.
+// fp32 -> bf16, round to nearest, ties to even; NaN stays a NaN. One v_cvt_pk_bf16_f32 (CDNA4):
+// for every non-NaN fp32 input it gives the bits of the textbook rounding (add 0x7fff plus the
+// lowest kept bit, truncate), which an exhaustive run over all 2^32 inputs confirmed.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float lo, float hi) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
+}
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  return static_cast<uint16_t>(f32x2_to_bf16x2(f, 0.0f));
 }
 
 // Storage element <-> fp32 for the two supported dtypes.
@@ -42,7 +46,12 @@ template <> struct Elt<float> {
   static __device__ __forceinline__ float store(float f) { return f; }
 };
 
-// silu(z) = z / (1 + e^-z), fp32 with the accurate device expf.
-__device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + expf(-z)); }
+// silu(z) = z / (1 + e^-z) with e^-z = 2^(-z log2(e)) from the hardware base-2 exponential and
+// the division as a multiply by the hardware reciprocal. Each is good to about 1 ulp of fp32,
+// and the rounding of -z log2(e) adds |z| * 2^-24 relative: a few 1e-6 at most over the range
+// where the result is not 0, against the 2^-9 of the bf16 rounding that follows.
+__device__ __forceinline__ float silu_f32(float z) {
+  return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
+}
 
 }  // namespace moe

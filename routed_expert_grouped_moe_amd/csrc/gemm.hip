@@ -372,9 +372,15 @@ void gu_kernel(GuParams p) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / TL::WN, wn = wave % TL::WN;
   constexpr int H = TL::FN / 2;
+  if (missing) {                // no weights for this expert: its h rows are NaN
+    const float nan = __builtin_nanf("");
+#pragma unroll
+    for (int i = 0; i < TL::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < TL::FN; ++j) acc[i][j] = f32x4_t{nan, nan, nan, nan};
+  }
   auto val = [&](int i, int j, int r) -> T {
-    const float hv = missing ? __builtin_nanf("") : silu_f32(acc[i][j][r]) * acc[i][j + H][r];
-    return Elt<T>::store(hv);
+    return Elt<T>::store(silu_f32(acc[i][j][r]) * acc[i][j + H][r]);
   };
   auto row_of = [&](int sr) -> int64_t {      // sr = block * 16 + row in block
     const int tr = block_row<TL>(sr >> 4, wm) + (sr & 15);
@@ -453,13 +459,31 @@ void down_kernel(DownParams p) {
   auto val = [&](int i, int j, int r) -> float {
     return missing ? __builtin_nanf("") : acc[i][j][r];
   };
-  auto row_of = [&](int sr) -> int64_t {      // sr = block * 16 + row in block
-    const int tr = block_row<TL>(sr >> 4, wm) + (sr & 15);
-    if (tr >= rows) return -1;
-    return kGrouped ? static_cast<int64_t>(p.row_slot[row0 + tr]) : row0 + tr;
-  };
   const int col0 = n0 + wn * TL::TN;
-  store_slab<TL, float, TL::TN, true>(lds, val, row_of, p.out, p.d, col0, min(TL::TN, p.d - col0));
+  if (kGrouped) {
+    // The output row (token slot) of each of the wave's rows, read once into LDS beside the
+    // staging area. Looked up per store instead, each lookup would wait on a global load, and
+    // that wait (vmcnt) also waits for every store the wave has issued before it.
+    const int lane = threadIdx.x & 63;
+    constexpr int kTab = TL::FM * 16;
+    constexpr int kStage = 16 * TL::TN * static_cast<int>(sizeof(float)) * TL::NW;
+    static_assert(kStage + TL::NW * kTab * 4 <= TL::LDS, "slot table fits in LDS");
+    int* tab = reinterpret_cast<int*>(lds + kStage) + wave * kTab;
+#pragma unroll
+    for (int idx = lane; idx < kTab; idx += 64) {
+      const int tr = block_row<TL>(idx >> 4, wm) + (idx & 15);
+      tab[idx] = tr < rows ? p.row_slot[row0 + tr] : -1;
+    }
+    __builtin_amdgcn_wave_barrier();  // a wave's LDS writes land before its later LDS reads
+    auto row_of = [&](int sr) -> int64_t { return tab[sr]; };   // sr = block * 16 + row
+    store_slab<TL, float, TL::TN, true>(lds, val, row_of, p.out, p.d, col0, min(TL::TN, p.d - col0));
+  } else {
+    auto row_of = [&](int sr) -> int64_t {    // sr = block * 16 + row in block
+      const int tr = block_row<TL>(sr >> 4, wm) + (sr & 15);
+      return tr < rows ? row0 + tr : -1;
+    };
+    store_slab<TL, float, TL::TN, true>(lds, val, row_of, p.out, p.d, col0, min(TL::TN, p.d - col0));
+  }
   clock.finish();
 }
 

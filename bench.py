@@ -209,7 +209,9 @@ def copy_probe(nbytes: int, runs: int) -> float:
     return 2 * a.numel() * 4 / (ms / 1e3) / 1e9
 
 
-def cpu_baseline(params, wl, x, n_tokens):
+def cpu_baseline(params, wl, x, seconds, chunk=1024):
+    """The fp64 oracle on the first tokens of the workload, in whole chunks of `chunk` tokens
+    until about `seconds` of CPU work have run (the rate differs a lot between hosts)."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
@@ -217,18 +219,22 @@ def cpu_baseline(params, wl, x, n_tokens):
     import oracle.moe_oracle as orc
     from tests.parity import oracle_params
     op = oracle_params(params, wl)
-    xs = mi.to_numpy_exact(x[:n_tokens])
     threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    t0 = time.perf_counter()
-    orc.moe_layer(xs, op)
-    dt = time.perf_counter() - t0
+    done, dt = 0, 0.0
+    while done < wl.T and dt < seconds:
+        n = min(chunk, wl.T - done)
+        xs = mi.to_numpy_exact(x[done:done + n])
+        t0 = time.perf_counter()
+        orc.moe_layer(xs, op)
+        dt += time.perf_counter() - t0
+        done += n
     sh = wl.shape
-    flop = n_tokens * (2 * sh.d * sh.n_experts + 6 * sh.d * sh.inter * sh.top_k
-                       + 6 * sh.d * sh.inter_shared)
-    return {"value": round(n_tokens / dt, 2), "unit": "tokens/s", "cores": int(threads),
+    flop = done * (2 * sh.d * sh.n_experts + 6 * sh.d * sh.inter * sh.top_k
+                   + 6 * sh.d * sh.inter_shared)
+    return {"value": round(done / dt, 2), "unit": "tokens/s", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"first {n_tokens} of the {wl.T} tokens, same layer (all 512 experts "
-                      f"widened from bf16 as used), fp64 numpy, {dt:.1f} s",
+            "sample": f"first {done} of the {wl.T} tokens in chunks of {chunk}, same layer "
+                      f"(all 512 experts widened from bf16 as used), fp64 numpy, {dt:.1f} s",
             "gflops_fp64": round(flop / dt / 1e9, 2)}
 
 
@@ -237,8 +243,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--cpu-sample-tokens", type=int, default=2048,
-                    help="tokens of the headline workload the fp64 oracle runs (about 10 s)")
+    ap.add_argument("--cpu-sample-seconds", type=float, default=12.0,
+                    help="seconds of fp64 oracle work on the headline workload's first tokens "
+                         "(whole chunks of 1,024 tokens)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--no-stack", action="store_true",
@@ -386,8 +393,8 @@ def main():
     copy_gbps = copy_probe(1 << 30, 5)
     cpu = None
     if not args.no_cpu_baseline:
-        log(f"[bench] CPU oracle baseline on {args.cpu_sample_tokens} tokens")
-        cpu = cpu_baseline(params, wl, x, args.cpu_sample_tokens)
+        log(f"[bench] CPU oracle baseline, about {args.cpu_sample_seconds:.0f} s")
+        cpu = cpu_baseline(params, wl, x, args.cpu_sample_seconds)
 
     line = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,

@@ -9,7 +9,7 @@ accumulation, T = 16,022 prompt tokens routed without bias, all experts resident
 as the batched pass (one chunk of T rows). Inputs and weights are seeded synthetic tensors,
 already in HBM when timing starts. One step = the whole path once: router GEMM, top-k,
 per-chunk counts, bucketing (histogram, scan, permute), shared and routed grouped GEMMs with
-the fused SiLU epilogue, and the combine.
+the fused SiLU epilogue, and the combine (folded into the shared down GEMM's epilogue).
 
 Prints one JSON line (stdout). Per-kernel times come from HIP events that the library records
 around each of its launches on the launch's own stream, over a second pass of the same K
@@ -61,6 +61,9 @@ def algorithmic(stage: str, T: int, sh, counts):
         return 2 * T * Is * d, d * Is * 2 + T * Is * 2 + T * d * 4
     if stage == "combine":
         return 2 * Ns * d, Ns * d * 4 + T * d * 4 + T * k * 4 + T * d * 2
+    if stage == "down_shared_combine":     # shared down GEMM with the combine in its epilogue
+        return (2 * T * Is * d + 2 * Ns * d,
+                d * Is * 2 + T * Is * 2 + Ns * d * 4 + T * k * 4 + T * d * 2)
     if stage in ("hist", "permute"):
         return 0, Ns * 4 * (1 if stage == "hist" else 3)
     return 0, 0
@@ -317,9 +320,12 @@ def main():
         if prof3[stage][2] > 0:
             ent["clock_mhz"] = round(prof3[stage][2], 0)
         kernels[stage] = ent
-    gemm = ["gu_routed", "down_routed", "gu_shared", "down_shared"]
+    gemm = [s for s in ("gu_routed", "down_routed", "gu_shared", "down_shared",
+                        "down_shared_combine") if prof[s][1] > 0]
     gemm_ms = sum(prof[s][0] for s in gemm) / args.steps
-    gemm_flop = sum(algorithmic(s, T, sh, counts)[0] for s in gemm)
+    # GEMM flops only (the fused combine's 2*k*d per token is not matrix work)
+    gemm_flop = sum(algorithmic(s, T, sh, counts)[0] for s in gemm) - (
+        2 * T * sh.top_k * sh.d if "down_shared_combine" in gemm else 0)
     dom = max(gemm, key=lambda s: prof[s][0])
     f, b = algorithmic(dom, T, sh, counts)
     n_l = prof[dom][1] / args.steps

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 2
+#define MOE_ABI_VERSION 3
 
 typedef enum {
   MOE_OK = 0,
@@ -135,7 +135,9 @@ moe_status moe_prefill_route(const moe_layer* layer, const void* x, int64_t T, i
 /* Expert-major prefill of rows [t0, t0+n) of a routed prompt: bucket the chunk's tokens per
  * expert (histogram, scan, stable permute on the GPU), run each expert's gate/up GEMM with the
  * fused silu(gate)*up epilogue and its down GEMM (grouped, bf16 MFMA, fp32 accumulation), the
- * shared expert over all n rows, then the fixed-order combine into out rows t0..t0+n-1.
+ * shared expert over all n rows, then the fixed-order combine into out rows t0..t0+n-1. With a
+ * shared expert its down GEMM runs last and forms the combine in its epilogue (same operations
+ * in the same order as the stand-alone combine, so the same bits).
  *   x, ids, weights: the whole prompt's tensors as passed to / returned by moe_prefill_route
  *   counts_host  HOST [E] int32 expert counts of this chunk, or NULL. Only used with a ring: if
  *                NULL the call copies the counts to the host and waits for them (its only
@@ -235,12 +237,14 @@ enum {
   MOE_STAGE_SCAN = 5,       /* expert offsets and M-tile list */
   MOE_STAGE_PERMUTE = 6,    /* stable member-list permute */
   MOE_STAGE_GU_SHARED = 7,
-  MOE_STAGE_DOWN_SHARED = 8,
+  MOE_STAGE_DOWN_SHARED = 8,  /* shared down GEMM alone (S); unused by the layer calls since
+                                 version 3, which fold it into the combine (stage 13) */
   MOE_STAGE_GU_ROUTED = 9,
   MOE_STAGE_DOWN_ROUTED = 10,
-  MOE_STAGE_COMBINE = 11,
+  MOE_STAGE_COMBINE = 11,    /* the combine alone: layers without a shared expert */
   MOE_STAGE_RMSNORM = 12,
-  MOE_STAGE_COUNT = 13
+  MOE_STAGE_DOWN_SHARED_COMBINE = 13, /* shared down GEMM with the combine in its epilogue */
+  MOE_STAGE_COUNT = 14
 };
 
 typedef struct {

@@ -38,7 +38,7 @@ class MoeProfile(ctypes.Structure):
 
 
 STAGES = ["router", "topk", "chunk_counts", "table", "hist", "scan", "permute", "gu_shared",
-          "down_shared", "gu_routed", "down_routed", "combine", "rmsnorm"]
+          "down_shared", "gu_routed", "down_routed", "combine", "rmsnorm", "down_shared_combine"]
 
 
 class MoeRingStats(ctypes.Structure):
@@ -78,7 +78,7 @@ SIGNATURES = {
 _lib = None
 
 
-ABI_VERSION = 2     # MOE_ABI_VERSION of include/moe_prefill.h
+ABI_VERSION = 3     # MOE_ABI_VERSION of include/moe_prefill.h
 
 
 def lib():

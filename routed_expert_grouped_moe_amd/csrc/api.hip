@@ -276,11 +276,11 @@ moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const i
                      ws_bytes, W.total, static_cast<long long>(n));
   char* ws = static_cast<char*>(ws_v);
   const void** wtab = reinterpret_cast<const void**>(ws + W.wtab);
-  float* sbuf = sh.inter_shared ? reinterpret_cast<float*>(ws + W.s) : nullptr;
-  // The shared expert depends only on x. With every expert resident it runs in order on
-  // the caller's stream: its GEMMs and the routed ones each fill the chip, and running them
+  // The shared expert's GU depends only on x. With every expert resident it runs in order
+  // on the caller's stream: its GEMM and the routed ones each fill the chip, and running them
   // side by side measured slower than in sequence. With a ring it runs on a side stream
-  // (joined before the combine), filling the time the routed GEMMs wait for copies.
+  // (joined before the last kernel), filling the time the routed GEMMs wait for copies. Its
+  // down GEMM runs last, with the combine folded into its epilogue.
   SideStream side;
   hipStream_t ss = offloaded ? nullptr : s;
   if (sh.inter_shared) {
@@ -290,8 +290,6 @@ moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const i
     }
     MOE_HIP(launch_gu_dense(sh.dtype, x, t0, n, sh.d, sh.inter_shared, L->w_gu_shared,
                             ws + W.h_shared, ss));
-    MOE_HIP(launch_down_dense(sh.dtype, ws + W.h_shared, n, sh.d, sh.inter_shared,
-                              L->w_down_shared, sbuf, ss));
     if (offloaded) MOE_HIP(side.record_done());
   }
   // Resident lines at a uniform stride (one block of E lines) need no table; otherwise the
@@ -319,7 +317,11 @@ moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const i
     if (sh.inter_shared) MOE_HIP(side.join(s));
     if (st != MOE_OK) return st;
   }
-  MOE_HIP(launch_combine(sh.dtype, y, sbuf, weights, t0, n, k, sh.d, out, s));
+  if (sh.inter_shared)
+    MOE_HIP(launch_down_combine(sh.dtype, ws + W.h_shared, n, sh.d, sh.inter_shared,
+                                L->w_down_shared, y, weights, t0, k, out, s));
+  else
+    MOE_HIP(launch_combine(sh.dtype, y, nullptr, weights, t0, n, k, sh.d, out, s));
   return MOE_OK;
 }
 
@@ -358,7 +360,6 @@ bool ws_layout(const moe_shape& sh, int64_t max_n, WsLayout* L) {
   L->h = take(elt * rows * I);
   L->h_shared = take(elt * max_n * Is);
   L->y = take(sizeof(float) * rows * d);
-  L->s = take(Is ? sizeof(float) * max_n * d : 0);
   L->total = off;
   L->max_n = max_n;
   L->max_rows = rows;

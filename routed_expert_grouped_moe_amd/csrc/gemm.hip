@@ -392,6 +392,99 @@ void gu_kernel(GuParams p) {
   clock.finish();
 }
 
+// Epilogue of the shared expert's down GEMM with the combine folded in. The tile holds S
+// (fp32) for its rows and columns; each (token, 4 columns) then gets
+//   acc = 0; acc = fma(w_j, y_j, acc) for j = 0 .. k-1 (ascending expert); acc += S;
+//   out = round(acc)
+// with the operations and their order of combine_kernel, so the bits do not depend on which
+// of the two formed them. A lane handles two 4-column chunks at a time, with the Y loads of
+// both in flight before their FMAs.
+template <class TL, typename T, class Val>
+__device__ __forceinline__ void combine_slab(char* lds, Val val, int wm, int64_t row0, int rows,
+                                             const float* __restrict__ y,
+                                             const float* __restrict__ wts, int64_t t0, int k,
+                                             int d, T* __restrict__ out, int col0, int cols) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int NCOL = TL::TN, RB = NCOL * 4, CPR = RB / 16, U = 2;
+  static_assert(16 * RB * TL::NW <= TL::LDS, "staging fits in LDS");
+  static_assert((16 * CPR) % (64 * U) == 0, "whole chunk pairs per block");
+  float* stg = reinterpret_cast<float*>(lds + wave * (16 * RB));
+#pragma unroll
+  for (int i = 0; i < TL::FM; ++i) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+      for (int j = 0; j < NCOL / 16; ++j)
+        stg[(4 * (lane >> 4) + r) * NCOL + j * 16 + (lane & 15)] = val(i, j, r);
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll 1
+    for (int c0 = lane; c0 < 16 * CPR; c0 += 64 * U) {
+      int64_t t[U];
+      int col[U];
+      bool on[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int c = c0 + 64 * u, row = c / CPR;
+        const int tr = block_row<TL>(i, wm) + row;
+        col[u] = (c % CPR) * 4;
+        on[u] = tr < rows && col[u] < cols;
+        t[u] = row0 + (on[u] ? tr : 0);
+      }
+      f32x4_t acc[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) acc[u] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      int j = 0;
+      for (; j + 8 <= k; j += 8) {
+        f32x4_t v[8][U];
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+          for (int u = 0; u < U; ++u)
+            v[q][u] = on[u] ? __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(
+                                  y + (t[u] * k + j + q) * d + col0 + col[u]))
+                            : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+            const float wj = wts[(t0 + t[u]) * k + j + q];
+            acc[u][0] = fmaf(wj, v[q][u][0], acc[u][0]);
+            acc[u][1] = fmaf(wj, v[q][u][1], acc[u][1]);
+            acc[u][2] = fmaf(wj, v[q][u][2], acc[u][2]);
+            acc[u][3] = fmaf(wj, v[q][u][3], acc[u][3]);
+          }
+      }
+      for (; j < k; ++j)
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const f32x4_t v = on[u] ? __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(
+                                        y + (t[u] * k + j) * d + col0 + col[u]))
+                                  : f32x4_t{0.f, 0.f, 0.f, 0.f};
+          const float wj = wts[(t0 + t[u]) * k + j];
+          acc[u][0] = fmaf(wj, v[0], acc[u][0]);
+          acc[u][1] = fmaf(wj, v[1], acc[u][1]);
+          acc[u][2] = fmaf(wj, v[2], acc[u][2]);
+          acc[u][3] = fmaf(wj, v[3], acc[u][3]);
+        }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (!on[u]) continue;
+        const int c = c0 + 64 * u;
+        const f32x4_t sv = *reinterpret_cast<const f32x4_t*>(stg + (c / CPR) * NCOL + col[u]);
+        const float a0 = acc[u][0] + sv[0], a1 = acc[u][1] + sv[1];
+        const float a2 = acc[u][2] + sv[2], a3 = acc[u][3] + sv[3];
+        T* o = out + (t0 + t[u]) * d + col0 + col[u];
+        if constexpr (sizeof(T) == 2) {
+          *reinterpret_cast<uint2*>(o) = uint2{f32x2_to_bf16x2(a0, a1), f32x2_to_bf16x2(a2, a3)};
+        } else {
+          *reinterpret_cast<f32x4_t*>(o) = f32x4_t{a0, a1, a2, a3};
+        }
+      }
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 struct DownParams {
   const void* h;          // [rows, K] intermediate
   int64_t n;              // dense: rows
@@ -400,8 +493,14 @@ struct DownParams {
   GemmGroups g;           // grouped: routed experts (down part of each line)
   int64_t line_down_off;  // grouped: element offset of W_down inside a line (2*I*d)
   const int32_t* row_slot;// grouped: output row (t*k + j) of each permuted row
-  float* out;             // grouped: Y [n*k, d]; dense: S [n, d]
+  float* out;             // grouped: Y [n*k, d]
   unsigned long long* clk;   // profiling clock counters of the stage, or NULL
+  // dense (the shared expert), with the combine in the epilogue; S stays in registers:
+  const float* y;         // Y [n*k, d], unweighted fp32 rows of the routed experts
+  const float* wts;       // [T, k] slot weights, row t0 + t for chunk token t
+  int64_t t0;             // first prompt row of the chunk
+  int k;                  // slots per token
+  void* cout;             // [T, d] layer output (dtype), rows t0 .. t0 + n - 1 written
 };
 
 template <typename T, class TL, bool kGrouped>
@@ -478,11 +577,8 @@ void down_kernel(DownParams p) {
     auto row_of = [&](int sr) -> int64_t { return tab[sr]; };   // sr = block * 16 + row
     store_slab<TL, float, TL::TN, true>(lds, val, row_of, p.out, p.d, col0, min(TL::TN, p.d - col0));
   } else {
-    auto row_of = [&](int sr) -> int64_t {    // sr = block * 16 + row in block
-      const int tr = block_row<TL>(sr >> 4, wm) + (sr & 15);
-      return tr < rows ? row0 + tr : -1;
-    };
-    store_slab<TL, float, TL::TN, true>(lds, val, row_of, p.out, p.d, col0, min(TL::TN, p.d - col0));
+    combine_slab<TL, T>(lds, val, wm, row0, rows, p.y, p.wts, p.t0, p.k, p.d,
+                        static_cast<T*>(p.cout), col0, min(TL::TN, p.d - col0));
   }
   clock.finish();
 }
@@ -636,13 +732,15 @@ hipError_t launch_down_routed(int dtype, const void* h, int d, int I, const Gemm
   return hipGetLastError();
 }
 
-hipError_t launch_down_dense(int dtype, const void* h, int64_t n, int d, int Is,
-                             const void* w_down, float* out, hipStream_t s) {
+hipError_t launch_down_combine(int dtype, const void* h, int64_t n, int d, int Is,
+                               const void* w_down, const float* y, const float* weights,
+                               int64_t t0, int k, void* out, hipStream_t s) {
   if (n <= 0 || Is <= 0) return hipSuccess;
-  ProfScope prof(MOE_STAGE_DOWN_SHARED, s);
+  ProfScope prof(MOE_STAGE_DOWN_SHARED_COMBINE, s);
   DownParams p{};
   p.h = h; p.n = n; p.d = d; p.K = Is; p.w = w_down; p.line_down_off = 0;
-  p.row_slot = nullptr; p.out = out; p.clk = prof_clock(MOE_STAGE_DOWN_SHARED);
+  p.row_slot = nullptr; p.out = nullptr; p.clk = prof_clock(MOE_STAGE_DOWN_SHARED_COMBINE);
+  p.y = y; p.wts = weights; p.t0 = t0; p.k = k; p.cout = out;
   const int64_t nt_big = (d + BigTile::BN - 1) / BigTile::BN;
   if (use_big_dense(n, nt_big)) {
     const unsigned grid = xcd_grid((n + BigTile::BM - 1) / BigTile::BM * nt_big);

@@ -25,7 +25,7 @@ struct MTile {                    // one M-tile of a routed expert: rows [m0, m0
 // Workspace layout for chunks of up to max_n tokens (all offsets 256-byte aligned).
 struct WsLayout {
   size_t wtab, blk_counts, blk_base, counts, offsets, meta, mtiles, row_tok, row_slot;
-  size_t h, h_shared, y, s, total;
+  size_t h, h_shared, y, total;
   int64_t max_n, max_rows, max_mtiles, n_blocks;
 };
 MOE_HIDDEN bool ws_layout(const moe_shape& sh, int64_t max_n, WsLayout* out);
@@ -78,8 +78,11 @@ MOE_HIDDEN hipError_t launch_gu_dense(int dtype, const void* x, int64_t t0, int6
 MOE_HIDDEN hipError_t launch_down_routed(int dtype, const void* h, int d, int I,
                                          const GemmGroups& g, const int32_t* row_slot,
                                          float* y, hipStream_t s);
-MOE_HIDDEN hipError_t launch_down_dense(int dtype, const void* h, int64_t n, int d, int Is,
-                                        const void* w_down, float* out, hipStream_t s);
+// The shared expert's down GEMM with the combine folded in: out rows t0 .. t0 + n - 1.
+MOE_HIDDEN hipError_t launch_down_combine(int dtype, const void* h, int64_t n, int d, int Is,
+                                          const void* w_down, const float* y,
+                                          const float* weights, int64_t t0, int k, void* out,
+                                          hipStream_t s);
 MOE_HIDDEN hipError_t launch_combine(int dtype, const float* y, const float* shared,
                                      const float* weights, int64_t t0, int64_t n, int k, int d,
                                      void* out, hipStream_t s);

@@ -303,11 +303,12 @@ def test_profile_times_and_clocks(moe):
     finally:
         moe.moe_profile_enable(False)
     prof = moe.moe_profile_read(reset=True, clocks=True)
-    for stage in ("router", "gu_routed", "down_routed", "gu_shared", "down_shared"):
+    for stage in ("router", "gu_routed", "down_routed", "gu_shared", "down_shared_combine"):
         ms, n, mhz = prof[stage]
         assert n >= 1 and ms > 0, (stage, prof[stage])
         assert 100 < mhz < 3500, (stage, mhz)
-    assert prof["combine"][1] == 3 and prof["combine"][2] == 0      # 3 chunks; not sampled
+    assert prof["down_shared_combine"][1] == 3                    # one per chunk
+    assert prof["combine"][1] == 0 and prof["down_shared"][1] == 0  # folded together
     _run(moe, L, x, 256)
     assert all(v[1] == 0 for v in moe.moe_profile_read(reset=True).values())
 

@@ -7,46 +7,13 @@
 #include "device_common.h"
 #include "moe_internal.h"
 #include "profile.h"
+#include "topk_select.h"
 
 namespace moe {
 namespace {
 
-// Orderable 32-bit key of a float: a > b as floats (no NaN) iff key(a) > key(b) as unsigned.
-// Every key of a real value is above 0x007FFFFF (the key of -inf); 0 marks a taken or missing
-// entry.
-__device__ __forceinline__ uint32_t order_key(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-__device__ __forceinline__ float key_value(uint32_t key) {
-  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
-}
-
-// Wavefront maximum of an unsigned key with DPP moves: within quads, mirrored half rows and
-// rows, then row broadcasts; the result is valid in lane 63.
-template <int kCtrl, int kRowMask>
-__device__ __forceinline__ uint32_t dpp_max_step(uint32_t m) {
-  const uint32_t o = static_cast<uint32_t>(__builtin_amdgcn_update_dpp(
-      static_cast<int>(m), static_cast<int>(m), kCtrl, kRowMask, 0xF, false));
-  return o > m ? o : m;
-}
-__device__ __forceinline__ uint32_t wave_max(uint32_t m) {
-  m = dpp_max_step<0xB1, 0xF>(m);     // quad_perm [1,0,3,2]
-  m = dpp_max_step<0x4E, 0xF>(m);     // quad_perm [2,3,0,1]
-  m = dpp_max_step<0x141, 0xF>(m);    // row_half_mirror
-  m = dpp_max_step<0x140, 0xF>(m);    // row_mirror
-  m = dpp_max_step<0x142, 0xA>(m);    // row_bcast:15 into rows 1 and 3
-  m = dpp_max_step<0x143, 0xC>(m);    // row_bcast:31 into rows 2 and 3
-  return static_cast<uint32_t>(__builtin_amdgcn_readlane(static_cast<int>(m), 63));
-}
-
-// One wavefront per token; lane l holds the logits of experts l, l + 64, ..., l + 64 (NJ-1).
-// k rounds pick the k largest logits, the lower id among equal values, NaN ranking as -inf
-// (and -0 as +0): a round takes the wavefront maximum of the untaken keys, then the lowest id
-// holding it (the first 64-expert slice with a match, its lowest lane, by ballots). The chosen
-// ids are written in ascending order by a ballot compaction, and each weight is
-// exp(l - l_max) / (sum over the chosen of exp(l' - l_max), taken in ascending id), which
-// equals the softmax over all experts renormalised over the chosen ones.
+// One wavefront per token (topk_select); lane l loads the logits of experts l, l + 64, ...
+// (one token per wavefront measured faster than two interleaved: occupancy hides the latency)
 template <int NJ>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int64_t T,
                                                    int E, int k, int32_t* __restrict__ ids,
@@ -54,67 +21,17 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   __shared__ float ex[4][1024];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + wv;
-  const bool active = t < T;
-
-  float v[NJ];
-  uint32_t key[NJ];
+  float x[1][NJ];
 #pragma unroll
   for (int j = 0; j < NJ; ++j) {
     const int e = lane + 64 * j;
-    float x = -INFINITY;
-    if (active && e < E) x = logits[t * E + e];
-    if (x != x) x = -INFINITY;
-    if (x == 0.f) x = 0.f;     // -0 and +0 are equal logits: one key for both
-    v[j] = x;
-    key[j] = e < E ? order_key(x) : 0u;
+    x[0][j] = (t < T && e < E) ? logits[t * E + e] : -INFINITY;
   }
-  uint32_t taken = 0;
-  float vmax = 0.f;
-  for (int r = 0; r < k; ++r) {
-    uint32_t m = key[0];
-#pragma unroll
-    for (int j = 1; j < NJ; ++j) m = key[j] > m ? key[j] : m;
-    const uint32_t best = wave_max(m);
-    int jw = 0, lw = 0;
-#pragma unroll
-    for (int j = NJ - 1; j >= 0; --j) {   // ends at the lowest slice holding the maximum
-      const uint64_t b = __ballot(key[j] == best);
-      if (b) {
-        jw = j;
-        lw = __ffsll(static_cast<unsigned long long>(b)) - 1;
-      }
-    }
-    if (r == 0) vmax = key_value(best);
-    if (lane == lw) {
-#pragma unroll
-      for (int j = 0; j < NJ; ++j)
-        if (j == jw) {
-          key[j] = 0u;
-          taken |= 1u << j;
-        }
-    }
-  }
-  int base = 0;
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const bool tk = (taken >> j) & 1u;
-    const uint64_t m = __ballot(tk);
-    if (tk) {
-      const int pos = base + __popcll(m & ((1ull << lane) - 1ull));
-      if (active) ids[t * k + pos] = lane + 64 * j;
-      ex[wv][pos] = v[j];
-    }
-    base += __popcll(m);
-  }
-  __syncthreads();
-  for (int p = lane; p < k; p += 64) ex[wv][p] = expf(ex[wv][p] - vmax);
-  __syncthreads();
-  float sum = 0.f;
-  if (lane == 0)
-    for (int p = 0; p < k; ++p) sum += ex[wv][p];
-  sum = __shfl(sum, 0);
-  if (active)
-    for (int p = lane; p < k; p += 64) weights[t * k + p] = ex[wv][p] / sum;
+  const bool act[1] = {t < T};
+  int32_t* const idr[1] = {ids + t * k};
+  float* const wr[1] = {weights + t * k};
+  float* const exr[1] = {ex[wv]};
+  topk_select<NJ, 1>(x, E, k, act, idr, wr, exr);
 }
 
 // Per-chunk expert counts. Block b covers tokens [256 b, 256 b + 256); when the chunks it

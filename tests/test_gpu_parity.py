@@ -236,6 +236,20 @@ def test_workspace_too_small_leaves_output(moe):
     assert torch.equal(bits(out), bits(full))
 
 
+def test_router_logits_independent_of_tile_shape(moe):
+    """The router GEMM picks its tile (64 or 128 rows) from T; a token's logits, and so its
+    routing, are the same bytes either way."""
+    wl = mi.custom_workload("rtile", T=12288, d=256, E=512, k=8, inter=64, inter_shared=0,
+                            seed=23)
+    params, L = place(wl)
+    x = mi.make_x(wl, device="cuda")
+    big = moe.moe_prefill_route(L, x, 12288)      # 96 x 2 = 192 tiles of 128 rows
+    small = moe.moe_prefill_route(L, x[:700].contiguous(), 700)   # 64-row tiles
+    torch.cuda.synchronize()
+    for key in ("logits", "ids", "weights"):
+        assert torch.equal(bits(big[key][:700]), bits(small[key])), key
+
+
 def test_layer_3001(moe):
     """bf16 layer, T = 3,001, all experts resident: deep chunk 1,024 equals the batched pass
     bit for bit, and both match the oracle."""

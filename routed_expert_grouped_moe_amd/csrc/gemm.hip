@@ -1,5 +1,6 @@
 // GEMMs of the layer on CDNA4 matrix cores: the router, each expert's gate/up projection with
-// the fused silu(gate)*up epilogue, and each expert's down projection.
+// the fused silu(gate)*up epilogue, each expert's down projection, and the shared expert's
+// down projection with the combine in its epilogue.
 //
 // Every GEMM here is X W^T with both operands K-contiguous (token rows and weight rows). A
 // workgroup computes a BM x BN tile; K advances 128 bytes per row and stage (64 bf16 or 32
@@ -12,9 +13,10 @@
 // 16-row block of the tile and accumulates 16 x 16 MFMA blocks: v_mfma_f32_16x16x32_bf16
 // (bf16) or v_mfma_f32_16x16x4_f32 (fp32), fp32 accumulation.
 //
-// Three tile shapes: tall (320 x 256, 8 waves of 80 x 128) and big (256 x 256, 8 waves of
+// Four tile shapes: tall (320 x 256, 8 waves of 80 x 128) and big (256 x 256, 8 waves of
 // 64 x 128) for large row counts, small (64 x 256, 4 waves of 64 x 64) for few rows per
-// expert. Which one runs never changes a bit: every output element is one token row against
+// expert, and mid (128 x 256, 8 waves of 64 x 64) for the router. Which one runs never
+// changes a bit: every output element is one token row against
 // one weight row, accumulated over K in the same stage order with the same instruction and the
 // same lane-to-K mapping in all of them. Together with
 // no split-K, no atomics and no shape-dependent arithmetic, that is what makes a token's bytes

@@ -40,8 +40,10 @@ MOE_HIDDEN hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStrea
 MOE_HIDDEN hipError_t launch_router_gemm(int dtype, const void* x, const void* w_router,
                                          const float* bias, int64_t T, int d, int E,
                                          float* logits, hipStream_t s);
+// Also zeroes n_zero ints at `zero` (the per-chunk counts launch_chunk_hist then adds to).
 MOE_HIDDEN hipError_t launch_topk(const float* logits, int64_t T, int E, int k, int32_t* ids,
-                                  float* weights, hipStream_t s);
+                                  float* weights, int32_t* zero, int64_t n_zero, hipStream_t s);
+// chunk_counts must be zero on entry (launch_topk zeroes them).
 MOE_HIDDEN hipError_t launch_chunk_hist(const int32_t* ids, int64_t T, int k, int E,
                                         int64_t chunk, int32_t* chunk_counts, hipStream_t s);
 

@@ -14,11 +14,17 @@ namespace {
 
 // One wavefront per token (topk_select); lane l loads the logits of experts l, l + 64, ...
 // (one token per wavefront measured faster than two interleaved: occupancy hides the latency)
+// The kernel also zeroes n_zero ints at `zero` (the per-chunk counts the next kernel adds
+// to), so that needs no launch of its own.
 template <int NJ>
 __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ logits, int64_t T,
                                                    int E, int k, int32_t* __restrict__ ids,
-                                                   float* __restrict__ weights) {
+                                                   float* __restrict__ weights,
+                                                   int32_t* __restrict__ zero, int64_t n_zero) {
   __shared__ float ex[4][1024];
+  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n_zero;
+       i += static_cast<int64_t>(gridDim.x) * 256)
+    zero[i] = 0;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + wv;
   float x[1][NJ];
@@ -77,25 +83,23 @@ hipError_t launch_fill_i32(int32_t* p, int64_t n, int32_t v, hipStream_t s) {
 }
 
 hipError_t launch_topk(const float* logits, int64_t T, int E, int k, int32_t* ids,
-                       float* weights, hipStream_t s) {
+                       float* weights, int32_t* zero, int64_t n_zero, hipStream_t s) {
   if (T <= 0) return hipSuccess;
   ProfScope prof(MOE_STAGE_TOPK, s);
   const unsigned blocks = static_cast<unsigned>((T + 3) / 4);
   const int nj = (E + 63) / 64;
-  if (nj <= 1) topk_kernel<1><<<blocks, 256, 0, s>>>(logits, T, E, k, ids, weights);
-  else if (nj <= 2) topk_kernel<2><<<blocks, 256, 0, s>>>(logits, T, E, k, ids, weights);
-  else if (nj <= 4) topk_kernel<4><<<blocks, 256, 0, s>>>(logits, T, E, k, ids, weights);
-  else if (nj <= 8) topk_kernel<8><<<blocks, 256, 0, s>>>(logits, T, E, k, ids, weights);
-  else topk_kernel<16><<<blocks, 256, 0, s>>>(logits, T, E, k, ids, weights);
+  if (nj <= 1) topk_kernel<1><<<blocks, 256, 0, s>>>(logits, T, E, k, ids, weights, zero, n_zero);
+  else if (nj <= 2) topk_kernel<2><<<blocks, 256, 0, s>>>(logits, T, E, k, ids, weights, zero, n_zero);
+  else if (nj <= 4) topk_kernel<4><<<blocks, 256, 0, s>>>(logits, T, E, k, ids, weights, zero, n_zero);
+  else if (nj <= 8) topk_kernel<8><<<blocks, 256, 0, s>>>(logits, T, E, k, ids, weights, zero, n_zero);
+  else topk_kernel<16><<<blocks, 256, 0, s>>>(logits, T, E, k, ids, weights, zero, n_zero);
   return hipGetLastError();
 }
 
 hipError_t launch_chunk_hist(const int32_t* ids, int64_t T, int k, int E, int64_t chunk,
                              int32_t* chunk_counts, hipStream_t s) {
-  const int64_t n_chunks = (T + chunk - 1) / chunk;
   ProfScope prof(MOE_STAGE_CHUNK_COUNTS, s);
-  hipError_t err = launch_fill_i32(chunk_counts, n_chunks * E, 0, s);
-  if (err != hipSuccess || T <= 0) return err;
+  if (T <= 0) return hipSuccess;      // chunk_counts were zeroed by the top-k kernel
   chunk_hist_kernel<<<static_cast<unsigned>((T + 255) / 256), 256, 0, s>>>(ids, T, k, E, chunk,
                                                                            chunk_counts);
   return hipGetLastError();

@@ -34,16 +34,18 @@ namespace {
 
 constexpr int kRowBytes = 128;     // K bytes per row per stage
 
-template <int BM_, int BN_, int WM_, int WN_>
+template <int BM_, int BN_, int WM_, int WN_, int NBUF_ = 2>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
+  static constexpr int NBUF = NBUF_;                        // LDS stage buffers (NBUF - 1 in flight)
   static constexpr int NW = WM * WN, NT = 64 * NW;
   static constexpr int TM = BM / WM, TN = BN / WN;          // wave tile
   static constexpr int FM = TM / 16, FN = TN / 16;          // 16 x 16 MFMA blocks per wave
   static constexpr int ROWS = BM + BN;
   static constexpr int STAGE = ROWS * kRowBytes;
-  static constexpr int LDS = 2 * STAGE;
+  static constexpr int LDS = NBUF * STAGE;
   static constexpr int LPW = ROWS / 8 / NW;                 // load instructions per wave per stage
+  static_assert(NBUF == 2 || NBUF == 4, "two or four stage buffers");
   static_assert(TM % 16 == 0 && TN % 16 == 0, "whole 16 x 16 MFMA blocks per wave");
   static_assert(ROWS % (8 * NW) == 0, "whole load instructions per wave");
 };
@@ -51,6 +53,9 @@ using BigTile = Tile<256, 256, 4, 2>;      // 8 waves, 64 x 128 each; 128 KB LDS
 using TallTile = Tile<320, 256, 4, 2>;     // 8 waves, 80 x 128 each; 144 KB LDS, 1 workgroup/CU
 using SmallTile = Tile<64, 256, 1, 4>;     // 4 waves, 64 x 64 each; 80 KB LDS, 2 workgroups/CU
 using MidTile = Tile<128, 256, 2, 4>;      // 8 waves, 64 x 64 each; 96 KB LDS, 1 workgroup/CU
+// Decode-sized calls: a GEMM of at most 16 rows has few tiles, and each walks its K stages one
+// round trip at a time; narrow one-wave tiles with three stages in flight (40 KB LDS).
+using DecodeTile = Tile<16, 64, 1, 1, 4>;
 
 // Wave rows: wave row-group wm owns the tile's 16-row blocks wm, wm + WM, wm + 2 WM, ...
 // (block i of the wave starts at tile row (i * WM + wm) * 16). Interleaving keeps the work of
@@ -156,7 +161,7 @@ __device__ __forceinline__ void mainloop(const char* const (&src)[TL::LPW], int 
   // M0 is a reserved register to the compiler (hence the silenced warning); no other code in
   // these kernels uses it, which tests/test_isa_guard.py checks on the compiled ISA.
   auto issue = [&](int s) {
-    const uint32_t dst = wave_lds + static_cast<uint32_t>((s & 1) * TL::STAGE);
+    const uint32_t dst = wave_lds + static_cast<uint32_t>((s % TL::NBUF) * TL::STAGE);
 #pragma unroll
     for (int q = 0; q < TL::LPW; ++q) {
 #pragma clang diagnostic push
@@ -170,13 +175,25 @@ __device__ __forceinline__ void mainloop(const char* const (&src)[TL::LPW], int 
   };
   // Two copies of the stage loop: every block valid (straight-line fragment reads, then the
   // MFMAs), or a partly valid wave that skips the blocks past `rows` (uniform branches).
+  // With NBUF buffers, stages s + 1 .. s + NBUF - 2 stay in flight while stage s is waited
+  // for (a wave's loads complete in issue order, so vmcnt(ahead * LPW) is enough).
+  auto wait_stage = [&](int s) {
+    if constexpr (TL::NBUF == 2) {
+      wait_vmcnt<0>();
+    } else {
+      const int ahead = min(TL::NBUF - 2, nk - 1 - s);
+      if (ahead >= 2) wait_vmcnt<2 * TL::LPW>();
+      else if (ahead == 1) wait_vmcnt<TL::LPW>();
+      else wait_vmcnt<0>();
+    }
+  };
   auto run = [&](auto guarded) {
-    issue(0);
+    for (int s = 0; s < TL::NBUF - 1 && s < nk; ++s) issue(s);
     for (int s = 0; s < nk; ++s) {
-      wait_vmcnt<0>();            // this wave's share of stage s has landed ...
+      wait_stage(s);              // this wave's share of stage s has landed ...
       __syncthreads();            // ... and everyone's; everyone also left stage s - 1
-      if (s + 1 < nk) issue(s + 1);
-      const char* buf = lds + (s & 1) * TL::STAGE;
+      if (s + TL::NBUF - 1 < nk) issue(s + TL::NBUF - 1);
+      const char* buf = lds + (s % TL::NBUF) * TL::STAGE;
       if constexpr (!decltype(guarded)::value) {
 #pragma unroll
         for (int ks = 0; ks < Frag<T>::kSteps; ++ks) {
@@ -651,6 +668,7 @@ int routed_tile_rows(int64_t n, int k, int E) {
   // a = mean rows per expert. With a in [192, 320) many experts hold just over 256 rows; a
   // 320-row tile keeps them in one tile instead of a full tile plus a nearly empty one.
   const int64_t rows = n * k, e = static_cast<int64_t>(E);
+  if (rows < e * 16) return DecodeTile::BM;
   if (rows >= e * 192 && rows < e * 320) return TallTile::BM;
   return rows >= e * 128 ? BigTile::BM : SmallTile::BM;
 }
@@ -661,7 +679,11 @@ hipError_t launch_router_gemm(int dtype, const void* x, const void* w_router, co
   ProfScope prof(MOE_STAGE_ROUTER, s);
   RouterParams p{x, w_router, bias, logits, T, d, E, prof_clock(MOE_STAGE_ROUTER)};
   const int64_t mid_tiles = (T + MidTile::BM - 1) / MidTile::BM * ((E + MidTile::BN - 1) / MidTile::BN);
-  if (use_big_dense(T, (E + BigTile::BN - 1) / BigTile::BN)) {
+  if (T <= DecodeTile::BM) {
+    const unsigned grid = xcd_grid((E + DecodeTile::BN - 1) / DecodeTile::BN);
+    if (dtype == MOE_BF16) router_kernel<uint16_t, DecodeTile><<<grid, DecodeTile::NT, 0, s>>>(p);
+    else router_kernel<float, DecodeTile><<<grid, DecodeTile::NT, 0, s>>>(p);
+  } else if (use_big_dense(T, (E + BigTile::BN - 1) / BigTile::BN)) {
     const unsigned grid = xcd_grid((T + BigTile::BM - 1) / BigTile::BM * ((E + BigTile::BN - 1) / BigTile::BN));
     if (dtype == MOE_BF16) router_kernel<uint16_t, BigTile><<<grid, BigTile::NT, 0, s>>>(p);
     else router_kernel<float, BigTile><<<grid, BigTile::NT, 0, s>>>(p);
@@ -696,6 +718,7 @@ hipError_t launch_gu_routed(int dtype, const void* x, int64_t t0, int d, int I,
   p.row_tok = row_tok; p.h = h; p.clk = prof_clock(MOE_STAGE_GU_ROUTED);
   if (g.tile_rows == TallTile::BM) gu_routed<TallTile>(dtype, p, g, I, s);
   else if (g.tile_rows == BigTile::BM) gu_routed<BigTile>(dtype, p, g, I, s);
+  else if (g.tile_rows == DecodeTile::BM) gu_routed<DecodeTile>(dtype, p, g, I, s);
   else gu_routed<SmallTile>(dtype, p, g, I, s);
   return hipGetLastError();
 }
@@ -708,7 +731,11 @@ hipError_t launch_gu_dense(int dtype, const void* x, int64_t t0, int64_t n, int 
   p.x = x; p.t0 = t0; p.n = n; p.d = d; p.I = Is; p.w = w_gu; p.row_tok = nullptr; p.h = h;
   p.clk = prof_clock(MOE_STAGE_GU_SHARED);
   const int64_t nt_big = (Is + BigTile::BN / 2 - 1) / (BigTile::BN / 2);
-  if (use_big_dense(n, nt_big)) {
+  if (n <= DecodeTile::BM) {
+    const unsigned grid = xcd_grid((Is + DecodeTile::BN / 2 - 1) / (DecodeTile::BN / 2));
+    if (dtype == MOE_BF16) gu_kernel<uint16_t, DecodeTile, false><<<grid, DecodeTile::NT, 0, s>>>(p);
+    else gu_kernel<float, DecodeTile, false><<<grid, DecodeTile::NT, 0, s>>>(p);
+  } else if (use_big_dense(n, nt_big)) {
     const unsigned grid = xcd_grid((n + BigTile::BM - 1) / BigTile::BM * nt_big);
     if (dtype == MOE_BF16) gu_kernel<uint16_t, BigTile, false><<<grid, BigTile::NT, 0, s>>>(p);
     else gu_kernel<float, BigTile, false><<<grid, BigTile::NT, 0, s>>>(p);
@@ -739,6 +766,7 @@ hipError_t launch_down_routed(int dtype, const void* h, int d, int I, const Gemm
   p.clk = prof_clock(MOE_STAGE_DOWN_ROUTED);
   if (g.tile_rows == TallTile::BM) down_routed<TallTile>(dtype, p, g, d, s);
   else if (g.tile_rows == BigTile::BM) down_routed<BigTile>(dtype, p, g, d, s);
+  else if (g.tile_rows == DecodeTile::BM) down_routed<DecodeTile>(dtype, p, g, d, s);
   else down_routed<SmallTile>(dtype, p, g, d, s);
   return hipGetLastError();
 }
@@ -753,7 +781,11 @@ hipError_t launch_down_combine(int dtype, const void* h, int64_t n, int d, int I
   p.row_slot = nullptr; p.out = nullptr; p.clk = prof_clock(MOE_STAGE_DOWN_SHARED_COMBINE);
   p.y = y; p.wts = weights; p.t0 = t0; p.k = k; p.cout = out;
   const int64_t nt_big = (d + BigTile::BN - 1) / BigTile::BN;
-  if (use_big_dense(n, nt_big)) {
+  if (n <= DecodeTile::BM) {
+    const unsigned grid = xcd_grid((d + DecodeTile::BN - 1) / DecodeTile::BN);
+    if (dtype == MOE_BF16) down_kernel<uint16_t, DecodeTile, false><<<grid, DecodeTile::NT, 0, s>>>(p);
+    else down_kernel<float, DecodeTile, false><<<grid, DecodeTile::NT, 0, s>>>(p);
+  } else if (use_big_dense(n, nt_big)) {
     const unsigned grid = xcd_grid((n + BigTile::BM - 1) / BigTile::BM * nt_big);
     if (dtype == MOE_BF16) down_kernel<uint16_t, BigTile, false><<<grid, BigTile::NT, 0, s>>>(p);
     else down_kernel<float, BigTile, false><<<grid, BigTile::NT, 0, s>>>(p);

@@ -13,7 +13,7 @@
 namespace moe {
 
 // ------------------------------------------------------------------ tiling constants
-constexpr int kMinTileRows = 64;  // smallest M-tile height of the routed GEMMs
+constexpr int kMinTileRows = 16;  // smallest M-tile height of the routed GEMMs
 constexpr int kTokBlock = 256;    // tokens per block of the bucketing kernels
 
 // ------------------------------------------------------------------ device-side records

@@ -4,25 +4,27 @@
 //
 // Every GEMM here is X W^T with both operands K-contiguous (token rows and weight rows). A
 // workgroup computes a BM x BN tile; K advances 128 bytes per row and stage (64 bf16 or 32
-// fp32 elements) through two LDS stages filled by direct global->LDS loads
-// (global_load_lds_dwordx4: each lane's 16 bytes land at the instruction's LDS base plus
-// 16 x lane, so one instruction fills 8 rows of 128 bytes; the A rows of a routed tile are
-// gathered from the prompt by pointer, no permuted copy of x exists). Inside LDS, 16-byte
-// segment g of row r sits at segment g ^ (r & 7), so the 16 lanes that read one MFMA operand
-// (16 rows, same K segment) hit 16 different bank groups. A wave row-group owns every WM-th
-// 16-row block of the tile and accumulates 16 x 16 MFMA blocks: v_mfma_f32_16x16x32_bf16
-// (bf16) or v_mfma_f32_16x16x4_f32 (fp32), fp32 accumulation.
+// fp32 elements) through two LDS stages (four in the decode tile) filled by direct
+// global->LDS loads (global_load_lds_dwordx4: each lane's 16 bytes land at the instruction's
+// LDS base plus 16 x lane, so one instruction fills 8 rows of 128 bytes; the stage's
+// instructions go round-robin over the waves, so every wave loads a share of both operands;
+// the A rows of a routed tile are gathered from the prompt by pointer, no permuted copy of x
+// exists). Inside LDS, 16-byte segment g of row r sits at segment g ^ (r & 7), so any 8
+// consecutive lanes reading one MFMA operand (8 rows, same K segment) hit 8 different bank
+// groups. A wave row-group owns every WM-th 16-row block of the tile and accumulates
+// 16 x 16 MFMA blocks: v_mfma_f32_16x16x32_bf16 (bf16) or v_mfma_f32_16x16x4_f32 (fp32),
+// fp32 accumulation.
 //
-// Four tile shapes: tall (320 x 256, 8 waves of 80 x 128) and big (256 x 256, 8 waves of
+// Five tile shapes: tall (320 x 256, 8 waves of 80 x 128) and big (256 x 256, 8 waves of
 // 64 x 128) for large row counts, small (64 x 256, 4 waves of 64 x 64) for few rows per
-// expert, and mid (128 x 256, 8 waves of 64 x 64) for the router. Which one runs never
-// changes a bit: every output element is one token row against
-// one weight row, accumulated over K in the same stage order with the same instruction and the
-// same lane-to-K mapping in all of them. Together with
-// no split-K, no atomics and no shape-dependent arithmetic, that is what makes a token's bytes
-// independent of the chunk size, of its position and of its expert's row count -- the
-// property the exact deep prefill page ("Flash Next EXL3: exact deep prefill", opening section)
-// asks of its GU/down kernels.
+// expert, mid (128 x 256, 8 waves of 64 x 64) for the router, and decode (16 x 64, one wave)
+// for calls of a few tokens. Which one runs never changes a bit: every output element is one
+// token row against one weight row, accumulated over K in the same stage order with the same
+// instruction and the same lane-to-K mapping in all of them. Together with no split-K, no
+// atomics and no shape-dependent arithmetic, that is what makes a token's bytes independent
+// of the chunk size, of its position and of its expert's row count -- the property the exact
+// deep prefill page ("Flash Next EXL3: exact deep prefill", opening section) asks of its
+// GU/down kernels.
 #include <type_traits>
 
 #include "device_common.h"
@@ -32,22 +34,30 @@
 namespace moe {
 namespace {
 
-constexpr int kRowBytes = 128;     // K bytes per row per stage
-
-template <int BM_, int BN_, int WM_, int WN_, int NBUF_ = 2>
+// RB_: K bytes per row and stage, 128 (64 bf16 / 32 fp32 elements) or 64. A 1 KB load
+// instruction fills RPL = 1024 / RB rows, and the stage's NBLK instructions go round-robin
+// over the waves (block b to wave b % NW): with NBLK not a multiple of NW the first FULL
+// waves issue LPW of them and the rest LPW - 1.
+template <int BM_, int BN_, int WM_, int WN_, int NBUF_ = 2, int RB_ = 128>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
   static constexpr int NBUF = NBUF_;                        // LDS stage buffers (NBUF - 1 in flight)
+  static constexpr int RB = RB_;
   static constexpr int NW = WM * WN, NT = 64 * NW;
   static constexpr int TM = BM / WM, TN = BN / WN;          // wave tile
   static constexpr int FM = TM / 16, FN = TN / 16;          // 16 x 16 MFMA blocks per wave
   static constexpr int ROWS = BM + BN;
-  static constexpr int STAGE = ROWS * kRowBytes;
+  static constexpr int STAGE = ROWS * RB;
   static constexpr int LDS = NBUF * STAGE;
-  static constexpr int LPW = ROWS / 8 / NW;                 // load instructions per wave per stage
-  static_assert(NBUF == 2 || NBUF == 4, "two or four stage buffers");
+  static constexpr int SPR = RB / 16;                       // 16-byte segments per row
+  static constexpr int RPL = 1024 / RB;                     // rows per load instruction
+  static constexpr int NBLK = ROWS / RPL;                   // load instructions per stage
+  static constexpr int LPW = (NBLK + NW - 1) / NW;          // per wave, at most
+  static constexpr int FULL = NBLK - (LPW - 1) * NW;        // waves that issue LPW
+  static_assert(NBUF >= 2 && NBUF <= 4, "two to four stage buffers");
+  static_assert(RB == 128 || RB == 64, "64 or 128 K bytes per row and stage");
   static_assert(TM % 16 == 0 && TN % 16 == 0, "whole 16 x 16 MFMA blocks per wave");
-  static_assert(ROWS % (8 * NW) == 0, "whole load instructions per wave");
+  static_assert(ROWS % RPL == 0, "whole load instructions per stage");
 };
 using BigTile = Tile<256, 256, 4, 2>;      // 8 waves, 64 x 128 each; 128 KB LDS, 1 workgroup/CU
 using TallTile = Tile<320, 256, 4, 2>;     // 8 waves, 80 x 128 each; 144 KB LDS, 1 workgroup/CU
@@ -56,6 +66,15 @@ using MidTile = Tile<128, 256, 2, 4>;      // 8 waves, 64 x 64 each; 96 KB LDS, 
 // Decode-sized calls: a GEMM of at most 16 rows has few tiles, and each walks its K stages one
 // round trip at a time; narrow one-wave tiles with three stages in flight (40 KB LDS).
 using DecodeTile = Tile<16, 64, 1, 1, 4>;
+
+// Segment swizzle of tile row r (16-row blocks start at multiples of 16, so a lane's row
+// within its MFMA block decides it): 16-byte segment g of the row sits at g ^ swz(r). For
+// 128-byte rows that is r & 7, for 64-byte rows (r >> 2) & 3; either way any 8 consecutive
+// lanes reading one MFMA operand (8 rows, one segment) hit 8 different bank groups.
+template <class TL>
+__device__ __forceinline__ int swz(int r) {
+  return TL::RB == 128 ? (r & 7) : ((r >> 2) & 3);
+}
 
 // Wave rows: wave row-group wm owns the tile's 16-row blocks wm, wm + WM, wm + 2 WM, ...
 // (block i of the wave starts at tile row (i * WM + wm) * 16). Interleaving keeps the work of
@@ -79,10 +98,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 template <typename T> struct Frag;
 
-// bf16: a stage holds 2 MFMA steps of 32 K elements. Lane l supplies row (l & 15) and the 8
+// bf16: a 64-byte MFMA step holds 32 K elements. Lane l supplies row (l & 15) and the 8
 // consecutive K elements of 16-byte segment (4 * step + (l >> 4)), for A and B alike.
 template <> struct Frag<uint16_t> {
-  static constexpr int kSteps = 2;
+  static constexpr int kStepBytes = 64;
   typedef bf16x8_t V;
   static __device__ __forceinline__ V load(const char* row, int step, int kq, int sw) {
     return *reinterpret_cast<const V*>(row + (((step * 4 + kq) ^ sw) << 4));
@@ -92,10 +111,10 @@ template <> struct Frag<uint16_t> {
   }
 };
 
-// fp32: a stage holds 8 MFMA steps of 4 K elements; lane l supplies element (l >> 4) of the
+// fp32: a 16-byte MFMA step holds 4 K elements; lane l supplies element (l >> 4) of the
 // step, i.e. 4-byte word (l >> 4) of 16-byte segment `step`.
 template <> struct Frag<float> {
-  static constexpr int kSteps = 8;
+  static constexpr int kStepBytes = 16;
   typedef float V;
   static __device__ __forceinline__ V load(const char* row, int step, int kq, int sw) {
     return *reinterpret_cast<const V*>(row + (((step ^ sw) << 4) | (kq << 2)));
@@ -105,35 +124,44 @@ template <> struct Frag<float> {
   }
 };
 
-// Row this lane stages for load instruction q, and the segment of it that it loads (so that
-// after the swizzle the instruction's 1 KB block holds 8 whole rows).
+// Row this lane stages for load instruction q (block wave + NW q of the stage), and the
+// segment of it that it loads, so that after the swizzle the instruction's 1 KB holds RPL
+// whole rows. Rows past ROWS (q beyond this wave's share) are never loaded.
 template <class TL>
 __device__ __forceinline__ int stage_row(int q) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  return (wave * TL::LPW + q) * 8 + (lane >> 3);
+  return (wave + TL::NW * q) * TL::RPL + lane / TL::SPR;
 }
+template <class TL>
 __device__ __forceinline__ int stage_seg() {
   const int lane = threadIdx.x & 63;
-  return (lane & 7) ^ (lane >> 3);
+  return (lane % TL::SPR) ^ swz<TL>(lane / TL::SPR);
 }
 
-// Mainloop. src[q]: this lane's global source (row start + 16 * stage_seg()) for load
-// instruction q; stage s reads 128 bytes further per stage. kPairedGU: the B half holds BN/2
-// gate rows then the BN/2 matching up rows; wave column wn takes gate blocks wn*TN/2.. and the
-// up blocks of the same columns, so acc[i][j] and acc[i][j + FN/2] are gate and up of one
-// output element. rows: valid rows of the tile; a wave keeps loading its share of the stages
-// but skips the fragment reads and MFMAs of its blocks past `rows` (their outputs are never
-// stored).
+// K stages of a GEMM with K elements of type T.
+template <typename T, class TL>
+__host__ __device__ constexpr int stages(int K) {
+  return K / (TL::RB / static_cast<int>(sizeof(T)));
+}
+
+// Mainloop. src[q]: this lane's global source (row start + 16 * stage_seg<TL>()) for load
+// instruction q; stage s reads TL::RB bytes further per stage. kPairedGU: the B half holds
+// BN/2 gate rows then the BN/2 matching up rows; wave column wn takes gate blocks wn*TN/2..
+// and the up blocks of the same columns, so acc[i][j] and acc[i][j + FN/2] are gate and up of
+// one output element. rows: valid rows of the tile; a wave keeps loading its share of the
+// stages but skips the fragment reads and MFMAs of its blocks past `rows` (their outputs are
+// never stored).
 template <typename T, class TL, bool kPairedGU>
 __device__ __forceinline__ void mainloop(const char* const (&src)[TL::LPW], int nk, char* lds,
                                          f32x4_t (&acc)[TL::FM][TL::FN], int rows) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / TL::WN, wn = wave % TL::WN, kq = lane >> 4, l16 = lane & 15;
   const int nbusy = busy_blocks<TL>(rows, wm);
-  const int sw = l16 & 7;
+  const int sw = swz<TL>(l16);
+  constexpr int kSteps = TL::RB / Frag<T>::kStepBytes;     // MFMA K steps per stage
   int arow[TL::FM], brow[TL::FN];
 #pragma unroll
-  for (int i = 0; i < TL::FM; ++i) arow[i] = (block_row<TL>(i, wm) + l16) * kRowBytes;
+  for (int i = 0; i < TL::FM; ++i) arow[i] = (block_row<TL>(i, wm) + l16) * TL::RB;
 #pragma unroll
   for (int j = 0; j < TL::FN; ++j) {
     int b;
@@ -143,48 +171,58 @@ __device__ __forceinline__ void mainloop(const char* const (&src)[TL::LPW], int 
     } else {
       b = wn * TL::TN + j * 16;
     }
-    brow[j] = (TL::BM + b + l16) * kRowBytes;
+    brow[j] = (TL::BM + b + l16) * TL::RB;
   }
 #pragma unroll
   for (int i = 0; i < TL::FM; ++i)
 #pragma unroll
     for (int j = 0; j < TL::FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // The stage loads are issued as inline asm (M0 = this wave's LDS block, one 1 KB
-  // global_load_lds_dwordx4 per instruction) so the compiler does not track them: the only
-  // wait they need is the explicit vmcnt(0) before each stage's barrier, and with them out
-  // of its bookkeeping the compiler waits on each fragment read separately (lgkmcnt(N))
-  // instead of on all of them (lgkmcnt(0)) -- 5-9% faster mainloops, same instructions.
+  // The stage loads are issued as inline asm (M0 = the instruction's 1 KB LDS block, one
+  // global_load_lds_dwordx4 each) so the compiler does not track them: the only waits they
+  // need are the explicit vmcnt waits before each stage's barrier, and with them out of its
+  // bookkeeping the compiler waits on each fragment read separately (lgkmcnt(N)) instead of
+  // on all of them (lgkmcnt(0)) -- 5-9% faster mainloops, same instructions.
   typedef __attribute__((address_space(3))) char lds_char;
+  const int uwave = __builtin_amdgcn_readfirstlane(wave);
+  const bool full = TL::FULL == TL::NW || uwave < TL::FULL;   // issues LPW loads, else LPW - 1
   const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(
-      static_cast<uint32_t>((uintptr_t)(lds_char*)lds) + static_cast<uint32_t>(wave * TL::LPW * 1024));
+      static_cast<uint32_t>((uintptr_t)(lds_char*)lds) + static_cast<uint32_t>(uwave * 1024));
   // M0 is a reserved register to the compiler (hence the silenced warning); no other code in
   // these kernels uses it, which tests/test_isa_guard.py checks on the compiled ISA.
   auto issue = [&](int s) {
     const uint32_t dst = wave_lds + static_cast<uint32_t>((s % TL::NBUF) * TL::STAGE);
 #pragma unroll
     for (int q = 0; q < TL::LPW; ++q) {
+      if (q < TL::LPW - 1 || full) {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
-      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-                   :
-                   : "s"(dst + static_cast<uint32_t>(q * 1024)), "v"(src[q] + s * kRowBytes)
-                   : "memory", "m0");
+        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                     :
+                     : "s"(dst + static_cast<uint32_t>(q * TL::NW * 1024)), "v"(src[q] + s * TL::RB)
+                     : "memory", "m0");
 #pragma clang diagnostic pop
+      }
     }
   };
   // Two copies of the stage loop: every block valid (straight-line fragment reads, then the
   // MFMAs), or a partly valid wave that skips the blocks past `rows` (uniform branches).
   // With NBUF buffers, stages s + 1 .. s + NBUF - 2 stay in flight while stage s is waited
-  // for (a wave's loads complete in issue order, so vmcnt(ahead * LPW) is enough).
+  // for (a wave's loads complete in issue order, so vmcnt(ahead x its loads per stage) is
+  // enough).
+  auto wait_ahead = [&](auto per_stage, int ahead) {
+    constexpr int L = decltype(per_stage)::value;
+    if (ahead >= 2) wait_vmcnt<2 * L>();
+    else if (ahead == 1) wait_vmcnt<L>();
+    else wait_vmcnt<0>();
+  };
   auto wait_stage = [&](int s) {
     if constexpr (TL::NBUF == 2) {
       wait_vmcnt<0>();
     } else {
       const int ahead = min(TL::NBUF - 2, nk - 1 - s);
-      if (ahead >= 2) wait_vmcnt<2 * TL::LPW>();
-      else if (ahead == 1) wait_vmcnt<TL::LPW>();
-      else wait_vmcnt<0>();
+      if (full) wait_ahead(std::integral_constant<int, TL::LPW>{}, ahead);
+      else wait_ahead(std::integral_constant<int, TL::LPW - 1>{}, ahead);
     }
   };
   auto run = [&](auto guarded) {
@@ -196,7 +234,7 @@ __device__ __forceinline__ void mainloop(const char* const (&src)[TL::LPW], int 
       const char* buf = lds + (s % TL::NBUF) * TL::STAGE;
       if constexpr (!decltype(guarded)::value) {
 #pragma unroll
-        for (int ks = 0; ks < Frag<T>::kSteps; ++ks) {
+        for (int ks = 0; ks < kSteps; ++ks) {
           typename Frag<T>::V a[TL::FM], b[TL::FN];
 #pragma unroll
           for (int i = 0; i < TL::FM; ++i) a[i] = Frag<T>::load(buf + arow[i], ks, kq, sw);
@@ -209,7 +247,7 @@ __device__ __forceinline__ void mainloop(const char* const (&src)[TL::LPW], int 
         }
       } else if (nbusy > 0) {
 #pragma unroll
-        for (int ks = 0; ks < Frag<T>::kSteps; ++ks) {
+        for (int ks = 0; ks < kSteps; ++ks) {
           typename Frag<T>::V b[TL::FN];
 #pragma unroll
           for (int j = 0; j < TL::FN; ++j) b[j] = Frag<T>::load(buf + brow[j], ks, kq, sw);
@@ -383,11 +421,11 @@ void gu_kernel(GuParams p) {
       const int wrow = (hc < p.I ? hc : n0h) + (br < HC ? 0 : p.I);
       base = (missing ? static_cast<const char*>(p.x) : wbase) + static_cast<int64_t>(wrow) * rowb;
     }
-    src[q] = base + 16 * stage_seg();
+    src[q] = base + 16 * stage_seg<TL>();
   }
   f32x4_t acc[TL::FM][TL::FN];
   if (!missing)
-    mainloop<T, TL, true>(src, p.d / (kRowBytes / static_cast<int>(sizeof(T))), lds, acc, rows);
+    mainloop<T, TL, true>(src, stages<T, TL>(p.d), lds, acc, rows);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / TL::WN, wn = wave % TL::WN;
@@ -567,11 +605,11 @@ void down_kernel(DownParams p) {
       base = missing ? static_cast<const char*>(p.h)
                      : wbase + static_cast<int64_t>(wr < p.d ? wr : n0) * rowb;
     }
-    src[q] = base + 16 * stage_seg();
+    src[q] = base + 16 * stage_seg<TL>();
   }
   f32x4_t acc[TL::FM][TL::FN];
   if (!missing)
-    mainloop<T, TL, false>(src, p.K / (kRowBytes / static_cast<int>(sizeof(T))), lds, acc, rows);
+    mainloop<T, TL, false>(src, stages<T, TL>(p.K), lds, acc, rows);
 
   const int wave = threadIdx.x >> 6;
   const int wm = wave / TL::WN, wn = wave % TL::WN;
@@ -636,10 +674,10 @@ void router_kernel(RouterParams p) {
       const int wr = n0 + r - TL::BM;
       base = static_cast<const char*>(p.w) + static_cast<int64_t>(wr < p.E ? wr : n0) * rowb;
     }
-    src[q] = base + 16 * stage_seg();
+    src[q] = base + 16 * stage_seg<TL>();
   }
   f32x4_t acc[TL::FM][TL::FN];
-  mainloop<T, TL, false>(src, p.d / (kRowBytes / static_cast<int>(sizeof(T))), lds, acc, rows);
+  mainloop<T, TL, false>(src, stages<T, TL>(p.d), lds, acc, rows);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / TL::WN, wn = wave % TL::WN;

@@ -237,17 +237,18 @@ def test_workspace_too_small_leaves_output(moe):
 
 
 def test_router_logits_independent_of_tile_shape(moe):
-    """The router GEMM picks its tile (64 or 128 rows) from T; a token's logits, and so its
-    routing, are the same bytes either way."""
-    wl = mi.custom_workload("rtile", T=12288, d=256, E=512, k=8, inter=64, inter_shared=0,
+    """The router GEMM picks its tile (16, 64, 128 or 256 rows) from T; a token's logits, and
+    so its routing, are the same bytes whichever tile computed them."""
+    wl = mi.custom_workload("rtile", T=49152, d=256, E=512, k=8, inter=64, inter_shared=0,
                             seed=23)
     params, L = place(wl)
     x = mi.make_x(wl, device="cuda")
-    big = moe.moe_prefill_route(L, x, 12288)      # 96 x 2 = 192 tiles of 128 rows
-    small = moe.moe_prefill_route(L, x[:700].contiguous(), 700)   # 64-row tiles
-    torch.cuda.synchronize()
-    for key in ("logits", "ids", "weights"):
-        assert torch.equal(bits(big[key][:700]), bits(small[key])), key
+    ref = moe.moe_prefill_route(L, x, 49152)      # 192 x 2 = 384 tiles of 256 rows
+    for T in (12288, 700, 9):                     # 128-row, 64-row and 16-row tiles
+        got = moe.moe_prefill_route(L, x[:T].contiguous(), T)
+        torch.cuda.synchronize()
+        for key in ("logits", "ids", "weights"):
+            assert torch.equal(bits(ref[key][:T]), bits(got[key])), (T, key)
 
 
 def test_layer_3001(moe):
@@ -272,6 +273,21 @@ def test_row_path_equals_batched(moe):
     torch.cuda.synchronize()
     for t in rows:
         assert torch.equal(bits(out[t]), bits(base["out"][t])), t
+
+
+def test_decode_sized_call_equals_batched(moe):
+    """A call of a few tokens runs every GEMM on the 16-row decode tiles; each token gets the
+    bytes the batched pass gives it, routing included."""
+    wl = mi.WORKLOADS["layer_3001"]
+    params, L = place(wl)
+    x = mi.make_x(wl, device="cuda")
+    base = _run(moe, L, x, wl.T)
+    for t0, n in ((0, 1), (5, 8), (2990, 11)):
+        xs = x[t0:t0 + n].contiguous()
+        got = _run(moe, L, xs, n)
+        torch.cuda.synchronize()
+        assert torch.equal(got["ids"], base["ids"][t0:t0 + n]), (t0, n)
+        assert torch.equal(bits(got["out"]), bits(base["out"][t0:t0 + n])), (t0, n)
 
 
 def test_chunk_gate_4099(moe):

@@ -150,8 +150,9 @@ __host__ __device__ constexpr int stages(int K) {
 // and the up blocks of the same columns, so acc[i][j] and acc[i][j + FN/2] are gate and up of
 // one output element. rows: valid rows of the tile; a wave keeps loading its share of the
 // stages but skips the fragment reads and MFMAs of its blocks past `rows` (their outputs are
-// never stored).
-template <typename T, class TL, bool kPairedGU>
+// never stored). kSpread: the next stage's loads go out between the MFMA rows of the first K
+// step instead of all at once after the barrier.
+template <typename T, class TL, bool kPairedGU, bool kSpread = false>
 __device__ __forceinline__ void mainloop(const char* const (&src)[TL::LPW], int nk, char* lds,
                                          f32x4_t (&acc)[TL::FM][TL::FN], int rows) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -188,22 +189,38 @@ __device__ __forceinline__ void mainloop(const char* const (&src)[TL::LPW], int 
   const bool full = TL::FULL == TL::NW || uwave < TL::FULL;   // issues LPW loads, else LPW - 1
   const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(
       static_cast<uint32_t>((uintptr_t)(lds_char*)lds) + static_cast<uint32_t>(uwave * 1024));
+  // Spread issue: after MFMA row i < FM - 1 of the first K step comes slot i with its share of
+  // the next stage's LPW load instructions, so a wave does not sit on a full load queue with its
+  // MFMAs waiting behind. That pays where the operands are mostly cache hits (the dense shared
+  // GU: 236 against 261 us at T = 16,022); the routed GEMMs, whose gathered rows and weights
+  // come from HBM, need every cycle of lead time and issue at once after the barrier.
+  constexpr int kSlots = TL::FM - 1;
+  constexpr bool kSpreadOn = kSpread && kSlots > 0;
   // M0 is a reserved register to the compiler (hence the silenced warning); no other code in
   // these kernels uses it, which tests/test_isa_guard.py checks on the compiled ISA.
-  auto issue = [&](int s) {
+  // issue(s, qlo, qhi): this wave's load instructions qlo .. qhi - 1 of stage s (issued from
+  // inside the MFMA rows with a scheduling fence on either side, so they stay where they are)
+  auto issue = [&](int s, int qlo, int qhi) {
     const uint32_t dst = wave_lds + static_cast<uint32_t>((s % TL::NBUF) * TL::STAGE);
+    if constexpr (kSpreadOn) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int q = 0; q < TL::LPW; ++q) {
-      if (q < TL::LPW - 1 || full) {
+      if (q >= qlo && q < qhi && (q < TL::LPW - 1 || full)) {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
         asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
                      :
-                     : "s"(dst + static_cast<uint32_t>(q * TL::NW * 1024)), "v"(src[q] + s * TL::RB)
+                     : "s"(__builtin_amdgcn_readfirstlane(dst + static_cast<uint32_t>(q * TL::NW * 1024))),
+                       "v"(src[q] + s * TL::RB)
                      : "memory", "m0");
 #pragma clang diagnostic pop
       }
     }
+    if constexpr (kSpreadOn) __builtin_amdgcn_sched_barrier(0);
+  };
+  auto issue_slot = [&](int s, int m) {
+    if constexpr (kSpreadOn)
+      issue(s, (m * TL::LPW + kSlots - 1) / kSlots, ((m + 1) * TL::LPW + kSlots - 1) / kSlots);
   };
   // Two copies of the stage loop: every block valid (straight-line fragment reads, then the
   // MFMAs), or a partly valid wave that skips the blocks past `rows` (uniform branches).
@@ -226,11 +243,13 @@ __device__ __forceinline__ void mainloop(const char* const (&src)[TL::LPW], int 
     }
   };
   auto run = [&](auto guarded) {
-    for (int s = 0; s < TL::NBUF - 1 && s < nk; ++s) issue(s);
+    for (int s = 0; s < TL::NBUF - 1 && s < nk; ++s) issue(s, 0, TL::LPW);
     for (int s = 0; s < nk; ++s) {
       wait_stage(s);              // this wave's share of stage s has landed ...
       __syncthreads();            // ... and everyone's; everyone also left stage s - 1
-      if (s + TL::NBUF - 1 < nk) issue(s + TL::NBUF - 1);
+      const int sn = s + TL::NBUF - 1;           // stage whose loads go out now
+      const bool pre = sn < nk;
+      if (!kSpreadOn && pre) issue(sn, 0, TL::LPW);
       const char* buf = lds + (s % TL::NBUF) * TL::STAGE;
       if constexpr (!decltype(guarded)::value) {
 #pragma unroll
@@ -241,9 +260,11 @@ __device__ __forceinline__ void mainloop(const char* const (&src)[TL::LPW], int 
 #pragma unroll
           for (int j = 0; j < TL::FN; ++j) b[j] = Frag<T>::load(buf + brow[j], ks, kq, sw);
 #pragma unroll
-          for (int i = 0; i < TL::FM; ++i)
+          for (int i = 0; i < TL::FM; ++i) {
 #pragma unroll
             for (int j = 0; j < TL::FN; ++j) acc[i][j] = Frag<T>::mma(a[i], b[j], acc[i][j]);
+            if (ks == 0 && i < TL::FM - 1 && pre) issue_slot(sn, i);
+          }
         }
       } else if (nbusy > 0) {
 #pragma unroll
@@ -258,8 +279,11 @@ __device__ __forceinline__ void mainloop(const char* const (&src)[TL::LPW], int 
 #pragma unroll
               for (int j = 0; j < TL::FN; ++j) acc[i][j] = Frag<T>::mma(a, b[j], acc[i][j]);
             }
+            if (ks == 0 && i < TL::FM - 1 && pre) issue_slot(sn, i);
           }
         }
+      } else if (pre && kSpreadOn) {
+        issue(sn, 0, TL::LPW);                  // no rows of this wave: all loads at once
       }
     }
   };
@@ -425,7 +449,7 @@ void gu_kernel(GuParams p) {
   }
   f32x4_t acc[TL::FM][TL::FN];
   if (!missing)
-    mainloop<T, TL, true>(src, stages<T, TL>(p.d), lds, acc, rows);
+    mainloop<T, TL, true, !kGrouped>(src, stages<T, TL>(p.d), lds, acc, rows);
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave / TL::WN, wn = wave % TL::WN;

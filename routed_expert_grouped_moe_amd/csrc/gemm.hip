@@ -62,7 +62,7 @@ struct Tile {
 using BigTile = Tile<256, 256, 4, 2>;      // 8 waves, 64 x 128 each; 128 KB LDS, 1 workgroup/CU
 using TallTile = Tile<320, 256, 4, 2>;     // 8 waves, 80 x 128 each; 144 KB LDS, 1 workgroup/CU
 using SmallTile = Tile<64, 256, 1, 4>;     // 4 waves, 64 x 64 each; 80 KB LDS, 2 workgroups/CU
-using MidTile = Tile<128, 256, 2, 4>;      // 8 waves, 64 x 64 each; 96 KB LDS, 1 workgroup/CU
+using MidTile = Tile<128, 256, 2, 4, 3>;   // 8 waves, 64 x 64 each; 3 stage buffers, 144 KB LDS, 1 workgroup/CU
 // Decode-sized calls: a GEMM of at most 16 rows has few tiles, and each walks its K stages one
 // round trip at a time; narrow one-wave tiles with three stages in flight (40 KB LDS).
 using DecodeTile = Tile<16, 64, 1, 1, 4>;

@@ -4,12 +4,12 @@
 //
 // Every GEMM here is X W^T with both operands K-contiguous (token rows and weight rows). A
 // workgroup computes a BM x BN tile; K advances 128 bytes per row and stage (64 bf16 or 32
-// fp32 elements) through two LDS stages (four in the decode tile) filled by direct
-// global->LDS loads (global_load_lds_dwordx4: each lane's 16 bytes land at the instruction's
-// LDS base plus 16 x lane, so one instruction fills 8 rows of 128 bytes; the stage's
-// instructions go round-robin over the waves, so every wave loads a share of both operands;
-// the A rows of a routed tile are gathered from the prompt by pointer, no permuted copy of x
-// exists). Inside LDS, 16-byte segment g of row r sits at segment g ^ (r & 7), so any 8
+// fp32 elements) through two LDS stages (three in the router's tile, four in the decode tile)
+// filled by direct global->LDS loads (global_load_lds_dwordx4: each lane's 16 bytes land at
+// the instruction's LDS base plus 16 x lane, so one instruction fills 8 rows of 128 bytes; the
+// stage's instructions go round-robin over the waves, so every wave loads a share of both
+// operands; the A rows of a routed tile are gathered from the prompt by pointer, no permuted
+// copy of x exists). The A stage buffers sit together in LDS, followed by the B ones. Inside LDS, 16-byte segment g of row r sits at segment g ^ (r & 7), so any 8
 // consecutive lanes reading one MFMA operand (8 rows, same K segment) hit 8 different bank
 // groups. A wave row-group owns every WM-th 16-row block of the tile and accumulates
 // 16 x 16 MFMA blocks: v_mfma_f32_16x16x32_bf16 (bf16) or v_mfma_f32_16x16x4_f32 (fp32),
@@ -36,8 +36,9 @@ namespace {
 
 // RB_: K bytes per row and stage, 128 (64 bf16 / 32 fp32 elements) or 64. A 1 KB load
 // instruction fills RPL = 1024 / RB rows, and the stage's NBLK instructions go round-robin
-// over the waves (block b to wave b % NW): with NBLK not a multiple of NW the first FULL
-// waves issue LPW of them and the rest LPW - 1.
+// over the waves (block b to wave b % NW): the A blocks come first and every wave issues QA of
+// them, then the B blocks (with NBLK not a multiple of NW the first FULL waves issue one more).
+// LDS holds the NBUF stage buffers of the A rows, then the NBUF stage buffers of the B rows.
 template <int BM_, int BN_, int WM_, int WN_, int NBUF_ = 2, int RB_ = 128>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
@@ -47,17 +48,21 @@ struct Tile {
   static constexpr int TM = BM / WM, TN = BN / WN;          // wave tile
   static constexpr int FM = TM / 16, FN = TN / 16;          // 16 x 16 MFMA blocks per wave
   static constexpr int ROWS = BM + BN;
-  static constexpr int STAGE = ROWS * RB;
-  static constexpr int LDS = NBUF * STAGE;
+  static constexpr int A_STAGE = BM * RB, B_STAGE = BN * RB;
+  static constexpr int B_OFF = NBUF * A_STAGE;              // first B stage buffer
+  static constexpr int LDS = NBUF * (A_STAGE + B_STAGE);
   static constexpr int SPR = RB / 16;                       // 16-byte segments per row
   static constexpr int RPL = 1024 / RB;                     // rows per load instruction
   static constexpr int NBLK = ROWS / RPL;                   // load instructions per stage
+  static constexpr int QA = BM / RPL / NW;                  // A load instructions per wave
   static constexpr int LPW = (NBLK + NW - 1) / NW;          // per wave, at most
   static constexpr int FULL = NBLK - (LPW - 1) * NW;        // waves that issue LPW
   static_assert(NBUF >= 2 && NBUF <= 4, "two to four stage buffers");
   static_assert(RB == 128 || RB == 64, "64 or 128 K bytes per row and stage");
   static_assert(TM % 16 == 0 && TN % 16 == 0, "whole 16 x 16 MFMA blocks per wave");
   static_assert(ROWS % RPL == 0, "whole load instructions per stage");
+  static_assert((BM / RPL) % NW == 0 && QA < LPW, "every wave loads whole A blocks and some B");
+  static_assert(LDS <= 160 * 1024, "LDS of one CU");
 };
 using BigTile = Tile<256, 256, 4, 2>;      // 8 waves, 64 x 128 each; 128 KB LDS, 1 workgroup/CU
 using TallTile = Tile<320, 256, 4, 2>;     // 8 waves, 80 x 128 each; 144 KB LDS, 1 workgroup/CU
@@ -172,7 +177,7 @@ __device__ __forceinline__ void mainloop(const char* const (&src)[TL::LPW], int 
     } else {
       b = wn * TL::TN + j * 16;
     }
-    brow[j] = (TL::BM + b + l16) * TL::RB;
+    brow[j] = (b + l16) * TL::RB;
   }
 #pragma unroll
   for (int i = 0; i < TL::FM; ++i)
@@ -198,24 +203,31 @@ __device__ __forceinline__ void mainloop(const char* const (&src)[TL::LPW], int 
   constexpr bool kSpreadOn = kSpread && kSlots > 0;
   // M0 is a reserved register to the compiler (hence the silenced warning); no other code in
   // these kernels uses it, which tests/test_isa_guard.py checks on the compiled ISA.
-  // issue(s, qlo, qhi): this wave's load instructions qlo .. qhi - 1 of stage s (issued from
-  // inside the MFMA rows with a scheduling fence on either side, so they stay where they are)
-  auto issue = [&](int s, int qlo, int qhi) {
-    const uint32_t dst = wave_lds + static_cast<uint32_t>((s % TL::NBUF) * TL::STAGE);
-    if constexpr (kSpreadOn) __builtin_amdgcn_sched_barrier(0);
+  auto issue_q = [&](uint32_t dst, int q, int s) {
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+    asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                 :
+                 : "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(src[q] + s * TL::RB)
+                 : "memory", "m0");
+#pragma clang diagnostic pop
+  };
+  auto issue_part = [&](int s, int qlo, int qhi) {
+    const uint32_t da = wave_lds + static_cast<uint32_t>((s % TL::NBUF) * TL::A_STAGE);
+    const uint32_t db = wave_lds + static_cast<uint32_t>(TL::B_OFF + (s % TL::NBUF) * TL::B_STAGE);
 #pragma unroll
     for (int q = 0; q < TL::LPW; ++q) {
       if (q >= qlo && q < qhi && (q < TL::LPW - 1 || full)) {
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-        asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
-                     :
-                     : "s"(__builtin_amdgcn_readfirstlane(dst + static_cast<uint32_t>(q * TL::NW * 1024))),
-                       "v"(src[q] + s * TL::RB)
-                     : "memory", "m0");
-#pragma clang diagnostic pop
+        if (q < TL::QA) issue_q(da + static_cast<uint32_t>(q * TL::NW * 1024), q, s);
+        else issue_q(db + static_cast<uint32_t>((q - TL::QA) * TL::NW * 1024), q, s);
       }
     }
+  };
+  // issue(s, qlo, qhi): this wave's load instructions qlo .. qhi - 1 of stage s (issued from
+  // inside the MFMA rows with a scheduling fence on either side, so they stay where they are)
+  auto issue = [&](int s, int qlo, int qhi) {
+    if constexpr (kSpreadOn) __builtin_amdgcn_sched_barrier(0);
+    issue_part(s, qlo, qhi);
     if constexpr (kSpreadOn) __builtin_amdgcn_sched_barrier(0);
   };
   auto issue_slot = [&](int s, int m) {
@@ -250,15 +262,16 @@ __device__ __forceinline__ void mainloop(const char* const (&src)[TL::LPW], int 
       const int sn = s + TL::NBUF - 1;           // stage whose loads go out now
       const bool pre = sn < nk;
       if (!kSpreadOn && pre) issue(sn, 0, TL::LPW);
-      const char* buf = lds + (s % TL::NBUF) * TL::STAGE;
+      const char* abuf = lds + (s % TL::NBUF) * TL::A_STAGE;
+      const char* bbuf = lds + TL::B_OFF + (s % TL::NBUF) * TL::B_STAGE;
       if constexpr (!decltype(guarded)::value) {
 #pragma unroll
         for (int ks = 0; ks < kSteps; ++ks) {
           typename Frag<T>::V a[TL::FM], b[TL::FN];
 #pragma unroll
-          for (int i = 0; i < TL::FM; ++i) a[i] = Frag<T>::load(buf + arow[i], ks, kq, sw);
+          for (int i = 0; i < TL::FM; ++i) a[i] = Frag<T>::load(abuf + arow[i], ks, kq, sw);
 #pragma unroll
-          for (int j = 0; j < TL::FN; ++j) b[j] = Frag<T>::load(buf + brow[j], ks, kq, sw);
+          for (int j = 0; j < TL::FN; ++j) b[j] = Frag<T>::load(bbuf + brow[j], ks, kq, sw);
 #pragma unroll
           for (int i = 0; i < TL::FM; ++i) {
 #pragma unroll
@@ -271,11 +284,11 @@ __device__ __forceinline__ void mainloop(const char* const (&src)[TL::LPW], int 
         for (int ks = 0; ks < kSteps; ++ks) {
           typename Frag<T>::V b[TL::FN];
 #pragma unroll
-          for (int j = 0; j < TL::FN; ++j) b[j] = Frag<T>::load(buf + brow[j], ks, kq, sw);
+          for (int j = 0; j < TL::FN; ++j) b[j] = Frag<T>::load(bbuf + brow[j], ks, kq, sw);
 #pragma unroll
           for (int i = 0; i < TL::FM; ++i) {
             if (i < nbusy) {
-              const typename Frag<T>::V a = Frag<T>::load(buf + arow[i], ks, kq, sw);
+              const typename Frag<T>::V a = Frag<T>::load(abuf + arow[i], ks, kq, sw);
 #pragma unroll
               for (int j = 0; j < TL::FN; ++j) acc[i][j] = Frag<T>::mma(a, b[j], acc[i][j]);
             }

@@ -731,8 +731,10 @@ void router_kernel(RouterParams p) {
   clock.finish();
 }
 
-// Big tiles when they still give the chip about two workgroups per CU (384 of them: 1.5 per
-// CU), else small ones.
+// Dense GEMMs (router, shared expert): big tiles when they still give the chip about two
+// workgroups per CU (384 of them: 1.5 per CU), else 128-row tiles while they give 0.75 per CU
+// (at 2,048 or 4,096 rows a chunk, the 64-row tiles would re-read the shared weights 32 or 64
+// times), else small ones.
 inline bool use_big_dense(int64_t n, int64_t n_tiles_big) {
   return n >= BigTile::BM && ((n + BigTile::BM - 1) / BigTile::BM) * n_tiles_big >= 384;
 }
@@ -814,6 +816,12 @@ hipError_t launch_gu_dense(int dtype, const void* x, int64_t t0, int64_t n, int 
     const unsigned grid = xcd_grid((n + BigTile::BM - 1) / BigTile::BM * nt_big);
     if (dtype == MOE_BF16) gu_kernel<uint16_t, BigTile, false><<<grid, BigTile::NT, 0, s>>>(p);
     else gu_kernel<float, BigTile, false><<<grid, BigTile::NT, 0, s>>>(p);
+  } else if (const int64_t mt = (n + MidTile::BM - 1) / MidTile::BM *
+                                ((Is + MidTile::BN / 2 - 1) / (MidTile::BN / 2));
+             n >= MidTile::BM && mt >= 192) {
+    const unsigned grid = xcd_grid(mt);
+    if (dtype == MOE_BF16) gu_kernel<uint16_t, MidTile, false><<<grid, MidTile::NT, 0, s>>>(p);
+    else gu_kernel<float, MidTile, false><<<grid, MidTile::NT, 0, s>>>(p);
   } else {
     const unsigned grid = xcd_grid((n + SmallTile::BM - 1) / SmallTile::BM *
                                    ((Is + SmallTile::BN / 2 - 1) / (SmallTile::BN / 2)));
@@ -864,6 +872,12 @@ hipError_t launch_down_combine(int dtype, const void* h, int64_t n, int d, int I
     const unsigned grid = xcd_grid((n + BigTile::BM - 1) / BigTile::BM * nt_big);
     if (dtype == MOE_BF16) down_kernel<uint16_t, BigTile, false><<<grid, BigTile::NT, 0, s>>>(p);
     else down_kernel<float, BigTile, false><<<grid, BigTile::NT, 0, s>>>(p);
+  } else if (const int64_t mt = (n + MidTile::BM - 1) / MidTile::BM *
+                                ((d + MidTile::BN - 1) / MidTile::BN);
+             n >= MidTile::BM && mt >= 192) {
+    const unsigned grid = xcd_grid(mt);
+    if (dtype == MOE_BF16) down_kernel<uint16_t, MidTile, false><<<grid, MidTile::NT, 0, s>>>(p);
+    else down_kernel<float, MidTile, false><<<grid, MidTile::NT, 0, s>>>(p);
   } else {
     const unsigned grid = xcd_grid((n + SmallTile::BM - 1) / SmallTile::BM *
                                    ((d + SmallTile::BN - 1) / SmallTile::BN));

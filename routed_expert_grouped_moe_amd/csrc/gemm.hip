@@ -16,9 +16,9 @@
 // fp32 accumulation.
 //
 // Five tile shapes: tall (320 x 256, 8 waves of 80 x 128) and big (256 x 256, 8 waves of
-// 64 x 128) for large row counts, small (64 x 256, 4 waves of 64 x 64) for few rows per
-// expert, mid (128 x 256, 8 waves of 64 x 64) for the router, and decode (16 x 64, one wave)
-// for calls of a few tokens. Which one runs never changes a bit: every output element is one
+// 64 x 128) for large row counts, small (64 x 256, 4 waves of 64 x 64; two or four stage
+// buffers) for few rows per expert or short dense GEMMs, mid (128 x 256, 8 waves of 64 x 64)
+// for mid-sized dense GEMMs, and decode (16 x 64, one wave) for calls of a few tokens. Which one runs never changes a bit: every output element is one
 // token row against one weight row, accumulated over K in the same stage order with the same
 // instruction and the same lane-to-K mapping in all of them. Together with no split-K, no
 // atomics and no shape-dependent arithmetic, that is what makes a token's bytes independent
@@ -67,6 +67,9 @@ struct Tile {
 using BigTile = Tile<256, 256, 4, 2>;      // 8 waves, 64 x 128 each; 128 KB LDS, 1 workgroup/CU
 using TallTile = Tile<320, 256, 4, 2>;     // 8 waves, 80 x 128 each; 144 KB LDS, 1 workgroup/CU
 using SmallTile = Tile<64, 256, 1, 4>;     // 4 waves, 64 x 64 each; 80 KB LDS, 2 workgroups/CU
+// Dense GEMMs with at most one small tile per CU: four stage buffers (three stages in
+// flight), 160 KB LDS, 1 workgroup/CU
+using SmallTile4 = Tile<64, 256, 1, 4, 4>;
 using MidTile = Tile<128, 256, 2, 4, 3>;   // 8 waves, 64 x 64 each; 3 stage buffers, 144 KB LDS, 1 workgroup/CU
 // Decode-sized calls: a GEMM of at most 16 rows has few tiles, and each walks its K stages one
 // round trip at a time; narrow one-wave tiles with three stages in flight (40 KB LDS).
@@ -731,10 +734,13 @@ void router_kernel(RouterParams p) {
   clock.finish();
 }
 
+constexpr int64_t kCus = 256;      // compute units of an MI355X
+
 // Dense GEMMs (router, shared expert): big tiles when they still give the chip about two
 // workgroups per CU (384 of them: 1.5 per CU), else 128-row tiles while they give 0.75 per CU
 // (at 2,048 or 4,096 rows a chunk, the 64-row tiles would re-read the shared weights 32 or 64
-// times), else small ones.
+// times), else small ones: with four stage buffers when there is at most one per CU, so the
+// few tiles keep three K stages in flight instead of one.
 inline bool use_big_dense(int64_t n, int64_t n_tiles_big) {
   return n >= BigTile::BM && ((n + BigTile::BM - 1) / BigTile::BM) * n_tiles_big >= 384;
 }
@@ -771,6 +777,11 @@ hipError_t launch_router_gemm(int dtype, const void* x, const void* w_router, co
     const unsigned grid = xcd_grid(mid_tiles);
     if (dtype == MOE_BF16) router_kernel<uint16_t, MidTile><<<grid, MidTile::NT, 0, s>>>(p);
     else router_kernel<float, MidTile><<<grid, MidTile::NT, 0, s>>>(p);
+  } else if (const int64_t st = (T + SmallTile::BM - 1) / SmallTile::BM * ((E + SmallTile::BN - 1) / SmallTile::BN);
+             st <= kCus) {
+    const unsigned grid = xcd_grid(st);
+    if (dtype == MOE_BF16) router_kernel<uint16_t, SmallTile4><<<grid, SmallTile4::NT, 0, s>>>(p);
+    else router_kernel<float, SmallTile4><<<grid, SmallTile4::NT, 0, s>>>(p);
   } else {
     const unsigned grid = xcd_grid((T + SmallTile::BM - 1) / SmallTile::BM * ((E + SmallTile::BN - 1) / SmallTile::BN));
     if (dtype == MOE_BF16) router_kernel<uint16_t, SmallTile><<<grid, SmallTile::NT, 0, s>>>(p);
@@ -822,6 +833,12 @@ hipError_t launch_gu_dense(int dtype, const void* x, int64_t t0, int64_t n, int 
     const unsigned grid = xcd_grid(mt);
     if (dtype == MOE_BF16) gu_kernel<uint16_t, MidTile, false><<<grid, MidTile::NT, 0, s>>>(p);
     else gu_kernel<float, MidTile, false><<<grid, MidTile::NT, 0, s>>>(p);
+  } else if (const int64_t st = (n + SmallTile::BM - 1) / SmallTile::BM *
+                                ((Is + SmallTile::BN / 2 - 1) / (SmallTile::BN / 2));
+             st <= kCus) {
+    const unsigned grid = xcd_grid(st);
+    if (dtype == MOE_BF16) gu_kernel<uint16_t, SmallTile4, false><<<grid, SmallTile4::NT, 0, s>>>(p);
+    else gu_kernel<float, SmallTile4, false><<<grid, SmallTile4::NT, 0, s>>>(p);
   } else {
     const unsigned grid = xcd_grid((n + SmallTile::BM - 1) / SmallTile::BM *
                                    ((Is + SmallTile::BN / 2 - 1) / (SmallTile::BN / 2)));
@@ -878,6 +895,12 @@ hipError_t launch_down_combine(int dtype, const void* h, int64_t n, int d, int I
     const unsigned grid = xcd_grid(mt);
     if (dtype == MOE_BF16) down_kernel<uint16_t, MidTile, false><<<grid, MidTile::NT, 0, s>>>(p);
     else down_kernel<float, MidTile, false><<<grid, MidTile::NT, 0, s>>>(p);
+  } else if (const int64_t st = (n + SmallTile::BM - 1) / SmallTile::BM *
+                                ((d + SmallTile::BN - 1) / SmallTile::BN);
+             st <= kCus) {
+    const unsigned grid = xcd_grid(st);
+    if (dtype == MOE_BF16) down_kernel<uint16_t, SmallTile4, false><<<grid, SmallTile4::NT, 0, s>>>(p);
+    else down_kernel<float, SmallTile4, false><<<grid, SmallTile4::NT, 0, s>>>(p);
   } else {
     const unsigned grid = xcd_grid((n + SmallTile::BM - 1) / SmallTile::BM *
                                    ((d + SmallTile::BN - 1) / SmallTile::BN));

@@ -171,15 +171,17 @@ def test_topk_ties_and_special_values(moe):
 
 def test_member_lists_bit_exact(moe):
     """The GPU's expert-major member lists equal the oracle's, integer for integer, for chunks
-    of one to eleven 256-token blocks."""
-    wl = mi.custom_workload("lists", T=3000, d=128, E=16, k=4, inter=64, inter_shared=64,
+    of one to twenty 256-token blocks (up to 8 blocks the scan runs inside the permute kernel,
+    above that in a kernel of its own)."""
+    wl = mi.custom_workload("lists", T=5000, d=128, E=16, k=4, inter=64, inter_shared=64,
                             zipf_s=1.5, seed=5)
     params, L = place(wl)
     x = mi.make_x(wl, device="cuda")
     sh = L.shape
     r = moe.moe_prefill_route(L, x, 300)
     out = torch.empty_like(x)
-    for t0, n in ((0, 300), (300, 300), (900, 100), (900, 2048), (400, 2600)):
+    for t0, n in ((0, 300), (300, 300), (900, 100), (900, 2048), (400, 2600), (0, 4096),
+                  (0, 5000)):
         ws = torch.empty(moe.moe_workspace_bytes(sh, n), dtype=torch.uint8, device="cuda")
         moe.moe_prefill_chunk(L, x, r["ids"], r["weights"], t0, n, out, ws)
         torch.cuda.synchronize()

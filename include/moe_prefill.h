@@ -150,6 +150,12 @@ moe_status moe_prefill_route(const moe_layer* layer, const void* x, int64_t T, i
  *                line's `ready` event marks its own copy, and the compute stream waits on those.
  * With a ring, the chunk's used offloaded experts are staged in waves that walk upward on
  * even calls of the ring and downward on odd ones; no result bit depends on that order.
+ * ids are expected as moe_prefill_route writes them (k distinct ids in [0, E) per token). A
+ * slot whose id is out of range, or repeats an id of the same token, is dropped by the
+ * bucketing (no access depends on it): with every expert resident the call completes, that
+ * token's output row is unspecified and every other token keeps its bytes; with a ring the
+ * chunk's counts then fall short of n*k and the call returns MOE_ERR_INVALID once they have
+ * been read back (the work already enqueued wrote only the workspace; out is unchanged).
  * The batched pass is t0 = 0, n = T. n == 0 enqueues nothing. */
 moe_status moe_prefill_chunk(const moe_layer* layer, const void* x, const int32_t* ids,
                              const float* weights, int64_t T, int64_t t0, int64_t n,

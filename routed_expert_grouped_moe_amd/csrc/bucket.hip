@@ -6,6 +6,12 @@
 //
 // Row order inside an expert is token order (a stable permute), so the member list of each
 // expert is unique and the whole bucketing is reproducible bit for bit.
+//
+// Slots whose id is outside [0, E), or repeats an expert already listed for the same token,
+// are dropped by every kernel here alike (a token's slots are taken in order, so the first
+// occurrence counts): counts, offsets and member lists then describe exactly the slots kept,
+// every member-list row is written, and no access depends on an unchecked id. Ids as
+// moe_prefill_route writes them are always kept.
 #include <algorithm>
 
 #include "device_common.h"
@@ -17,17 +23,42 @@ namespace {
 
 constexpr int kMaxE = 1024;
 
-// blk_counts[b][e] = slots of tokens [b*256, b*256+256) routed to e (LDS histogram).
+// Marks token `tid` of the block in expert e's 256-bit LDS mask; true if the slot is kept (e in
+// range and not yet marked for this token).
+__device__ __forceinline__ bool mark_slot(uint32_t* mask, int e, int E, int tid) {
+  if (static_cast<unsigned>(e) >= static_cast<unsigned>(E)) return false;
+  const uint32_t bit = 1u << (tid & 31);
+  return (atomicOr(&mask[e * (kTokBlock / 32) + (tid >> 5)], bit) & bit) == 0u;
+}
+
+// Whether slot j (expert e) of a token is kept: e in range and no earlier slot of the token
+// names e. Slots below 64 use the bits mark_slot returned; later ones (k > 64) are checked
+// against the token's earlier ids.
+__device__ __forceinline__ bool slot_kept(const int32_t* tok_ids, int j, int e, int E,
+                                          uint64_t kept) {
+  if (j < 64) return (kept >> j) & 1u;
+  if (static_cast<unsigned>(e) >= static_cast<unsigned>(E)) return false;
+  for (int i = 0; i < j; ++i)
+    if (tok_ids[i] == e) return false;
+  return true;
+}
+
+// blk_counts[b][e] = kept slots of tokens [b*256, b*256+256) routed to e (LDS histogram).
 __global__ __launch_bounds__(kTokBlock) void block_hist_kernel(const int32_t* __restrict__ ids,
                                                                int64_t n, int k, int E,
                                                                int32_t* __restrict__ blk_counts) {
   __shared__ int32_t hist[kMaxE];
+  __shared__ uint32_t mask[kMaxE * (kTokBlock / 32)];
   const int tid = threadIdx.x;
   for (int e = tid; e < E; e += kTokBlock) hist[e] = 0;
+  for (int w = tid; w < E * (kTokBlock / 32); w += kTokBlock) mask[w] = 0u;
   __syncthreads();
   const int64_t t = static_cast<int64_t>(blockIdx.x) * kTokBlock + tid;
   if (t < n)
-    for (int j = 0; j < k; ++j) atomicAdd(&hist[ids[t * k + j]], 1);
+    for (int j = 0; j < k; ++j) {
+      const int e = ids[t * k + j];
+      if (mark_slot(mask, e, E, tid)) atomicAdd(&hist[e], 1);
+    }
   __syncthreads();
   int32_t* out = blk_counts + static_cast<int64_t>(blockIdx.x) * E;
   for (int e = tid; e < E; e += kTokBlock) out[e] = hist[e];
@@ -106,13 +137,16 @@ __global__ __launch_bounds__(kTokBlock) void permute_kernel(const int32_t* __res
   const bool valid = t < n;
   const int word = tid >> 5;
   const uint32_t bit = 1u << (tid & 31);
+  uint64_t kept = 0;              // slots j < 64 kept (k > 64: later slots are re-checked)
   if (valid)
-    for (int j = 0; j < k; ++j) atomicOr(&mask[ids[t * k + j] * (kTokBlock / 32) + word], bit);
+    for (int j = 0; j < k; ++j)
+      if (mark_slot(mask, ids[t * k + j], E, tid) && j < 64) kept |= uint64_t{1} << j;
   __syncthreads();
   if (!valid) return;
   const int32_t* base = blk_base + static_cast<int64_t>(blockIdx.x) * E;
   for (int j = 0; j < k; ++j) {
     const int e = ids[t * k + j];
+    if (!slot_kept(ids + t * k, j, e, E, kept)) continue;
     const uint32_t* m = mask + e * (kTokBlock / 32);
     int rank = __popc(m[word] & (bit - 1u));
     for (int w = 0; w < word; ++w) rank += __popc(m[w]);
@@ -195,12 +229,15 @@ __global__ __launch_bounds__(kTokBlock) void permute_scan_kernel(
   const bool valid = t < n;
   const int word = tid >> 5;
   const uint32_t bit = 1u << (tid & 31);
+  uint64_t kept = 0;
   if (valid)
-    for (int j = 0; j < k; ++j) atomicOr(&mask[ids[t * k + j] * (kTokBlock / 32) + word], bit);
+    for (int j = 0; j < k; ++j)
+      if (mark_slot(mask, ids[t * k + j], E, tid) && j < 64) kept |= uint64_t{1} << j;
   __syncthreads();
   if (!valid) return;
   for (int j = 0; j < k; ++j) {
     const int e = ids[t * k + j];
+    if (!slot_kept(ids + t * k, j, e, E, kept)) continue;
     const uint32_t* m = mask + e * (kTokBlock / 32);
     int rank = __popc(m[word] & (bit - 1u));
     for (int w = 0; w < word; ++w) rank += __popc(m[w]);

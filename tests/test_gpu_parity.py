@@ -196,6 +196,47 @@ def test_member_lists_bit_exact(moe):
         assert np.array_equal(as_i32(off["row_slot"], n * sh.top_k), row_slot)
 
 
+def test_invalid_ids_are_dropped(moe):
+    """Caller-provided ids with a slot out of range or repeated within a token: the bucketing
+    drops those slots alike in every kernel, the resident call completes, and every other
+    token keeps the bytes it gets with valid ids, both when the scan runs inside the permute
+    kernel (3 token blocks) and in its own kernel (10 blocks). With a ring the counts fall short
+    of n*k and the call fails with MOE_ERR_INVALID, leaving out unchanged."""
+    wl = mi.custom_workload("badids", T=2500, d=128, E=16, k=4, inter=64, inter_shared=64,
+                            seed=27)
+    params, L = place(wl)
+    x = mi.make_x(wl, device="cuda")
+    sh = L.shape
+    r = moe.moe_prefill_route(L, x, wl.T)
+    bad = r["ids"].clone()
+    bad[5, 1] = sh.n_experts            # one past the last expert
+    bad[6, 2] = -3
+    bad[7, 3] = bad[7, 0]               # repeated expert
+    bad[300, 0] = 1 << 20
+    bad[2400, :] = bad[2400, 0]         # every slot the same expert
+    hit = [5, 6, 7, 300, 2400]
+    for n in (600, wl.T):
+        ws = torch.empty(moe.moe_workspace_bytes(sh, n), dtype=torch.uint8, device="cuda")
+        ref = torch.zeros_like(x)
+        moe.moe_prefill_chunk(L, x, r["ids"], r["weights"], 0, n, ref, ws)
+        got = torch.zeros_like(x)
+        moe.moe_prefill_chunk(L, x, bad, r["weights"], 0, n, got, ws)
+        torch.cuda.synchronize()
+        keep = torch.ones(wl.T, dtype=torch.bool, device="cuda")
+        keep[n:] = False
+        keep[hit] = False
+        assert torch.equal(bits(got[keep]), bits(ref[keep])), n
+    ring = moe.Ring(sh, 8)
+    _, Lr = place(wl, offloaded=range(sh.n_experts), ring=ring, params=params)
+    ws = torch.empty(moe.moe_workspace_bytes(sh, 600), dtype=torch.uint8, device="cuda")
+    out = torch.zeros_like(x)
+    with pytest.raises(moe.MoeError, match="MOE_ERR_INVALID"):
+        moe.moe_prefill_chunk(Lr, x, bad, r["weights"], 0, 600, out, ws)
+    torch.cuda.synchronize()
+    assert not out.any()
+    ring.close()
+
+
 def test_repeatable_five_runs(moe):
     wl = mi.custom_workload("rep", T=700, d=256, E=64, k=6, inter=128, inter_shared=256,
                             zipf_s=1.1, seed=9)

@@ -749,10 +749,14 @@ inline bool use_big_dense(int64_t n, int64_t n_tiles_big) {
 
 int routed_tile_rows(int64_t n, int k, int E) {
   // a = mean rows per expert. With a in [192, 320) many experts hold just over 256 rows; a
-  // 320-row tile keeps them in one tile instead of a full tile plus a nearly empty one.
+  // 320-row tile keeps them in one tile instead of a full tile plus a nearly empty one. With
+  // a in [48, 128), 128-row tiles do the same for experts just over 64 rows: an expert's
+  // second M-tile would stream its weight slice again (the MFMAs of empty row blocks are
+  // skipped either way).
   const int64_t rows = n * k, e = static_cast<int64_t>(E);
   if (rows < e * 16) return DecodeTile::BM;
   if (rows >= e * 192 && rows < e * 320) return TallTile::BM;
+  if (rows >= e * 48 && rows < e * 128) return MidTile::BM;
   return rows >= e * 128 ? BigTile::BM : SmallTile::BM;
 }
 
@@ -806,6 +810,7 @@ hipError_t launch_gu_routed(int dtype, const void* x, int64_t t0, int d, int I,
   p.row_tok = row_tok; p.h = h; p.clk = prof_clock(MOE_STAGE_GU_ROUTED);
   if (g.tile_rows == TallTile::BM) gu_routed<TallTile>(dtype, p, g, I, s);
   else if (g.tile_rows == BigTile::BM) gu_routed<BigTile>(dtype, p, g, I, s);
+  else if (g.tile_rows == MidTile::BM) gu_routed<MidTile>(dtype, p, g, I, s);
   else if (g.tile_rows == DecodeTile::BM) gu_routed<DecodeTile>(dtype, p, g, I, s);
   else gu_routed<SmallTile>(dtype, p, g, I, s);
   return hipGetLastError();
@@ -866,6 +871,7 @@ hipError_t launch_down_routed(int dtype, const void* h, int d, int I, const Gemm
   p.clk = prof_clock(MOE_STAGE_DOWN_ROUTED);
   if (g.tile_rows == TallTile::BM) down_routed<TallTile>(dtype, p, g, d, s);
   else if (g.tile_rows == BigTile::BM) down_routed<BigTile>(dtype, p, g, d, s);
+  else if (g.tile_rows == MidTile::BM) down_routed<MidTile>(dtype, p, g, d, s);
   else if (g.tile_rows == DecodeTile::BM) down_routed<DecodeTile>(dtype, p, g, d, s);
   else down_routed<SmallTile>(dtype, p, g, d, s);
   return hipGetLastError();

@@ -186,12 +186,19 @@ except moe.MoeError as e:
 
 def test_offload_16022_ring64(moe):
     """T = 16,022, every expert in a pinned bank, 64-line ring, chunk 2,048 (as specified):
-    bit-identical to the all-resident batched pass, and sampled rows match the oracle."""
+    bit-identical to the all-resident batched pass, and sampled rows match the oracle. The
+    resident layer at chunks 512, 4,096 and 8,192 (16-, 128- and 256-row expert tiles against
+    the batched pass's 320-row ones, at the full shape) gives the batched bytes too."""
     wl = mi.WORKLOADS["offload_16022"]
     print(f"[ring] {wl.name}: T={wl.T} E={wl.shape.n_experts} lines={wl.ring_lines}", flush=True)
     params, L_res = place(wl)
     x = mi.make_x(wl, device="cuda")
     ref = moe.moe_prefill_layer(L_res, x, wl.T)
+    for c in (512, 4096, 8192):
+        got_c = moe.moe_prefill_layer(L_res, x, c)
+        torch.cuda.synchronize()
+        assert torch.equal(bits(got_c["out"]), bits(ref["out"])), c
+        del got_c
     ring = moe.Ring(L_res.shape, wl.ring_lines)
     _, L = place(wl, offloaded=range(wl.shape.n_experts), ring=ring, params=params)
     got = moe.moe_prefill_layer(L, x, 2048, copy_stream=torch.cuda.Stream())

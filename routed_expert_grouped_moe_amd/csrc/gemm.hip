@@ -70,6 +70,8 @@ using SmallTile = Tile<64, 256, 1, 4>;     // 4 waves, 64 x 64 each; 80 KB LDS, 
 // Dense GEMMs with at most one small tile per CU: four stage buffers (three stages in
 // flight), 160 KB LDS, 1 workgroup/CU
 using SmallTile4 = Tile<64, 256, 1, 4, 4>;
+// ... and at most half a tile per CU: half as wide (4 waves of 64 x 32), twice the tiles, 96 KB
+using NarrowTile4 = Tile<64, 128, 1, 4, 4>;
 using MidTile = Tile<128, 256, 2, 4, 3>;   // 8 waves, 64 x 64 each; 3 stage buffers, 144 KB LDS, 1 workgroup/CU
 // Decode-sized calls: a GEMM of at most 16 rows has few tiles, and each walks its K stages one
 // round trip at a time; narrow one-wave tiles with three stages in flight (40 KB LDS).
@@ -740,7 +742,9 @@ constexpr int64_t kCus = 256;      // compute units of an MI355X
 // workgroups per CU (384 of them: 1.5 per CU), else 128-row tiles while they give 0.75 per CU
 // (at 2,048 or 4,096 rows a chunk, the 64-row tiles would re-read the shared weights 32 or 64
 // times), else small ones: with four stage buffers when there is at most one per CU, so the
-// few tiles keep three K stages in flight instead of one.
+// few tiles keep three K stages in flight instead of one, and half as wide when there would be
+// at most half a tile per CU (twice the tiles; in the shared down each then combines half the
+// columns).
 inline bool use_big_dense(int64_t n, int64_t n_tiles_big) {
   return n >= BigTile::BM && ((n + BigTile::BM - 1) / BigTile::BM) * n_tiles_big >= 384;
 }
@@ -840,6 +844,13 @@ hipError_t launch_gu_dense(int dtype, const void* x, int64_t t0, int64_t n, int 
     else gu_kernel<float, MidTile, false><<<grid, MidTile::NT, 0, s>>>(p);
   } else if (const int64_t st = (n + SmallTile::BM - 1) / SmallTile::BM *
                                 ((Is + SmallTile::BN / 2 - 1) / (SmallTile::BN / 2));
+             st <= kCus / 2) {
+    const unsigned grid = xcd_grid((n + NarrowTile4::BM - 1) / NarrowTile4::BM *
+                                   ((Is + NarrowTile4::BN / 2 - 1) / (NarrowTile4::BN / 2)));
+    if (dtype == MOE_BF16) gu_kernel<uint16_t, NarrowTile4, false><<<grid, NarrowTile4::NT, 0, s>>>(p);
+    else gu_kernel<float, NarrowTile4, false><<<grid, NarrowTile4::NT, 0, s>>>(p);
+  } else if (const int64_t st = (n + SmallTile::BM - 1) / SmallTile::BM *
+                                ((Is + SmallTile::BN / 2 - 1) / (SmallTile::BN / 2));
              st <= kCus) {
     const unsigned grid = xcd_grid(st);
     if (dtype == MOE_BF16) gu_kernel<uint16_t, SmallTile4, false><<<grid, SmallTile4::NT, 0, s>>>(p);
@@ -901,6 +912,13 @@ hipError_t launch_down_combine(int dtype, const void* h, int64_t n, int d, int I
     const unsigned grid = xcd_grid(mt);
     if (dtype == MOE_BF16) down_kernel<uint16_t, MidTile, false><<<grid, MidTile::NT, 0, s>>>(p);
     else down_kernel<float, MidTile, false><<<grid, MidTile::NT, 0, s>>>(p);
+  } else if (const int64_t st = (n + SmallTile::BM - 1) / SmallTile::BM *
+                                ((d + SmallTile::BN - 1) / SmallTile::BN);
+             st <= kCus / 2) {
+    const unsigned grid = xcd_grid((n + NarrowTile4::BM - 1) / NarrowTile4::BM *
+                                   ((d + NarrowTile4::BN - 1) / NarrowTile4::BN));
+    if (dtype == MOE_BF16) down_kernel<uint16_t, NarrowTile4, false><<<grid, NarrowTile4::NT, 0, s>>>(p);
+    else down_kernel<float, NarrowTile4, false><<<grid, NarrowTile4::NT, 0, s>>>(p);
   } else if (const int64_t st = (n + SmallTile::BM - 1) / SmallTile::BM *
                                 ((d + SmallTile::BN - 1) / SmallTile::BN);
              st <= kCus) {

@@ -15,10 +15,11 @@
 // 16 x 16 MFMA blocks: v_mfma_f32_16x16x32_bf16 (bf16) or v_mfma_f32_16x16x4_f32 (fp32),
 // fp32 accumulation.
 //
-// Five tile shapes: tall (320 x 256, 8 waves of 80 x 128) and big (256 x 256, 8 waves of
-// 64 x 128) for large row counts, small (64 x 256, 4 waves of 64 x 64; two or four stage
-// buffers) for few rows per expert or short dense GEMMs, mid (128 x 256, 8 waves of 64 x 64)
-// for mid-sized dense GEMMs, and decode (16 x 64, one wave) for calls of a few tokens. Which one runs never changes a bit: every output element is one
+// Tile shapes: tall (320 x 256, 8 waves of 80 x 128) and big (256 x 256, 8 waves of 64 x 128)
+// for large row counts; mid (128 x 256, 8 waves of 64 x 64, three stage buffers) for experts
+// of 48 to 128 rows and mid-sized dense GEMMs; small (64 x 256, 4 waves of 64 x 64; two or,
+// for short dense GEMMs, four stage buffers) for fewer rows, and its narrow variant (64 x
+// 128) for the shortest dense GEMMs; decode (16 x 64, one wave) for calls of a few tokens. Which one runs never changes a bit: every output element is one
 // token row against one weight row, accumulated over K in the same stage order with the same
 // instruction and the same lane-to-K mapping in all of them. Together with no split-K, no
 // atomics and no shape-dependent arithmetic, that is what makes a token's bytes independent

@@ -96,16 +96,94 @@ def silu(z):
     return z / (1.0 + np.exp(-z))
 
 
-def expert_ffn(xr, w_gu, w_down):
-    """One SwiGLU expert on rows xr [n, d]: w_gu [2I, d] (gate rows, then up rows),
-    w_down [d, I]. Returns [n, d] float64."""
+def expert_hidden(xr, w_gu):
+    """The gate/up stage of one SwiGLU expert on rows xr [n, d] with w_gu [2I, d] (gate rows,
+    then up rows): returns (gate, up, h) [n, I] float64 with h = silu(gate) * up. This is the
+    gate/up ("GU") kernel's result before any rounding of h (the exact deep prefill page,
+    "Flash Next EXL3: exact deep prefill", names the split into GU and down expert kernels
+    in its numerical-phase audit)."""
     xr = as_f64(xr)
     w_gu = as_f64(w_gu)
     inter = w_gu.shape[0] // 2
     gate = xr @ w_gu[:inter].T
     up = xr @ w_gu[inter:].T
-    h = silu(gate) * up
-    return h @ as_f64(w_down).T
+    return gate, up, silu(gate) * up
+
+
+def expert_down(h, w_down):
+    """The down stage of one expert: h [n, I] times w_down [d, I] transposed, [n, d] float64."""
+    return as_f64(h) @ as_f64(w_down).T
+
+
+def expert_ffn(xr, w_gu, w_down):
+    """One SwiGLU expert on rows xr [n, d]: w_gu [2I, d] (gate rows, then up rows),
+    w_down [d, I]. Returns [n, d] float64."""
+    return expert_down(expert_hidden(xr, w_gu)[2], w_down)
+
+
+# ---------------------------------------------------------------- rounding points
+#
+# The plain result above is what the method reaches up to rounding. The pages fix where a
+# deep-prefill result may be rounded: fp32 accumulation inside the expert kernels, and one
+# rounding of each routed/shared sum at the finish ("Flash Next EXL3: exact deep prefill",
+# numerical-phase audit; "deep prefill (3/8)", the TP-partials item of its checklist). The
+# canonical reduction order itself is a reading: each token's expert contributions are
+# added in ascending expert id, the shared expert's output last. The functions below write
+# those rounding points out exactly, so a GPU result can be compared with them bit for bit.
+
+def bf16_rne(v):
+    """Nearest bfloat16 value of each float64 value, ties to the even significand, returned
+    as float64. bfloat16 is binary32 with 8 significant bits: a finite value with
+    2^(e-1) <= |v| < 2^e is a multiple of 2^(e-8), and below 2^-126 every value is a
+    multiple of 2^-133 (the subnormal spacing). Values that round to 2^128 or beyond become
+    infinite; zeros keep their sign; NaN stays NaN."""
+    v = np.array(v, dtype=np.float64, copy=True)
+    out = v.copy()
+    fin = np.isfinite(v) & (v != 0)
+    if np.any(fin):
+        vf = v[fin]
+        _, e = np.frexp(vf)                         # vf = m * 2^e with 1/2 <= |m| < 1
+        q = np.maximum(e - 8, -133)                 # exponent of the spacing at vf
+        r = np.ldexp(np.rint(np.ldexp(vf, -q)), q)  # np.rint: halves go to the even integer
+        out[fin] = np.where(np.abs(r) >= 2.0 ** 128, np.copysign(np.inf, r), r)
+    return out
+
+
+def fma_f32(a, b, c):
+    """binary32 fused multiply-add: a*b + c rounded once to the nearest binary32 (ties to
+    even), for binary32 inputs. The product of two binary32 values is exact in binary64;
+    the binary64 sum is rounded to odd (its last bit set whenever the sum was inexact,
+    found with the exact error term of the two-sum algorithm), and a round-to-odd value
+    with two or more extra bits rounds to the same binary32 as the exact sum (Boldo and
+    Melquiond, "When double rounding is odd")."""
+    a = np.asarray(a, dtype=np.float32).astype(np.float64)
+    b = np.asarray(b, dtype=np.float32).astype(np.float64)
+    c = np.asarray(c, dtype=np.float32).astype(np.float64)
+    p = a * b
+    s = p + c
+    bb = s - p
+    err = (p - (s - bb)) + (c - bb)                 # p + c = s + err exactly
+    even = (np.asarray(s).view(np.int64) & 1) == 0
+    fix = (err != 0) & even & np.isfinite(s)
+    s = np.where(fix, np.nextafter(s, np.where(err > 0, np.inf, -np.inf)), s)
+    return s.astype(np.float32)
+
+
+def combine_fp32(weights, y, shared=None):
+    """The canonical reduction of one chunk in binary32: for each token and column,
+    acc = 0; acc = fma(w[t, j], y[t, j], acc) for j = 0 .. k-1 (the token's experts in
+    ascending id); acc = acc + shared[t] when there is a shared expert. weights [n, k]
+    binary32, y [n, k, d] binary32 (expert outputs, unweighted), shared [n, d] or None.
+    Returns acc [n, d] binary32 (before the final rounding to the storage type)."""
+    w = np.asarray(weights, dtype=np.float32)
+    y = np.asarray(y, dtype=np.float32)
+    n, k = w.shape
+    acc = np.zeros((n, y.shape[2]), dtype=np.float32)
+    for j in range(k):
+        acc = fma_f32(w[:, j, None], y[:, j, :], acc)
+    if shared is not None:
+        acc = acc + np.asarray(shared, dtype=np.float32)   # binary32 addition, one rounding
+    return acc
 
 
 # ---------------------------------------------------------------- bookkeeping

@@ -7,6 +7,7 @@ pins against copies of the oracle with a planted mistake and see at least one of
 import itertools
 import json
 import os
+import re
 
 import numpy as np
 from scipy.special import expit, softmax
@@ -313,6 +314,120 @@ def pin_chunk_invariance(o):
     for c in (7, 1, 16, 50):
         parts = np.concatenate([o.moe_layer(x[i:i + c], p)["out"] for i in range(0, 50, c)])
         _close(parts, full, 1e-13)
+
+
+
+# --- rounding points (hand-derived fixtures, library routines) ---------------------------
+
+_ROUNDING = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden",
+                         "rounding_points.json")
+
+
+def _num(text):
+    """A fixture number: a short arithmetic expression over integers and powers of two."""
+    t = text.strip()
+    if t in ("inf", "-inf", "-0.0"):
+        return float(t)
+    assert re.fullmatch(r"[0-9+\-*/(). ^]+", t), t
+    return float(eval(t.replace("^", "**"), {"__builtins__": {}}, {}))
+
+
+def _rounding():
+    with open(_ROUNDING) as f:
+        return json.load(f)
+
+
+def _same(a, b):
+    return (a == b and np.signbit(a) == np.signbit(b)) or (np.isnan(a) and np.isnan(b))
+
+
+def pin_bf16_rne(o):
+    """Hand-derived ties, spacing changes, subnormals and overflow; then torch's own
+    binary32 -> bfloat16 conversion (round to nearest even) on random bit patterns and on
+    exact ties (low half 0x8000)."""
+    for c in _rounding()["bf16_rne"]:
+        got = float(o.bf16_rne(np.array([_num(c["in"])]))[0])
+        assert _same(got, _num(c["out"])), c
+    import torch
+    rng = np.random.default_rng(31)
+    bits = rng.integers(0, 2 ** 32, size=200000, dtype=np.uint64).astype(np.uint32)
+    ties = (bits[:50000] & np.uint32(0xFFFF0000)) | np.uint32(0x8000)
+    f = np.concatenate([bits, ties]).view(np.float32)
+    f = f[np.isfinite(f)]
+    want = torch.from_numpy(f.copy()).to(torch.bfloat16).to(torch.float64).numpy()
+    got = o.bf16_rne(f.astype(np.float64))
+    assert np.array_equal(got, want)
+    assert np.array_equal(np.signbit(got), np.signbit(want))
+
+
+def _libm_fmaf():
+    import ctypes
+    import ctypes.util
+    m = ctypes.CDLL(ctypes.util.find_library("m"))
+    m.fmaf.restype = ctypes.c_float
+    m.fmaf.argtypes = [ctypes.c_float] * 3
+    return m.fmaf
+
+
+def pin_fma_f32(o):
+    """Hand-derived fused cases, then the C library's fmaf (correctly rounded) on random
+    triples, many of them cancelling (c close to -a*b)."""
+    for c in _rounding()["fma_f32"]:
+        got = float(o.fma_f32(np.float32(_num(c["a"])), np.float32(_num(c["b"])),
+                              np.float32(_num(c["c"]))))
+        assert _same(got, _num(c["out"])), c
+    fmaf = _libm_fmaf()
+    rng = np.random.default_rng(32)
+    a = (rng.standard_normal(3000) * np.exp2(rng.integers(-20, 20, 3000))).astype(np.float32)
+    b = (rng.standard_normal(3000) * np.exp2(rng.integers(-20, 20, 3000))).astype(np.float32)
+    c = (rng.standard_normal(3000) * np.exp2(rng.integers(-40, 40, 3000))).astype(np.float32)
+    c[:1500] = -(a[:1500] * b[:1500]) * (1 + rng.integers(-4, 5, 1500) * 2.0 ** -23)
+    got = o.fma_f32(a, b, c)
+    want = np.array([fmaf(float(x), float(y), float(z)) for x, y, z in zip(a, b, c)],
+                    dtype=np.float32)
+    assert np.array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def pin_combine_fp32(o):
+    """Order and fusion witnesses (hand-derived), then a slot-by-slot loop over the C
+    library's fmaf in ascending slot order with the shared output added last."""
+    for c in _rounding()["combine_fp32"]:
+        w = np.array([[_num(v) for v in c["w"]]], dtype=np.float32)
+        y = np.array([[[_num(v)] for v in c["y"]]], dtype=np.float32)
+        sh = None if c["shared"] is None else np.array([[_num(c["shared"])]], dtype=np.float32)
+        got = float(o.combine_fp32(w, y, sh)[0, 0])
+        assert _same(got, _num(c["out"])), c
+    fmaf = _libm_fmaf()
+    rng = np.random.default_rng(33)
+    n, k, d = 6, 5, 7
+    w = rng.random((n, k)).astype(np.float32)
+    y = rng.standard_normal((n, k, d)).astype(np.float32)
+    sh = rng.standard_normal((n, d)).astype(np.float32)
+    got = o.combine_fp32(w, y, sh)
+    for t in range(n):
+        for col in range(d):
+            acc = 0.0
+            for j in range(k):
+                acc = fmaf(float(w[t, j]), float(y[t, j, col]), acc)
+            want = np.float32(acc) + sh[t, col]
+            assert got[t, col].view(np.uint32) == np.float32(want).view(np.uint32)
+
+
+def pin_expert_stages(o):
+    """gate/up/h on a hand example (h = 2 silu(1)), and the stages compose to the expert."""
+    g, u, h = o.expert_hidden(np.array([[1.0, 2.0]]), np.array([[1.0, 0.0], [0.0, 1.0]]))
+    assert g[0, 0] == 1.0 and u[0, 0] == 2.0
+    _close(h, [[2.0 / (1.0 + np.exp(-1.0))]], 1e-15)
+    rng = np.random.default_rng(34)
+    x = rng.standard_normal((9, 6))
+    wgu = rng.standard_normal((10, 6))
+    wd = rng.standard_normal((6, 5))
+    g, u, h = o.expert_hidden(x, wgu)
+    _close(g, x @ wgu[:5].T, 1e-14)
+    _close(u, x @ wgu[5:].T, 1e-14)
+    _close(h, g * expit(g) * u, 1e-14)
+    _close(o.expert_down(h, wd), np.einsum("ti,di->td", h, wd), 1e-13)
+    _close(o.expert_ffn(x, wgu, wd), _bf_ffn(x, wgu, wd), 1e-13)
 
 
 ALL_PINS = [v for k_, v in sorted(globals().items()) if k_.startswith("pin_")]

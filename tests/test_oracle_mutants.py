@@ -155,6 +155,76 @@ def _m_down_transposed_square(m):
     m.expert_ffn = expert_ffn
 
 
+def _m_bf16_ties_away(m):
+    def bf16_rne(v):
+        v = np.array(v, dtype=np.float64, copy=True)
+        fin = np.isfinite(v) & (v != 0)
+        _, e = np.frexp(v[fin]); q = np.maximum(e - 8, -133)
+        s_ = np.ldexp(v[fin], -q)
+        v[fin] = np.ldexp(np.sign(s_) * np.floor(np.abs(s_) + 0.5), q)
+        return v
+    m.bf16_rne = bf16_rne
+
+
+def _m_bf16_truncate(m):
+    def bf16_rne(v):
+        v = np.array(v, dtype=np.float64, copy=True)
+        fin = np.isfinite(v) & (v != 0)
+        _, e = np.frexp(v[fin]); q = np.maximum(e - 8, -133)
+        v[fin] = np.ldexp(np.trunc(np.ldexp(v[fin], -q)), q)
+        return v
+    m.bf16_rne = bf16_rne
+
+
+def _m_bf16_nine_bits(m):
+    def bf16_rne(v):
+        v = np.array(v, dtype=np.float64, copy=True)
+        fin = np.isfinite(v) & (v != 0)
+        _, e = np.frexp(v[fin]); q = np.maximum(e - 9, -133)
+        v[fin] = np.ldexp(np.rint(np.ldexp(v[fin], -q)), q)
+        return v
+    m.bf16_rne = bf16_rne
+
+
+def _m_fma_unfused(m):
+    def fma_f32(a, b, c):
+        p = (np.asarray(a, dtype=np.float32) * np.asarray(b, dtype=np.float32)).astype(np.float32)
+        return (p + np.asarray(c, dtype=np.float32)).astype(np.float32)
+    m.fma_f32 = fma_f32
+
+
+def _m_combine_descending(m):
+    def combine_fp32(weights, y, shared=None):
+        w = np.asarray(weights, dtype=np.float32); y = np.asarray(y, dtype=np.float32)
+        acc = np.zeros((w.shape[0], y.shape[2]), dtype=np.float32)
+        for j in reversed(range(w.shape[1])):
+            acc = m.fma_f32(w[:, j, None], y[:, j, :], acc)
+        if shared is not None:
+            acc = acc + np.asarray(shared, dtype=np.float32)
+        return acc
+    m.combine_fp32 = combine_fp32
+
+
+def _m_combine_shared_first(m):
+    def combine_fp32(weights, y, shared=None):
+        w = np.asarray(weights, dtype=np.float32); y = np.asarray(y, dtype=np.float32)
+        acc = np.zeros((w.shape[0], y.shape[2]), dtype=np.float32)
+        if shared is not None:
+            acc = acc + np.asarray(shared, dtype=np.float32)
+        for j in range(w.shape[1]):
+            acc = m.fma_f32(w[:, j, None], y[:, j, :], acc)
+        return acc
+    m.combine_fp32 = combine_fp32
+
+
+def _m_hidden_roles_swapped(m):
+    def expert_hidden(xr, w_gu):
+        xr = m.as_f64(xr); w_gu = m.as_f64(w_gu); inter = w_gu.shape[0] // 2
+        up = xr @ w_gu[:inter].T; gate = xr @ w_gu[inter:].T
+        return gate, up, m.silu(gate) * up
+    m.expert_hidden = expert_hidden
+
+
 MUTANTS = [v for k, v in sorted(globals().items()) if k.startswith("_m_")]
 
 

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 3
+#define MOE_ABI_VERSION 4
 
 typedef enum {
   MOE_OK = 0,
@@ -101,18 +101,29 @@ const char* moe_last_error(void);
  * (0 for an invalid shape). Pure host computation. */
 size_t moe_workspace_bytes(const moe_shape* shape, int64_t max_chunk_tokens);
 
-/* Where a moe_prefill_chunk call over n rows leaves its expert-major member lists inside the
- * workspace (byte offsets from the workspace start; the buckets of the per-expert lists of
- * the pages' "EXL3 on upstream" page, PR #1113, "Latest prefill efficiency candidate"). After
- * the call: counts int32 [E] rows per expert; offsets int32 [E+1] first row of each expert
- * (exclusive prefix sum); row_tok int32 [n*k] chunk-local token of each expert-major row, in
- * ascending token order within an expert; row_slot int32 [n*k] t*k + j of each row (j = the
- * expert's position among the token's ascending ids). For inspection and tests. */
+/* Where a moe_prefill_chunk call over n rows leaves its expert-major member lists and its
+ * intermediate results inside the workspace (byte offsets from the workspace start; the
+ * buckets of the per-expert lists of the pages' "EXL3 on upstream" page, PR #1113, "Latest
+ * prefill efficiency candidate"; the GU and down results of "Flash Next EXL3: exact deep
+ * prefill", numerical-phase audit). After the call:
+ *   counts   int32 [E] rows per expert
+ *   offsets  int32 [E+1] first row of each expert (exclusive prefix sum)
+ *   row_tok  int32 [n*k] chunk-local token of each expert-major row, ascending within an expert
+ *   row_slot int32 [n*k] t*k + j of each row (j = the expert's position among the token's
+ *            ascending ids)
+ *   h        dtype [n*k, I] silu(gate) * up of each expert-major row, rounded to dtype
+ *   h_shared dtype [n, I_s] the same for the shared expert, one row per chunk token
+ *   y        fp32 [n*k, d] each routed expert's output, unweighted, at row t*k + j
+ * With a ring, h and y of a row hold its expert's results only once the expert's wave has run
+ * (all of them after the call's work completes). For inspection and tests. */
 typedef struct {
   size_t counts;
   size_t offsets;
   size_t row_tok;
   size_t row_slot;
+  size_t h;
+  size_t h_shared;
+  size_t y;
   size_t total;   /* == moe_workspace_bytes(shape, n) */
 } moe_ws_offsets;
 

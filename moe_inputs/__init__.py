@@ -202,3 +202,85 @@ def custom_workload(name="custom", T=64, d=64, E=8, k=2, inter=64, inter_shared=
     return Workload(name, T=T, shape=LayerShape(d, E, k, inter, inter_shared, dtype),
                     chunks=tuple(chunks) if chunks else (T,), zipf_s=zipf_s,
                     n_layers=n_layers, rmsnorm_eps=rmsnorm_eps, seed=seed)
+
+
+# ---------------------------------------------------------------- small-integer layers
+#
+# A layer whose every GEMM is exact in binary32, for bit-exact checks of the stages: integer
+# activations and weights small enough that no product or partial sum needs more than 24
+# bits. Routing is planted through the router: feature e < E of x is 1 exactly for the
+# token's k planted experts (0 otherwise) and the router weight is the identity on those
+# features, so the planted experts have logit 1 and every other expert logit 0 (ties among
+# equal logits are then irrelevant) and each routing weight is exactly 1/k (k a power of
+# two). Feature E is the constant 1; the rest are -1, 0 or 1. A gate row puts 26..29 on the
+# constant feature and at most 7 entries of +-1 elsewhere, so gate lies in [19, 36], where
+# silu(gate) equals gate to far below bf16 (and binary32) resolution; an up row has at most 7
+# entries of +-1, so |up| <= 7 and |gate * up| <= 252 is exactly representable in bfloat16; a
+# down row has at most 8 entries of +-1 over the intermediate features.
+
+_T_INT_X, _T_INT_GU, _T_INT_DN, _T_INT_SGU, _T_INT_SDN = range(10, 15)
+
+
+def int_layer_ok(wl: Workload) -> bool:
+    sh = wl.shape
+    return sh.d >= sh.n_experts + 17 and sh.top_k in (1, 2, 4, 8) and sh.top_k <= sh.n_experts
+
+
+def make_int_x(wl: Workload, device="cpu", T: Optional[int] = None) -> torch.Tensor:
+    """Small-integer activations [T, d] with the planted routing (see above)."""
+    assert int_layer_ok(wl), "small-integer layers need d >= E + 17 and k in {1, 2, 4, 8}"
+    T = wl.T if T is None else T
+    sh = wl.shape
+    E, d, k = sh.n_experts, sh.d, sh.top_k
+    rng = np.random.default_rng(_subseed(wl.seed, 0, _T_INT_X))
+    x = np.zeros((T, d), dtype=np.float32)
+    for t0 in range(0, T, 4096):
+        t1 = min(T, t0 + 4096)
+        pick = np.argpartition(rng.random((t1 - t0, E)), k - 1, axis=1)[:, :k]
+        np.put_along_axis(x[t0:t1, :E], pick, 1.0, axis=1)
+    x[:, E] = 1.0
+    x[:, E + 1:] = rng.integers(-1, 2, size=(T, d - E - 1)).astype(np.float32)
+    return torch.from_numpy(x).to(device=device, dtype=sh.torch_dtype)
+
+
+def _sparse_rows(rng, n_rows, width, lo, n_nz, const_col=None, const_range=None):
+    """Dense [n_rows, width] float32 rows with n_nz entries of +-1 at columns >= lo (entries
+    that land on the same column add up) and, optionally, a constant in const_range at
+    const_col."""
+    m = np.zeros((n_rows, width), dtype=np.float32)
+    cols = rng.integers(lo, width, size=(n_rows, n_nz))
+    vals = rng.choice(np.array([-1.0, 1.0], dtype=np.float32), size=(n_rows, n_nz))
+    np.add.at(m, (np.repeat(np.arange(n_rows), n_nz), cols.ravel()), vals.ravel())
+    if const_col is not None:
+        m[:, const_col] = rng.integers(const_range[0], const_range[1] + 1, size=n_rows)
+    return m
+
+
+def make_int_layer(wl: Workload, layer: int = 0, device="cpu") -> dict:
+    """A small-integer layer (keys as make_layer; router_bias None)."""
+    assert int_layer_ok(wl), "small-integer layers need d >= E + 17 and k in {1, 2, 4, 8}"
+    sh = wl.shape
+    E, d, I, Is = sh.n_experts, sh.d, sh.inter, sh.inter_shared
+    dt = sh.torch_dtype
+    w_router = torch.zeros((E, d), dtype=dt)
+    w_router[:, :E] = torch.eye(E, dtype=dt)
+    lines = torch.empty((E, sh.line_elems), dtype=dt, device=device)
+    for e in range(E):
+        rng = np.random.default_rng(_subseed(wl.seed, layer, _T_INT_GU, e))
+        gate = _sparse_rows(rng, I, d, E + 1, 7, E, (26, 29))
+        up = _sparse_rows(rng, I, d, E + 1, 7)
+        down = _sparse_rows(rng, d, I, 0, 8)
+        line = np.concatenate([gate.ravel(), up.ravel(), down.ravel()])
+        lines[e].copy_(torch.from_numpy(line).to(dt))
+    out = {"w_router": w_router.to(device), "router_bias": None, "lines": lines}
+    if Is > 0:
+        rng = np.random.default_rng(_subseed(wl.seed, layer, _T_INT_SGU))
+        gate = _sparse_rows(rng, Is, d, E + 1, 7, E, (26, 29))
+        up = _sparse_rows(rng, Is, d, E + 1, 7)
+        out["w_gu_shared"] = torch.from_numpy(np.concatenate([gate, up])).to(device=device, dtype=dt)
+        rng = np.random.default_rng(_subseed(wl.seed, layer, _T_INT_SDN))
+        out["w_down_shared"] = torch.from_numpy(_sparse_rows(rng, d, Is, 0, 8)).to(device=device, dtype=dt)
+    else:
+        out["w_gu_shared"] = None
+        out["w_down_shared"] = None
+    return out

@@ -29,7 +29,7 @@ class MoeLayer(ctypes.Structure):
 
 class MoeWsOffsets(ctypes.Structure):
     _fields_ = [("counts", c_sz), ("offsets", c_sz), ("row_tok", c_sz), ("row_slot", c_sz),
-                ("total", c_sz)]
+                ("h", c_sz), ("h_shared", c_sz), ("y", c_sz), ("total", c_sz)]
 
 
 class MoeProfile(ctypes.Structure):
@@ -78,7 +78,7 @@ SIGNATURES = {
 _lib = None
 
 
-ABI_VERSION = 3     # MOE_ABI_VERSION of include/moe_prefill.h
+ABI_VERSION = 4     # MOE_ABI_VERSION of include/moe_prefill.h
 
 
 def lib():

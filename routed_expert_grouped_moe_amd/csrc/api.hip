@@ -411,6 +411,9 @@ moe_status moe_workspace_offsets(const moe_shape* shape, int64_t n, moe_ws_offse
   out->offsets = L.offsets;
   out->row_tok = L.row_tok;
   out->row_slot = L.row_slot;
+  out->h = L.h;
+  out->h_shared = L.h_shared;
+  out->y = L.y;
   out->total = L.total;
   return MOE_OK;
 }

@@ -42,7 +42,7 @@ def _run(cmd):
     return r.returncode, "\n".join(lines)
 
 
-def build(verbose: bool = False, jobs: int = 8) -> str:
+def build(verbose: bool = False, jobs: int = 8, plants: bool = True) -> str:
     hipcc = _hipcc()
     os.makedirs(OUT_DIR, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
@@ -62,12 +62,62 @@ def build(verbose: bool = False, jobs: int = 8) -> str:
     if failed:
         msg = "\n".join(f"--- {s}\n{l}" for s, l in failed)
         raise RuntimeError(f"hipcc failed:\n{msg}")
-    tmp = LIB + ".tmp"
+    _link(hipcc, objs, LIB)
+    if plants:
+        build_plants(hipcc, srcs, objs, jobs)
+    return LIB
+
+
+def _link(hipcc, objs, lib):
+    tmp = lib + ".tmp"
     rc, log = _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp])
     if rc != 0:
         raise RuntimeError(f"link failed:\n{log}")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+
+
+# Test-only builds, each with one known mistake planted (csrc/device_common.h, "planted
+# mistakes"): the GPU parity tests must go red on every one of them. Only the sources that use
+# the macros are compiled again; the libraries land in _build/, never next to the real one.
+PLANTS = {
+    "combine_desc": "MOE_PLANT_COMBINE_DESC",
+    "h_trunc": "MOE_PLANT_H_TRUNC",
+    "out_twice": "MOE_PLANT_OUT_TWICE",
+    "korder_tall": "MOE_PLANT_KORDER_TALL",
+}
+_PLANTED_SOURCES = ("gemm.hip", "combine.hip")
+
+
+def plant_lib(name: str) -> str:
+    return os.path.join(OUT_DIR, f"libmoeprefill_plant_{name}.so")
+
+
+def build_plants(hipcc, srcs, objs, jobs):
+    jobs_list = []
+    for name, macro in PLANTS.items():
+        d = os.path.join(OUT_DIR, f"plant_{name}")
+        os.makedirs(d, exist_ok=True)
+        for src in srcs:
+            if os.path.basename(src) in _PLANTED_SOURCES:
+                jobs_list.append((name, macro, src, os.path.join(d, os.path.basename(src)[:-4] + ".o")))
+
+    def compile_one(job):
+        name, macro, src, obj = job
+        return job, _run([hipcc, *HIP_FLAGS, f"-D{macro}=1", "-c", src, "-o", obj])
+
+    failed = []
+    with cf.ThreadPoolExecutor(max_workers=jobs) as ex:
+        for job, (rc, log) in ex.map(compile_one, jobs_list):
+            if rc != 0:
+                failed.append((job, log))
+    if failed:
+        msg = "\n".join(f"--- {j[0]} {j[2]}\n{l}" for j, l in failed)
+        raise RuntimeError(f"hipcc failed (planted builds):\n{msg}")
+    for name in PLANTS:
+        d = os.path.join(OUT_DIR, f"plant_{name}")
+        pobjs = [os.path.join(d, os.path.basename(o)) if os.path.basename(o)[:-2] + ".hip"
+                 in _PLANTED_SOURCES else o for o in objs]
+        _link(hipcc, pobjs, plant_lib(name))
 
 
 if __name__ == "__main__":

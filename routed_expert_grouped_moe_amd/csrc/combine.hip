@@ -72,10 +72,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 #pragma unroll
         for (int u = 0; u < U; ++u)
           if (on[u])
-            v[i][u] = load_stream(yt + static_cast<int64_t>(j + i) * d + c0 + 1024 * u);
+            v[i][u] = load_stream(yt + static_cast<int64_t>(MOE_SLOT(j + i, k)) * d + c0 + 1024 * u);
 #pragma unroll
       for (int i = 0; i < J; ++i) {
-        const float wj = wt[j + i];
+        const float wj = wt[MOE_SLOT(j + i, k)];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           acc[u].x = fmaf(wj, v[i][u].x, acc[u].x);
@@ -86,11 +86,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       }
     }
     for (; j < k; ++j) {
-      const float wj = wt[j];
+      const float wj = wt[MOE_SLOT(j, k)];
 #pragma unroll
       for (int u = 0; u < U; ++u)
         if (on[u]) {
-          const float4 v = load_stream(yt + static_cast<int64_t>(j) * d + c0 + 1024 * u);
+          const float4 v = load_stream(yt + static_cast<int64_t>(MOE_SLOT(j, k)) * d + c0 + 1024 * u);
           acc[u].x = fmaf(wj, v.x, acc[u].x);
           acc[u].y = fmaf(wj, v.y, acc[u].y);
           acc[u].z = fmaf(wj, v.z, acc[u].z);
@@ -114,10 +114,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
 }
 
 // x_new = round(x + delta) (when delta is given); normed = round(x_new / sqrt(mean(x_new^2) +
-// eps)). Each thread sums squares of columns tid, tid + 256, ... in order, then a fixed
+// eps)). x_out may be x itself (each element is read before the same thread overwrites it), so
+// neither carries __restrict__. Each thread sums squares of columns tid, tid + 256, ... in order, then a fixed
 // halving tree over the 256 partial sums: the same bits on every run.
 template <typename T>
-__global__ __launch_bounds__(256) void add_rmsnorm_kernel(const T* __restrict__ x,
+__global__ __launch_bounds__(256) void add_rmsnorm_kernel(const T* x,
                                                           const T* __restrict__ delta, int d,
                                                           float eps, T* x_out,
                                                           T* __restrict__ normed) {

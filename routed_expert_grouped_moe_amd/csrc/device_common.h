@@ -54,4 +54,44 @@ __device__ __forceinline__ float silu_f32(float z) {
   return z * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(z * -1.4426950408889634f));
 }
 
+// ---------------------------------------------------------------- planted mistakes
+// Test-only builds of the library each define one MOE_PLANT_* macro and so carry one known
+// mistake, which the GPU parity tests must catch (tests/test_gpu_controls.py); the library
+// itself is built with none of them, and then every helper below is the identity.
+//   MOE_PLANT_COMBINE_DESC  the combine walks a token's experts in descending id
+//   MOE_PLANT_H_TRUNC       h is truncated to bf16 instead of rounded to nearest even
+//   MOE_PLANT_OUT_TWICE     the routed sum is rounded to bf16 before the shared output is added
+//   MOE_PLANT_KORDER_TALL   the 320-row tiles walk their K stages backwards (a K order that
+//                           depends on the M-tile height)
+#if defined(MOE_PLANT_COMBINE_DESC)
+#define MOE_SLOT(j, k) ((k) - 1 - (j))
+#else
+#define MOE_SLOT(j, k) (j)
+#endif
+
+template <typename T>
+__device__ __forceinline__ T h_store(float f) {
+#if defined(MOE_PLANT_H_TRUNC)
+  if constexpr (sizeof(T) == 2) return static_cast<T>(__float_as_uint(f) >> 16);
+#endif
+  return Elt<T>::store(f);
+}
+
+template <typename T>
+__device__ __forceinline__ float routed_sum(float a) {
+#if defined(MOE_PLANT_OUT_TWICE)
+  if constexpr (sizeof(T) == 2) return bf16_to_f32(f32_to_bf16(a));
+#endif
+  return a;
+}
+
+template <int BM>
+__device__ __forceinline__ int k_stage(int s, int nk) {
+#if defined(MOE_PLANT_KORDER_TALL)
+  if constexpr (BM == 320) return nk - 1 - s;
+#endif
+  (void)nk;
+  return s;
+}
+
 }  // namespace moe

@@ -214,7 +214,8 @@ __device__ __forceinline__ void mainloop(const char* const (&src)[TL::LPW], int 
 #pragma clang diagnostic ignored "-Winline-asm"
     asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
                  :
-                 : "s"(__builtin_amdgcn_readfirstlane(dst)), "v"(src[q] + s * TL::RB)
+                 : "s"(__builtin_amdgcn_readfirstlane(dst)),
+                   "v"(src[q] + k_stage<TL::BM>(s, nk) * TL::RB)
                  : "memory", "m0");
 #pragma clang diagnostic pop
   };
@@ -481,7 +482,7 @@ void gu_kernel(GuParams p) {
       for (int j = 0; j < TL::FN; ++j) acc[i][j] = f32x4_t{nan, nan, nan, nan};
   }
   auto val = [&](int i, int j, int r) -> T {
-    return Elt<T>::store(silu_f32(acc[i][j][r]) * acc[i][j + H][r]);
+    return h_store<T>(silu_f32(acc[i][j][r]) * acc[i][j + H][r]);
   };
   auto row_of = [&](int sr) -> int64_t {      // sr = block * 16 + row in block
     const int tr = block_row<TL>(sr >> 4, wm) + (sr & 15);
@@ -542,13 +543,13 @@ __device__ __forceinline__ void combine_slab(char* lds, Val val, int wm, int64_t
 #pragma unroll
           for (int u = 0; u < U; ++u)
             v[q][u] = on[u] ? __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(
-                                  y + (t[u] * k + j + q) * d + col0 + col[u]))
+                                  y + (t[u] * k + MOE_SLOT(j + q, k)) * d + col0 + col[u]))
                             : f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int q = 0; q < 8; ++q)
 #pragma unroll
           for (int u = 0; u < U; ++u) {
-            const float wj = wts[(t0 + t[u]) * k + j + q];
+            const float wj = wts[(t0 + t[u]) * k + MOE_SLOT(j + q, k)];
             acc[u][0] = fmaf(wj, v[q][u][0], acc[u][0]);
             acc[u][1] = fmaf(wj, v[q][u][1], acc[u][1]);
             acc[u][2] = fmaf(wj, v[q][u][2], acc[u][2]);
@@ -559,9 +560,9 @@ __device__ __forceinline__ void combine_slab(char* lds, Val val, int wm, int64_t
 #pragma unroll
         for (int u = 0; u < U; ++u) {
           const f32x4_t v = on[u] ? __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(
-                                        y + (t[u] * k + j) * d + col0 + col[u]))
+                                        y + (t[u] * k + MOE_SLOT(j, k)) * d + col0 + col[u]))
                                   : f32x4_t{0.f, 0.f, 0.f, 0.f};
-          const float wj = wts[(t0 + t[u]) * k + j];
+          const float wj = wts[(t0 + t[u]) * k + MOE_SLOT(j, k)];
           acc[u][0] = fmaf(wj, v[0], acc[u][0]);
           acc[u][1] = fmaf(wj, v[1], acc[u][1]);
           acc[u][2] = fmaf(wj, v[2], acc[u][2]);
@@ -572,8 +573,8 @@ __device__ __forceinline__ void combine_slab(char* lds, Val val, int wm, int64_t
         if (!on[u]) continue;
         const int c = c0 + 64 * u;
         const f32x4_t sv = *reinterpret_cast<const f32x4_t*>(stg + (c / CPR) * NCOL + col[u]);
-        const float a0 = acc[u][0] + sv[0], a1 = acc[u][1] + sv[1];
-        const float a2 = acc[u][2] + sv[2], a3 = acc[u][3] + sv[3];
+        const float a0 = routed_sum<T>(acc[u][0]) + sv[0], a1 = routed_sum<T>(acc[u][1]) + sv[1];
+        const float a2 = routed_sum<T>(acc[u][2]) + sv[2], a3 = routed_sum<T>(acc[u][3]) + sv[3];
         T* o = out + (t0 + t[u]) * d + col0 + col[u];
         if constexpr (sizeof(T) == 2) {
           *reinterpret_cast<uint2*>(o) = uint2{f32x2_to_bf16x2(a0, a1), f32x2_to_bf16x2(a2, a3)};

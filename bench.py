@@ -52,7 +52,9 @@ def algorithmic(stage: str, T: int, sh, counts):
     if stage == "topk":
         return 0, T * E * 4 + T * k * 8
     if stage == "gu_routed":
-        return 2 * Ns * d * 2 * I, used * 2 * I * d * 2 + Ns * d * 2 + Ns * I * 2
+        # each prompt row is read once (its reads for its other k - 1 experts are re-reads,
+        # not algorithmic bytes), the used experts' gate/up weights once, h written once
+        return 2 * Ns * d * 2 * I, used * 2 * I * d * 2 + T * d * 2 + Ns * I * 2
     if stage == "down_routed":
         return 2 * Ns * I * d, used * d * I * 2 + Ns * I * 2 + Ns * d * 4
     if stage == "gu_shared":
@@ -67,6 +69,21 @@ def algorithmic(stage: str, T: int, sh, counts):
     if stage in ("hist", "permute"):
         return 0, Ns * 4 * (1 if stage == "hist" else 3)
     return 0, 0
+
+
+def _shape(wl):
+    import routed_expert_grouped_moe_amd as moe
+    s = wl.shape
+    return moe.make_shape(s.d, s.n_experts, s.top_k, s.inter, s.inter_shared, s.dtype)
+
+
+def _place(wl, layer=0, offloaded=(), ring=None, params=None):
+    """(params on cuda:0, library Layer) for one layer of a workload."""
+    import moe_inputs as mi
+    import routed_expert_grouped_moe_amd as moe
+    if params is None:
+        params = mi.make_layer(wl, layer, device="cuda")
+    return params, moe.Layer.from_params(params, _shape(wl), "cuda", offloaded, ring, layer)
 
 
 def time_steps(fn, steps, warmup):
@@ -149,17 +166,13 @@ def stack_variant(steps: int):
 
     import moe_inputs as mi
     import routed_expert_grouped_moe_amd as moe
-    from tests.parity import place
     wl = mi.WORKLOADS["stack_32700"]
     E = wl.shape.n_experts
     off = range(E - wl.n_offloaded, E)
-    ring, layers = None, []
+    ring, layers = moe.Ring(_shape(wl), wl.ring_lines), []
     for layer in range(wl.n_layers):
         p = mi.make_layer(wl, layer, device="cuda")
-        if ring is None:
-            from tests.parity import moe_shape
-            ring = moe.Ring(moe_shape(wl), wl.ring_lines)
-        layers.append(place(wl, layer=layer, offloaded=off, ring=ring, params=p)[1])
+        layers.append(_place(wl, layer=layer, offloaded=off, ring=ring, params=p)[1])
         del p
     x = mi.make_x(wl, device="cuda")
     cs = torch.cuda.Stream()
@@ -241,6 +254,58 @@ def cpu_baseline(params, wl, x, seconds, chunk=1024):
             "gflops_fp64": round(flop / dt / 1e9, 2)}
 
 
+def cpu_baseline_configs(sample_tokens=256):
+    """The fp64 oracle on the first tokens of the three smaller workloads (the tiny fp32
+    layer, the 3,001-token layer and the 4,099-token chunk-gate layer), once on one BLAS
+    thread and once on all of them."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    import moe_inputs as mi
+    import oracle.moe_oracle as orc
+    from tests.parity import oracle_params
+    res = {}
+    for name in ("tiny_fp32", "layer_3001", "chunk_gate_4099"):
+        wl = mi.WORKLOADS[name]
+        params = mi.make_layer(wl, device="cuda")
+        n = min(wl.T, sample_tokens)
+        xs = mi.to_numpy_exact(mi.make_x(wl, device="cuda", T=n))
+        op = oracle_params(params, wl)
+        del params
+        ent = {"tokens": n}
+        for label, lim in (("one_core", 1), ("all_cores", None)):
+            with threadpool_limits(limits=lim):
+                threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+                t0 = time.perf_counter()
+                orc.moe_layer(xs, op)
+                dt = time.perf_counter() - t0
+            ent[label] = {"tokens_per_s": round(n / dt, 2), "cores": int(threads),
+                          "seconds": round(dt, 2)}
+        res[name] = ent
+        del op
+    return res
+
+
+def h2d_line_probe(line_bytes: int, n_lines: int, runs: int = 2) -> float:
+    """Pinned host -> HBM rate (GB/s) of n_lines copies of one expert line each, alternating
+    two streams as the ring's copies do."""
+    import torch
+    src = torch.empty(n_lines * line_bytes, dtype=torch.uint8, pin_memory=True)
+    dst = torch.empty(n_lines * line_bytes, dtype=torch.uint8, device="cuda")
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    best = float("inf")
+    for _ in range(runs):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(n_lines):
+            with torch.cuda.stream(streams[i % 2]):
+                dst[i * line_bytes:(i + 1) * line_bytes].copy_(
+                    src[i * line_bytes:(i + 1) * line_bytes], non_blocking=True)
+        for s in streams:
+            s.synchronize()
+        best = min(best, time.perf_counter() - t0)
+    return n_lines * line_bytes / best / 1e9
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -268,7 +333,6 @@ def main():
 
     import moe_inputs as mi
     import routed_expert_grouped_moe_amd as moe
-    from tests.parity import place
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
@@ -288,7 +352,7 @@ def main():
     wl = mi.WORKLOADS["offload_16022"]      # T = 16,022 inputs (seeded), placed resident here
     T = wl.T
     log(f"[bench] generating layer and {T} tokens on cuda:0")
-    params, L = place(wl)
+    params, L = _place(wl)
     x = mi.make_x(wl, device="cuda")
     sh = L.shape
     torch.cuda.synchronize()
@@ -325,6 +389,10 @@ def main():
         if b:
             ent["gbps"] = round(b_l / (per_launch_ms / 1e3) / 1e9, 1)
             ent["hbm_frac"] = round(ent["gbps"] * 1e9 / PEAK_HBM, 4)
+            tr = measured_traffic(stage)
+            if tr is not None:
+                # HBM bytes the counters saw over the algorithmic bytes: re-reads and waste
+                ent["traffic_over_algorithmic"] = round(tr / b_l, 3)
         if prof3[stage][2] > 0:
             ent["clock_mhz"] = round(prof3[stage][2], 0)
         kernels[stage] = ent
@@ -351,6 +419,8 @@ def main():
         roof = {"kernel": dom, "bound": "mfma", "achieved": round(ach, 1), "peak": 2500.0,
                 "unit": "TFLOP/s", "frac": round(ach / 2500.0, 4), "traffic": measured_traffic(dom),
                 "flops_per_launch": int(f / n_l), "avg_launch_us": round(avg_s * 1e6, 2)}
+    if roof["traffic"] is not None:
+        roof["traffic_over_algorithmic"] = round(roof["traffic"] / (b / n_l), 3)
     clk = prof3[dom][2]
     if clk > 0:
         # the shader clock the kernel ran at (sampled in the kernel): the MFMA peak scales with
@@ -372,7 +442,7 @@ def main():
         variants["small_call_T8"] = small_call_variant(L, mi, wl)
         log("[bench] ring variant: all 512 experts in a pinned bank, 64 lines, chunk 2048")
         ring = moe.Ring(sh, 64)
-        _, Lr = place(wl, offloaded=range(sh.n_experts), ring=ring, params=params)
+        _, Lr = _place(wl, offloaded=range(sh.n_experts), ring=ring, params=params)
         br = moe.layer_buffers(Lr, T, 2048)
         cs = torch.cuda.Stream()
         ring_step = lambda: moe.moe_prefill_layer(Lr, x, 2048, bufs=br, copy_stream=cs)
@@ -384,11 +454,16 @@ def main():
         st = ring.stats()
         per_step_bytes = st["bytes_h2d"] / 3
         link = h2d_probe(1 << 30, 3)
+        line_rate = h2d_line_probe(ring.line_bytes, 64)
         # the copies at the link rate of one 1 GiB pinned copy: a floor the 6 MiB line copies of
         # the ring do not reach, so the compute share below is a lower bound
         t_copy = per_step_bytes / (link * 1e9) * 1e3
+        # the same bytes as 6 MiB line copies alternating two streams with nothing else on the
+        # GPU (the ring's copy pattern): the copy time the ring would take without compute
+        t_lines = per_step_bytes / (line_rate * 1e9) * 1e3
         t_gemm = variants["resident_chunk2048"]["ms_per_step"]        # ms, compute alone
         hidden = (t_copy + t_gemm - r_wall) / t_gemm
+        hidden_lines = (t_lines + t_gemm - r_wall) / t_gemm
         variants["offload_ring64_chunk2048"] = {
             "tokens_per_s": round(T / (r_wall / 1e3), 1), "ms_per_step": round(r_wall, 2),
             "step_ms": spread(r_per),
@@ -401,6 +476,9 @@ def main():
             "ring_hit_rate": round(st["hits"] / max(1, st["hits"] + st["misses"]), 4),
             "copy_waits_per_step": st["copy_waits"] // 3,
             "compute_hidden_frac_vs_link_floor": round(max(0.0, min(1.0, hidden)), 3),
+            "h2d_line_copy_gbps_measured": round(line_rate, 2),
+            "line_copies_alone_ms": round(t_lines, 2),
+            "compute_hidden_frac_vs_line_copies": round(max(0.0, min(1.0, hidden_lines)), 3),
             "bit_identical_to_batched": bool(ok)}
         del br, Lr
         ring.close()
@@ -412,6 +490,10 @@ def main():
     if not args.no_cpu_baseline:
         log(f"[bench] CPU oracle baseline, about {args.cpu_sample_seconds:.0f} s")
         cpu = cpu_baseline(params, wl, x, args.cpu_sample_seconds)
+        del params, L, bufs
+        torch.cuda.empty_cache()
+        log("[bench] CPU oracle on the three smaller workloads, one core and all cores")
+        cpu["other_workloads"] = cpu_baseline_configs()
 
     line = {
         "metric": METRIC, "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1,

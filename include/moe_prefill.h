@@ -152,7 +152,14 @@ moe_status moe_prefill_route(const moe_layer* layer, const void* x, int64_t T, i
  *   x, ids, weights: the whole prompt's tensors as passed to / returned by moe_prefill_route
  *   counts_host  HOST [E] int32 expert counts of this chunk, or NULL. Only used with a ring: if
  *                NULL the call copies the counts to the host and waits for them (its only
- *                synchronisation).
+ *                synchronisation). When given, they must equal the chunk's counts as the GPU
+ *                buckets its ids (chunk_counts of moe_prefill_route for these rows, as
+ *                moe_prefill_layer passes them): the waves are planned from them. The call
+ *                checks only that they sum to n*k. Other counts leave out rows t0..t0+n-1
+ *                unspecified (routed rows may be missed, or read an expert from no line and
+ *                come out NaN: each wave's table entries are cleared once the wave is done),
+ *                while every access stays inside the caller's tensors, the workspace and the
+ *                ring's lines, and the ring's bookkeeping stays consistent.
  *   out          device [T, d] dtype; only rows t0..t0+n-1 are written
  *   ws, ws_bytes device workspace of at least moe_workspace_bytes(shape, n) bytes
  *   stream       compute stream; copy_stream: stream for ring copies (NULL = stream). The
@@ -217,9 +224,32 @@ moe_status moe_ring_release(moe_ring* ring, const int32_t* lines, int32_t n, voi
 /* Device pointer of a ring line (NULL for a bad index). */
 const void* moe_ring_line_ptr(const moe_ring* ring, int32_t line);
 
+/* Stage an expert list for a layer that runs later (the cross-layer prefetch of "EXL3 on
+ * upstream", PR #1113, "Latest measured follow-up"): like moe_stage_experts, but the lines are
+ * not held. Each miss is copied on copy_stream and its line's `release` is recorded right
+ * behind the copy, so the line keeps the expert for a later staging (a hit) unless it is
+ * evicted first. Misses need free lines as in moe_stage_experts (MOE_ERR_RING otherwise,
+ * nothing changes). experts: HOST [n], distinct, offloaded in the layer's bank. */
+moe_status moe_ring_prefetch(moe_ring* ring, int32_t layer_id, const int32_t* experts, int32_t n,
+                             void* copy_stream);
+
+/* Why a staging was asked for. The chunk sequencer of moe_prefill_chunk stages a chunk's
+ * offloaded experts in waves: INITIAL is a chunk's first wave (no routed GEMM of the chunk can
+ * start before it lands), AHEAD a later wave staged while the wave before it computes, DEMAND
+ * a later wave staged only once the wave before it has released its lines (too few free lines
+ * to stage it ahead); moe_stage_experts calls count as DEMAND and moe_ring_prefetch calls as
+ * CROSS_LAYER. */
+enum {
+  MOE_COPY_INITIAL = 0,
+  MOE_COPY_AHEAD = 1,
+  MOE_COPY_DEMAND = 2,
+  MOE_COPY_CROSS_LAYER = 3,
+  MOE_COPY_KINDS = 4
+};
+
 /* Ring counters (all cumulative since creation or moe_ring_reset_stats). */
 typedef struct {
-  int32_t version;            /* set to 1 by the library */
+  int32_t version;            /* set to 2 by the library */
   int32_t n_lines;
   int64_t hits;               /* staged experts already present in a line */
   int64_t misses;             /* staged experts copied from a bank */
@@ -227,6 +257,10 @@ typedef struct {
   int64_t copy_waits;         /* copy-stream waits on release events (a staging call waits
                                  once per copy stream for the newest release it needs) */
   int64_t waves;              /* staging waves run by moe_prefill_chunk */
+  /* version 2: per kind of staging (MOE_COPY_*), the line bytes of every expert asked for
+   * (hits and misses) and of those copied (misses); copied_bytes sum to bytes_h2d */
+  int64_t requested_bytes[MOE_COPY_KINDS];
+  int64_t copied_bytes[MOE_COPY_KINDS];
 } moe_ring_stats_t;
 
 moe_status moe_ring_stats(const moe_ring* ring, moe_ring_stats_t* stats_out);
@@ -242,9 +276,10 @@ void moe_ring_destroy(moe_ring* ring);
 /* Per-kernel timing with HIP events. While enabled, every launch the library enqueues is
  * bracketed by two timing events recorded on the launch's own stream; moe_profile_read waits
  * for the recorded events and adds their elapsed times to per-stage totals. The GEMM kernels
- * also sample the shader clock (thread 0 of every workgroup, start to last store) into a small
- * device buffer the library allocates on first use per device. Process-wide and thread-safe;
- * off by default (then nothing is recorded). Version 2 of moe_profile_t adds clock_mhz. */
+ * also sample the shader clock (thread 0 of every workgroup, start to last store) into 256
+ * bytes of counters held in the library's own device code object (one copy per device; no
+ * allocation). Process-wide and thread-safe; off by default (then nothing is recorded).
+ * Version 2 of moe_profile_t adds clock_mhz. */
 enum {
   MOE_STAGE_ROUTER = 0,     /* router GEMM */
   MOE_STAGE_TOPK = 1,       /* top-k + weights */

@@ -103,9 +103,23 @@ class Ring:
         self._banks[int(layer_id)] = bank
 
     def stats(self) -> dict:
+        """Ring counters; requested_bytes / copied_bytes are dicts by kind of staging
+        (initial, ahead, demand, cross_layer)."""
+        from ._abi import COPY_KINDS
         st = MoeRingStats()
         check(lib().moe_ring_stats(self.handle, ctypes.byref(st)), "moe_ring_stats")
-        return {f: getattr(st, f) for f, _ in MoeRingStats._fields_}
+        out = {}
+        for f, _ in MoeRingStats._fields_:
+            v = getattr(st, f)
+            out[f] = {k: int(v[i]) for i, k in enumerate(COPY_KINDS)} if f.endswith("_bytes") else v
+        return out
+
+    def prefetch(self, layer_id: int, experts: Sequence[int], copy_stream=None):
+        """moe_ring_prefetch: stage experts of a later layer without holding their lines."""
+        n = len(experts)
+        ex = (ctypes.c_int32 * max(n, 1))(*[int(e) for e in experts])
+        check(lib().moe_ring_prefetch(self.handle, int(layer_id), ex, n, _stream(copy_stream)),
+              "moe_ring_prefetch")
 
     def reset_stats(self):
         check(lib().moe_ring_reset_stats(self.handle), "moe_ring_reset_stats")

@@ -41,9 +41,13 @@ STAGES = ["router", "topk", "chunk_counts", "table", "hist", "scan", "permute", 
           "down_shared", "gu_routed", "down_routed", "combine", "rmsnorm", "down_shared_combine"]
 
 
+COPY_KINDS = ["initial", "ahead", "demand", "cross_layer"]     # MOE_COPY_* order
+
+
 class MoeRingStats(ctypes.Structure):
     _fields_ = [("version", c_i32), ("n_lines", c_i32), ("hits", c_i64), ("misses", c_i64),
-                ("bytes_h2d", c_i64), ("copy_waits", c_i64), ("waves", c_i64)]
+                ("bytes_h2d", c_i64), ("copy_waits", c_i64), ("waves", c_i64),
+                ("requested_bytes", c_i64 * 4), ("copied_bytes", c_i64 * 4)]
 
 
 # name -> (restype, argtypes); every function declared in include/moe_prefill.h
@@ -63,6 +67,7 @@ SIGNATURES = {
     "moe_ring_create": (c_i32, [ctypes.POINTER(MoeShape), c_vp, c_i32, ctypes.POINTER(c_vp)]),
     "moe_ring_bind_bank": (c_i32, [c_vp, c_i32, c_vp, c_vp]),
     "moe_stage_experts": (c_i32, [c_vp, c_i32, c_vp, c_i32, c_vp, c_vp]),
+    "moe_ring_prefetch": (c_i32, [c_vp, c_i32, c_vp, c_i32, c_vp]),
     "moe_ring_wait_ready": (c_i32, [c_vp, c_vp, c_i32, c_vp]),
     "moe_ring_release": (c_i32, [c_vp, c_vp, c_i32, c_vp]),
     "moe_ring_line_ptr": (c_vp, [c_vp, c_i32]),

@@ -237,8 +237,10 @@ moe_status ring_waves(const moe_layer* L, const void* x, int64_t t0, int64_t n,
     while (staged < nw && staged <= i + 1) {   // this wave, and the next one if lines allow
       const int ws_ = wave_at(staged);
       for (int e : wexp[ws_]) later[e] = 0;
+      const int kind = staged == 0 ? MOE_COPY_INITIAL
+                                   : (staged > i ? MOE_COPY_AHEAD : MOE_COPY_DEMAND);
       st = ring_stage(R, L->layer_id, wexp[ws_].data(), static_cast<int32_t>(wexp[ws_].size()),
-                      cs, wlines[ws_].data(), &later, /*two_streams=*/true);
+                      cs, wlines[ws_].data(), &later, /*two_streams=*/true, kind);
       if (st == MOE_ERR_RING && staged > i) { st = MOE_OK; break; }   // retry after release
       if (st != MOE_OK) { release_held(i); return st; }
       ++staged;
@@ -255,6 +257,13 @@ moe_status ring_waves(const moe_layer* L, const void* x, int64_t t0, int64_t n,
       err = launch_gu_routed(sh.dtype, x, t0, sh.d, sh.inter, g, row_tok, h, s);
     if (st == MOE_OK && err == hipSuccess)
       err = launch_down_routed(sh.dtype, h, sh.d, sh.inter, g, row_slot, y, s);
+    // The wave's table entries go back to NULL: a tile outside the planned waves (only
+    // possible with caller counts that differ from the chunk's own) then finds no line and
+    // writes NaN, instead of reading a line a later copy may be refilling.
+    if (st == MOE_OK && err == hipSuccess) {
+      std::vector<const void*> none(nl, nullptr);
+      err = launch_upload_pairs(wtab, wexp[w].data(), none.data(), nl, s);
+    }
     if (st == MOE_OK && err != hipSuccess)
       st = set_error(MOE_ERR_HIP, "wave %d launch: %s", w, hipGetErrorString(err));
     moe_status rst = ring_release(R, wlines[w].data(), nl, s);
@@ -335,6 +344,40 @@ moe_status check_rows(int64_t T, const moe_shape& sh) {
 }
 
 }  // namespace
+
+moe_status prefill_chunk_checked(const moe_layer* layer, const void* x, const int32_t* ids,
+                                 const float* weights, int64_t T, int64_t t0, int64_t n,
+                                 const int32_t* counts_host, void* out, void* ws,
+                                 size_t ws_bytes, void* stream, void* copy_stream,
+                                 bool resident_only, void* (*ws_of_device)(moe_status*)) {
+  moe_status st = check_layer(layer);
+  if (st != MOE_OK) return st;
+  if ((st = check_rows(T, layer->shape)) != MOE_OK) return st;
+  if (t0 < 0 || n < 0 || t0 + n > T)
+    return set_error(MOE_ERR_INVALID, "rows [%lld, %lld) outside [0, %lld)",
+                     static_cast<long long>(t0), static_cast<long long>(t0 + n),
+                     static_cast<long long>(T));
+  bool offloaded = false;
+  if ((st = check_experts(layer, &offloaded)) != MOE_OK) return st;
+  if (offloaded && resident_only)
+    return set_error(MOE_ERR_UNSUPPORTED, "this entry point takes resident experts only");
+  if (ws_of_device) {                 // the workspace is the library's own array on this device
+    WsLayout W;
+    ws_layout(layer->shape, n, &W);
+    if (W.total > ws_bytes)
+      return set_error(MOE_ERR_WORKSPACE, "%lld rows need %zu bytes of workspace, %zu available",
+                       static_cast<long long>(n), W.total, ws_bytes);
+  }
+  if (n == 0) return MOE_OK;
+  if (ws_of_device && !(ws = ws_of_device(&st))) return st;
+  if (!x || !ids || !weights || !out || !ws)
+    return set_error(MOE_ERR_INVALID, "NULL tensor argument");
+  if (!aligned(x, 16) || !aligned(out, 16) || !aligned(ids, 4) || !aligned(weights, 4) ||
+      !aligned(ws, 256))
+    return set_error(MOE_ERR_INVALID, "misaligned tensor argument (ws needs 256 bytes)");
+  return chunk_impl(layer, offloaded, x, ids, weights, t0, n, counts_host, out, ws, ws_bytes,
+                    static_cast<hipStream_t>(stream), static_cast<hipStream_t>(copy_stream));
+}
 
 bool ws_layout(const moe_shape& sh, int64_t max_n, WsLayout* L) {
   if (max_n < 1) max_n = 1;
@@ -441,24 +484,9 @@ moe_status moe_prefill_chunk(const moe_layer* layer, const void* x, const int32_
                              const int32_t* counts_host, void* out, void* ws, size_t ws_bytes,
                              void* stream, void* copy_stream) {
   moe::clear_error();
-  moe_status st = moe::check_layer(layer);
-  if (st != MOE_OK) return st;
-  if ((st = moe::check_rows(T, layer->shape)) != MOE_OK) return st;
-  if (t0 < 0 || n < 0 || t0 + n > T)
-    return set_error(MOE_ERR_INVALID, "rows [%lld, %lld) outside [0, %lld)",
-                     static_cast<long long>(t0), static_cast<long long>(t0 + n),
-                     static_cast<long long>(T));
-  bool offloaded = false;
-  if ((st = moe::check_experts(layer, &offloaded)) != MOE_OK) return st;
-  if (n == 0) return MOE_OK;
-  if (!x || !ids || !weights || !out || !ws)
-    return set_error(MOE_ERR_INVALID, "NULL tensor argument");
-  if (!moe::aligned(x, 16) || !moe::aligned(out, 16) || !moe::aligned(ids, 4) ||
-      !moe::aligned(weights, 4) || !moe::aligned(ws, 256))
-    return set_error(MOE_ERR_INVALID, "misaligned tensor argument (ws needs 256 bytes)");
-  return moe::chunk_impl(layer, offloaded, x, ids, weights, t0, n, counts_host, out, ws,
-                         ws_bytes, static_cast<hipStream_t>(stream),
-                         static_cast<hipStream_t>(copy_stream));
+  return moe::prefill_chunk_checked(layer, x, ids, weights, T, t0, n, counts_host, out, ws,
+                                    ws_bytes, stream, copy_stream, /*resident_only=*/false,
+                                    nullptr);
 }
 
 moe_status moe_prefill_layer(const moe_layer* layer, const void* x, int64_t T, int64_t chunk,

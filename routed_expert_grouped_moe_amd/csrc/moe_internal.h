@@ -30,6 +30,17 @@ struct WsLayout {
 };
 MOE_HIDDEN bool ws_layout(const moe_shape& sh, int64_t max_n, WsLayout* out);
 
+// moe_prefill_chunk after its argument checks. resident_only: a layer with offloaded experts is
+// MOE_ERR_UNSUPPORTED. ws_of_device: when given, the workspace is ws_bytes of library-owned
+// device memory whose address this returns for the current device (NULL with *status set on
+// failure); it is asked for only after every argument check has passed.
+MOE_HIDDEN moe_status prefill_chunk_checked(const moe_layer* layer, const void* x,
+                                            const int32_t* ids, const float* weights, int64_t T,
+                                            int64_t t0, int64_t n, const int32_t* counts_host,
+                                            void* out, void* ws, size_t ws_bytes, void* stream,
+                                            void* copy_stream, bool resident_only,
+                                            void* (*ws_of_device)(moe_status*));
+
 // meta words in the workspace
 enum { kMetaMTiles = 0, kMetaRows = 1, kMetaWords = 64 };
 

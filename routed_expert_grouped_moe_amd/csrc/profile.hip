@@ -23,6 +23,11 @@ int64_t g_n[16];
 double g_clk[16], g_rt[16];                        // summed clock samples read back so far
 std::unordered_map<int, unsigned long long*> g_clk_dev;   // per device: [16][2] counters
 
+// The clock counters live in a device array of the library's own code object (each device
+// holds its own copy), so profiling allocates no device memory. In host code the array's name
+// is only a stand-in: its device address comes from hipGetSymbolAddress, once per device.
+__device__ __align__(256) unsigned long long g_clk_counters[16 * 2];
+
 hipEvent_t take_event() {   // caller holds g_mu
   if (!g_pool.empty()) {
     hipEvent_t e = g_pool.back();
@@ -43,15 +48,10 @@ unsigned long long* prof_clock(int stage) {
   if (hipGetDevice(&dev) != hipSuccess) return nullptr;
   unsigned long long*& buf = g_clk_dev[dev];
   if (!buf) {
-    if (hipMalloc(&buf, 16 * 2 * sizeof(unsigned long long)) != hipSuccess) {
-      buf = nullptr;
-      return nullptr;
-    }
-    if (hipMemset(buf, 0, 16 * 2 * sizeof(unsigned long long)) != hipSuccess) {
-      (void)hipFree(buf);
-      buf = nullptr;
-      return nullptr;
-    }
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_clk_counters)) != hipSuccess || !p) return nullptr;
+    if (hipMemset(p, 0, 16 * 2 * sizeof(unsigned long long)) != hipSuccess) return nullptr;
+    buf = static_cast<unsigned long long*>(p);
   }
   return buf + 2 * stage;
 }

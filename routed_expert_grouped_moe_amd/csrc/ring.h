@@ -60,10 +60,14 @@ inline int64_t ring_key(int32_t layer, int32_t expert) {
 // pass will ask for. A miss then evicts, least recently used first, a line that holds none of
 // them when there is one (a near-Belady choice for the known rest of the pass), else the least
 // recently used line.
+// kind: MOE_COPY_* category the staging's requested and copied bytes are counted under.
+// hold: the lines stay held until ring_release (else each miss's release is recorded on its
+// copy stream right behind the copy, and no line stays held).
 MOE_HIDDEN moe_status ring_stage(moe_ring* r, int32_t layer, const int32_t* experts, int32_t n,
                                  hipStream_t copy_stream, int32_t* lines_out,
                                  const std::vector<char>* later = nullptr,
-                                 bool two_streams = false);
+                                 bool two_streams = false, int kind = MOE_COPY_DEMAND,
+                                 bool hold = true);
 MOE_HIDDEN moe_status ring_wait_ready(moe_ring* r, const int32_t* lines, int32_t n,
                                       hipStream_t stream);
 MOE_HIDDEN moe_status ring_release(moe_ring* r, const int32_t* lines, int32_t n,

@@ -38,7 +38,8 @@ void clear_error() { g_last_error.clear(); }
 
 moe_status ring_stage(moe_ring* r, int32_t layer, const int32_t* experts, int32_t n,
                       hipStream_t cs0, int32_t* lines_out, const std::vector<char>* later,
-                      bool two_streams) {
+                      bool two_streams, int kind, bool hold) {
+  if (kind < 0 || kind >= MOE_COPY_KINDS) kind = MOE_COPY_DEMAND;
   auto bit = r->banks.find(layer);
   if (bit == r->banks.end())
     return set_error(MOE_ERR_RING, "no bank bound for layer %d", layer);
@@ -82,9 +83,10 @@ moe_status ring_stage(moe_ring* r, int32_t layer, const int32_t* experts, int32_
   for (int i = 0; i < n; ++i) {            // hits first: they must not be chosen as victims
     if (hit_line[i] < 0) continue;
     moe_ring::Line& ln = r->line[hit_line[i]];
-    ln.held = true;
+    if (hold) ln.held = true;
     ln.last_use = ++r->clock;
     r->stats.hits++;
+    r->stats.requested_bytes[kind] += static_cast<int64_t>(r->line_bytes);
     if (lines_out) lines_out[i] = hit_line[i];
   }
   // Misses in three passes: choose every victim, then make each copy stream wait once per
@@ -116,8 +118,9 @@ moe_status ring_stage(moe_ring* r, int32_t layer, const int32_t* experts, int32_
   // On a HIP error nothing this call took stays held: hit lines and filled victims keep their
   // (valid) contents, victims not yet filled stay empty.
   auto unwind = [&](size_t) {
-    for (int i = 0; i < n; ++i)
-      if (hit_line[i] >= 0) r->line[hit_line[i]].held = false;
+    if (hold)
+      for (int i = 0; i < n; ++i)
+        if (hit_line[i] >= 0) r->line[hit_line[i]].held = false;
     for (const Planned& pl : plan) r->line[pl.victim].held = false;
   };
   for (int sj = 0; sj < 2; ++sj) {
@@ -160,6 +163,8 @@ moe_status ring_stage(moe_ring* r, int32_t layer, const int32_t* experts, int32_
     char* dst = r->lines + static_cast<size_t>(pl.victim) * r->line_bytes;
     hipError_t err = hipMemcpyAsync(dst, src, r->line_bytes, hipMemcpyHostToDevice, cs);
     if (err == hipSuccess) err = hipEventRecord(r->ready[pl.victim], cs);
+    // not held: the copy stream itself is the line's last reader so far
+    if (err == hipSuccess && !hold) err = hipEventRecord(r->release[pl.victim], cs);
     if (err != hipSuccess) {
       unwind(q);
       return set_error(MOE_ERR_HIP, "copy into line %d: %s", pl.victim, hipGetErrorString(err));
@@ -169,9 +174,17 @@ moe_status ring_stage(moe_ring* r, int32_t layer, const int32_t* experts, int32_
     ln.layer = layer;
     ln.expert = e;
     ln.last_use = ++r->clock;
+    if (!hold) {
+      ln.held = false;
+      ln.has_release = true;
+      ln.release_seq = ++r->release_counter;
+      ln.release_stream = cs;
+    }
     r->where[ring_key(layer, e)] = pl.victim;
     r->stats.misses++;
     r->stats.bytes_h2d += static_cast<int64_t>(r->line_bytes);
+    r->stats.requested_bytes[kind] += static_cast<int64_t>(r->line_bytes);
+    r->stats.copied_bytes[kind] += static_cast<int64_t>(r->line_bytes);
     if (lines_out) lines_out[pl.i] = pl.victim;
   }
   return MOE_OK;
@@ -193,10 +206,17 @@ moe_status ring_release(moe_ring* r, const int32_t* lines, int32_t n, hipStream_
   for (int i = 0; i < n; ++i) {
     const int l = lines[i];
     if (l < 0 || l >= r->n_lines) return set_error(MOE_ERR_INVALID, "line %d out of range", l);
-    hipError_t err = hipEventRecord(r->release[l], s);
-    if (err != hipSuccess)
-      return set_error(MOE_ERR_HIP, "hipEventRecord(release): %s", hipGetErrorString(err));
     moe_ring::Line& ln = r->line[l];
+    // The line's last release may be on another stream (an earlier reader released it there,
+    // then a staging found it as a hit and handed it to this stream): the one release event
+    // must cover both readers, so this stream first waits for the earlier release.
+    hipError_t err = hipSuccess;
+#if !defined(MOE_PLANT_RELEASE_ONE_STREAM)   // test-only build of the host check: no such wait
+    if (ln.has_release && ln.release_stream != s) err = hipStreamWaitEvent(s, r->release[l], 0);
+#endif
+    if (err == hipSuccess) err = hipEventRecord(r->release[l], s);
+    if (err != hipSuccess)
+      return set_error(MOE_ERR_HIP, "release of line %d: %s", l, hipGetErrorString(err));
     ln.has_release = true;
     ln.release_seq = ++r->release_counter;
     ln.release_stream = s;
@@ -253,7 +273,7 @@ moe_status moe_ring_create(const moe_shape* shape, void* device_lines, int32_t n
     delete r;
     return set_error(MOE_ERR_HIP, "hipEventCreateWithFlags: %s", hipGetErrorString(err));
   }
-  r->stats.version = 1;
+  r->stats.version = 2;
   r->stats.n_lines = n_lines;
   *out = r;
   return MOE_OK;
@@ -296,6 +316,14 @@ moe_status moe_stage_experts(moe_ring* r, int32_t layer_id, const int32_t* exper
                          lines_out);
 }
 
+moe_status moe_ring_prefetch(moe_ring* r, int32_t layer_id, const int32_t* experts, int32_t n,
+                             void* copy_stream) {
+  moe::clear_error();
+  if (!r || (n > 0 && !experts) || n < 0) return set_error(MOE_ERR_INVALID, "bad arguments");
+  return moe::ring_stage(r, layer_id, experts, n, static_cast<hipStream_t>(copy_stream),
+                         nullptr, nullptr, false, MOE_COPY_CROSS_LAYER, /*hold=*/false);
+}
+
 moe_status moe_ring_wait_ready(moe_ring* r, const int32_t* lines, int32_t n, void* stream) {
   moe::clear_error();
   if (!r || (n > 0 && !lines) || n < 0) return set_error(MOE_ERR_INVALID, "bad arguments");
@@ -325,7 +353,7 @@ moe_status moe_ring_reset_stats(moe_ring* r) {
   if (!r) return set_error(MOE_ERR_INVALID, "ring is NULL");
   const int32_t nl = r->stats.n_lines;
   r->stats = moe_ring_stats_t{};
-  r->stats.version = 1;
+  r->stats.version = 2;
   r->stats.n_lines = nl;
   return MOE_OK;
 }

@@ -21,6 +21,9 @@ class RingModel:
         self.sweeps = 0
         self.hits = 0
         self.misses = 0
+        self.copied = [0, 0, 0, 0]          # misses by kind: initial, ahead, demand, cross-layer
+        self.requested = [0, 0, 0, 0]
+        self.log = []                       # ("stage", kind, experts, later) / ("release", experts)
 
     def _stage(self, layer, experts, later):
         where = {k: i for i, k in enumerate(self.expert) if k is not None}
@@ -78,11 +81,29 @@ class RingModel:
             while staged < nw and staged <= i + 1:
                 w = order[staged]
                 later -= set(waves[w])
+                kind = 0 if staged == 0 else (1 if staged > i else 2)
+                m0 = self.misses
                 got = self._stage(layer, waves[w], later)
+                self.log.append(("stage", kind, list(waves[w]), sorted(later)))
                 if got is None and staged > i:
                     break
                 assert got is not None, "the model ran out of lines for the current wave"
+                self.copied[kind] += self.misses - m0
+                self.requested[kind] += len(waves[w])
                 lines[w] = got
                 staged += 1
             for l in lines[order[i]]:
                 self.held[l] = False
+            self.log.append(("release", list(waves[order[i]])))
+
+    def write_log(self, path: str, n_experts: int):
+        """The staging and release sequence in the host check's replay format."""
+        with open(path, "w") as f:
+            f.write(f"ring {self.n} {n_experts}\n")
+            for op in self.log:
+                if op[0] == "stage":
+                    _, kind, ex, later = op
+                    f.write(f"stage {kind} {len(ex)} {' '.join(map(str, ex))} "
+                            f"later {len(later)} {' '.join(map(str, later))}\n")
+                else:
+                    f.write(f"release {len(op[1])} {' '.join(map(str, op[1]))}\n")

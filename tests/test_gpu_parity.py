@@ -85,15 +85,30 @@ def test_edge_shapes(moe, case):
     _full_parity(moe, wl, BF16_TOL, chunks=chunks)
 
 
+def _stage_parity(moe, wl):
+    """Element-wise stage parity of the batched pass (tests/stage_checks.py): h, Y and out
+    of every expert and token against the oracle's stages within derived bounds. Used where
+    the whole-tensor max-abs/RMS metric is dominated by the bf16 roundings themselves (few
+    terms per output, skewed routing): an ideal bf16 pipeline scores 1.5e-2 to 2.8e-2 on
+    such shapes, so that metric cannot tell a right kernel from a slightly wrong one."""
+    from tests import test_gpu_stages as st
+    params = mi.make_layer(wl, device="cuda")
+    x = mi.make_x(wl, device="cuda")
+    c = st.Chunk(moe, wl, params, x, 0, wl.T)
+    op = oracle_params(params, wl)
+    stats = st._new_stats()
+    st._check_routed(c, op, range(wl.shape.n_experts), stats)
+    st._check_out(c, op, np.arange(wl.T), stats)
+    st._report(wl.name, stats)
+
+
 def test_big_tiles_with_partial_tiles(moe):
     """A chunk averaging at least 128 rows per expert takes 256-row M-tiles; an expert's
     remainder gets one more, partly filled tile. The seeded routing hits the cases (experts
     with fewer than 64 rows, small remainders after full tiles, several full tiles plus a
-    large partial one). Oracle parity, and the bytes equal those of the all-64-row tiling that a
-    100-token chunk takes. (At this size the max-abs/RMS metric is crest-sensitive: rounding
-    the exact output once to bf16 already scores 1.15e-2 here, and 2.1e-2 -- above the bar --
-    for the same routing at d = 128, so the layer is taken at d = 256.)"""
-    wl = mi.custom_workload("tails", T=2000, d=256, E=16, k=4, inter=128, inter_shared=256,
+    large partial one). Element-wise stage parity with the oracle, and the bytes equal those
+    of the all-64-row tiling that a 100-token chunk takes."""
+    wl = mi.custom_workload("tails", T=2000, d=128, E=16, k=4, inter=128, inter_shared=256,
                             zipf_s=1.1, seed=15)
     params, L = place(wl)
     x = mi.make_x(wl, device="cuda")
@@ -104,16 +119,24 @@ def test_big_tiles_with_partial_tiles(moe):
     rem = c % 256
     assert ((c > 0) & (c <= 64)).any()
     assert ((c > 256) & (rem > 0) & (rem <= 64)).any() and ((c > 512) & (rem > 64)).any()
-    _full_parity(moe, wl, BF16_TOL, chunks=(100, wl.T))
+    _chunks_identical(moe, wl, (100, wl.T))
+    _stage_parity(moe, wl)
+
+
+def _chunks_identical(moe, wl, chunks):
+    params, L = place(wl)
+    x = mi.make_x(wl, device="cuda")
+    outs = [_run(moe, L, x, c)["out"].clone() for c in chunks]
+    for c, o in zip(chunks[1:], outs[1:]):
+        assert torch.equal(bits(o), bits(outs[0])), f"chunk {c} against chunk {chunks[0]}"
 
 
 def test_tall_tiles(moe):
     """A chunk averaging 192 to 320 rows per expert takes 320-row M-tiles (8 waves of 80 x 128):
     an expert of 257..320 rows fits one tile. The seeded routing has experts above 320 rows
     (several tiles), of 257..320 rows, of about 200 rows (the last wave slab idle) and under
-    80 rows. Oracle parity, and the bytes equal those of the 64-row tiling of a 100-token
-    chunk. (Seed chosen for headroom under the 2e-2 bar: with this skew and d = 256, the bf16
-    roundings of h and of the output alone cost 1.6e-2 to 2.1e-2 depending on the seed.)"""
+    80 rows (the seed is one whose routing covers all four cases). Element-wise stage parity
+    with the oracle, and the bytes equal those of the 64-row tiling of a 100-token chunk."""
     wl = mi.custom_workload("tall", T=1000, d=256, E=16, k=4, inter=128, inter_shared=256,
                             zipf_s=1.1, seed=32)
     params, L = place(wl)
@@ -124,7 +147,8 @@ def test_tall_tiles(moe):
     rows, E = wl.T * wl.shape.top_k, wl.shape.n_experts
     assert 192 * E <= rows < 320 * E                               # 320-row tiling
     assert (c > 320).any() and ((c > 256) & (c <= 320)).any() and ((c > 0) & (c < 80)).any()
-    _full_parity(moe, wl, BF16_TOL, chunks=(100, wl.T))
+    _chunks_identical(moe, wl, (100, wl.T))
+    _stage_parity(moe, wl)
 
 
 def test_topk_ties_and_special_values(moe):

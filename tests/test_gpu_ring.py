@@ -217,3 +217,168 @@ def test_offload_16022_ring64(moe):
     print(f"[ring] sampled rel err {err:.3e}")
     assert err <= 2e-2
     ring.close()
+
+
+def test_copy_categories_match_the_model(moe):
+    """The ring's requested and copied bytes by kind of staging (a chunk's first wave, a wave
+    staged ahead, a wave staged on demand) equal the host model's counts, and reconcile with
+    the totals."""
+    from tests.ring_model import RingModel
+    wl = mi.custom_workload("kinds", T=600, d=64, E=24, k=4, inter=64, inter_shared=0, seed=12)
+    params, L_res = place(wl)
+    x = mi.make_x(wl, device="cuda")
+    for n_lines in (8, 3):
+        ring = moe.Ring(L_res.shape, n_lines)
+        _, L = place(wl, offloaded=range(24), ring=ring, params=params)
+        got = moe.moe_prefill_layer(L, x, 100, copy_stream=torch.cuda.Stream())
+        torch.cuda.synchronize()
+        st = ring.stats()
+        model = RingModel(n_lines)
+        for row in got["chunk_counts"].cpu().numpy():
+            model.chunk(0, [int(e) for e in np.nonzero(row)[0]])
+        lb = ring.line_bytes
+        kinds = ["initial", "ahead", "demand", "cross_layer"]
+        print(f"[ring] kinds, {n_lines} lines: copied {[st['copied_bytes'][k] // lb for k in kinds]}"
+              f" model {model.copied}", flush=True)
+        assert [st["copied_bytes"][k] for k in kinds] == [c * lb for c in model.copied]
+        assert [st["requested_bytes"][k] for k in kinds] == [c * lb for c in model.requested]
+        assert sum(st["copied_bytes"].values()) == st["bytes_h2d"]
+        assert sum(st["requested_bytes"].values()) == (st["hits"] + st["misses"]) * lb
+        ring.close()
+
+
+def test_prefetch_stages_without_holding(moe):
+    """moe_ring_prefetch copies experts of a later layer into free lines without holding them:
+    the layer's own staging then finds them as hits, the bytes count as cross-layer copies, and
+    the output equals the all-resident layer bit for bit."""
+    wl = mi.custom_workload("prefetch", T=64, d=128, E=16, k=2, inter=64, inter_shared=64,
+                            seed=6)
+    params, L_res = place(wl)
+    x = mi.make_x(wl, device="cuda")
+    ref = moe.moe_prefill_layer(L_res, x, 64)
+    torch.cuda.synchronize()
+    used = [int(e) for e in np.nonzero(ref["chunk_counts"][0].cpu().numpy())[0]]
+    ring = moe.Ring(L_res.shape, 16)
+    _, L = place(wl, offloaded=range(16), ring=ring, params=params, layer=3)
+    cs = torch.cuda.Stream()
+    ring.prefetch(3, used[:4], copy_stream=cs)
+    st0 = ring.stats()
+    assert st0["copied_bytes"]["cross_layer"] == 4 * ring.line_bytes and st0["misses"] == 4
+    lines = moe.moe_stage_experts(ring, 3, used[4:], copy_stream=cs)   # nothing left held
+    ring.release(lines)
+    got = moe.moe_prefill_layer(L, x, 64, copy_stream=cs)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(got["out"]), bits(ref["out"]))
+    st = ring.stats()
+    assert st["hits"] - st0["hits"] == len(used)
+    with pytest.raises(moe.MoeError, match="MOE_ERR_INVALID"):
+        ring.prefetch(3, [1, 1], copy_stream=cs)
+    ring.close()
+
+
+def test_release_on_a_second_stream_covers_the_first_reader(moe):
+    """A line read on stream A and released there, then found as a hit and released on stream
+    B, is refilled only after A's read: the line's one release event covers both streams. A
+    bounded spin on A before its read keeps A's read late."""
+    wl = mi.custom_workload("rel2", T=8, d=256, E=4, k=1, inter=64, inter_shared=0, seed=5)
+    params, L_res = place(wl)
+    ring = moe.Ring(L_res.shape, 1)
+    place(wl, offloaded=range(4), ring=ring, params=params)
+    view = ring.lines.view(torch.bfloat16)
+    want = params["lines"][0].float().sum()
+    cs, A, B = torch.cuda.Stream(), torch.cuda.Stream(), torch.cuda.Stream()
+    torch.cuda.synchronize()
+    l0 = moe.moe_stage_experts(ring, 0, [0], copy_stream=cs)
+    ring.wait_ready(l0, stream=A)
+    with torch.cuda.stream(A):
+        torch.cuda._sleep(20_000_000)
+        got = view.float().sum()
+    ring.release(l0, stream=A)
+    l1 = moe.moe_stage_experts(ring, 0, [0], copy_stream=cs)      # a hit
+    assert l1 == l0
+    ring.wait_ready(l1, stream=B)
+    ring.release(l1, stream=B)
+    l2 = moe.moe_stage_experts(ring, 0, [1], copy_stream=cs)      # refills the line
+    ring.wait_ready(l2, stream=A)
+    ring.release(l2, stream=A)
+    torch.cuda.synchronize()
+    assert torch.equal(got, want)
+    assert torch.equal(view, params["lines"][1])
+    ring.close()
+
+
+_SERIAL_CHILD = r"""
+import sys
+import numpy as np, torch
+sys.path.insert(0, sys.argv[1])
+import moe_inputs as mi
+import routed_expert_grouped_moe_amd as moe
+from tests.parity import place
+wl = mi.custom_workload("ring", T=300, d=128, E=32, k=4, inter=64, inter_shared=128,
+                        zipf_s=1.1, seed=21)
+params, L_res = place(wl)
+ring = moe.Ring(L_res.shape, 4)
+_, L = place(wl, offloaded=range(32), ring=ring, params=params)
+x = mi.make_x(wl, device="cuda")
+out = moe.moe_prefill_layer(L, x, 64, copy_stream=torch.cuda.Stream())["out"]
+torch.cuda.synchronize()
+np.save(sys.argv[2], out.view(torch.int16).cpu().numpy())
+ring.close()
+print("saved")
+"""
+
+
+def test_serialized_run_equals_async(moe, tmp_path):
+    """The ring layer with every kernel and copy serialised by the runtime
+    (AMD_SERIALIZE_KERNEL=3, AMD_SERIALIZE_COPY=3, in a child process) gives the bytes of the
+    asynchronous run."""
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    outs = {}
+    for mode, extra in (("async", {}), ("serial", {"AMD_SERIALIZE_KERNEL": "3",
+                                                   "AMD_SERIALIZE_COPY": "3"})):
+        path = str(tmp_path / f"{mode}.npy")
+        env = dict(os.environ, **extra)
+        print(f"[ring] {mode} child", flush=True)
+        r = subprocess.run([sys.executable, "-c", _SERIAL_CHILD, root, path], env=env,
+                           capture_output=True, text=True, timeout=180, cwd=root)
+        assert "saved" in r.stdout, (mode, r.stdout[-1000:], r.stderr[-2000:])
+        outs[mode] = np.load(path)
+    assert np.array_equal(outs["async"], outs["serial"])
+
+
+def test_wrong_counts_host_stay_in_bounds(moe):
+    """Caller counts that sum to n*k but differ from the chunk's own plan the waves wrongly:
+    the call completes (its rows are unspecified), nothing outside the caller's tensors, the
+    workspace and the ring is touched, no line stays held, and the next call with the right
+    counts gives the all-resident bytes."""
+    wl = mi.custom_workload("badcounts", T=300, d=128, E=32, k=4, inter=64, inter_shared=128,
+                            zipf_s=1.1, seed=21)
+    params, L_res = place(wl)
+    x = mi.make_x(wl, device="cuda")
+    ref = moe.moe_prefill_layer(L_res, x, 300)
+    ring = moe.Ring(L_res.shape, 8)
+    _, L = place(wl, offloaded=range(32), ring=ring, params=params)
+    r = moe.moe_prefill_route(L, x, 300)
+    torch.cuda.synchronize()
+    counts = r["chunk_counts"][0].cpu().numpy().astype(np.int64)
+    bad = counts.copy()
+    i = int(np.argmax(counts))
+    j = int(np.argmin(np.where(counts > 0, counts, 1 << 30)))
+    bad[i] -= 60
+    bad[j] += 60
+    assert bad.min() >= 0 and bad.sum() == counts.sum()
+    ws = torch.empty(moe.moe_workspace_bytes(L.shape, 300), dtype=torch.uint8, device="cuda")
+    sentinel = torch.full((4, 128), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = torch.zeros_like(x)
+    cs = torch.cuda.Stream()
+    moe.moe_prefill_chunk(L, x, r["ids"], r["weights"], 0, 300, out, ws,
+                          counts_host=bad.tolist(), copy_stream=cs)
+    torch.cuda.synchronize()
+    assert torch.all(sentinel == 7.0)
+    lines = moe.moe_stage_experts(ring, 0, list(range(8)), copy_stream=cs)   # every line free
+    ring.release(lines)
+    moe.moe_prefill_chunk(L, x, r["ids"], r["weights"], 0, 300, out, ws,
+                          counts_host=counts.tolist(), copy_stream=cs)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(out), bits(ref["out"]))
+    ring.close()

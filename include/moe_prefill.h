@@ -180,6 +180,21 @@ moe_status moe_prefill_chunk(const moe_layer* layer, const void* x, const int32_
                              const int32_t* counts_host, void* out, void* ws, size_t ws_bytes,
                              void* stream, void* copy_stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, serving loops
+ * and harnesses that forbid hipMalloc): moe_prefill_chunk with a workspace the library holds
+ * itself in place of the caller's. Each device the call runs on holds
+ * moe_noalloc_workspace_bytes() (128 MiB) of library device memory from the first call there
+ * until the process ends; the call itself allocates nothing. Every expert must be resident (a
+ * layer with offloaded experts is MOE_ERR_UNSUPPORTED); rows needing more workspace than that
+ * (moe_workspace_bytes(shape, n) above it: about 1,700 rows at d = 2,048, E = 512, k = 8,
+ * I = 512, I_s = 2,048) are MOE_ERR_WORKSPACE, with nothing enqueued. Calls that overlap on one
+ * device share that memory and race: one call at a time per device. Results are the bytes
+ * moe_prefill_chunk gives. Other arguments as moe_prefill_chunk. */
+size_t moe_noalloc_workspace_bytes(void);
+moe_status moe_prefill_chunk_noalloc(const moe_layer* layer, const void* x, const int32_t* ids,
+                                     const float* weights, int64_t T, int64_t t0, int64_t n,
+                                     void* out, void* stream);
+
 /* Whole-prompt convenience: route, then moe_prefill_chunk over [c*chunk, min((c+1)*chunk, T))
  * for every chunk in order. With a ring, the per-chunk counts come from one device-to-host copy
  * of chunk_counts (one synchronisation per call). Arguments as in the two calls above;

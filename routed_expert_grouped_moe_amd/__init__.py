@@ -276,6 +276,26 @@ def moe_prefill_chunk(layer: Layer, x, ids, weights, t0: int, n: int, out, works
           "moe_prefill_chunk")
 
 
+def moe_noalloc_workspace_bytes() -> int:
+    return int(lib().moe_noalloc_workspace_bytes())
+
+
+def moe_prefill_chunk_noalloc(layer: Layer, x, ids, weights, t0: int, n: int, out,
+                              stream=None) -> None:
+    """moe_prefill_chunk with the library's own per-device workspace (see the header):
+    resident experts only; allocates nothing."""
+    sh = layer.shape
+    T = x.shape[0]
+    dt = _torch_dtype(sh.dtype)
+    _need(x, "x", dt, (T, sh.d))
+    _need(out, "out", dt, (T, sh.d))
+    _need(ids, "ids", torch.int32, (T, sh.top_k))
+    _need(weights, "weights", torch.float32, (T, sh.top_k))
+    check(lib().moe_prefill_chunk_noalloc(ctypes.byref(layer.c), _vp(x), _vp(ids), _vp(weights),
+                                          T, int(t0), int(n), _vp(out), _stream(stream)),
+          "moe_prefill_chunk_noalloc")
+
+
 def layer_buffers(layer: Layer, T: int, chunk: int, device="cuda") -> dict:
     """Output, routing and workspace tensors for moe_prefill_layer over T tokens."""
     sh = layer.shape

@@ -62,6 +62,9 @@ SIGNATURES = {
                                   c_vp, c_vp, c_vp]),
     "moe_prefill_chunk": (c_i32, [ctypes.POINTER(MoeLayer), c_vp, c_vp, c_vp, c_i64, c_i64,
                                   c_i64, c_vp, c_vp, c_vp, c_sz, c_vp, c_vp]),
+    "moe_noalloc_workspace_bytes": (c_sz, []),
+    "moe_prefill_chunk_noalloc": (c_i32, [ctypes.POINTER(MoeLayer), c_vp, c_vp, c_vp, c_i64,
+                                          c_i64, c_i64, c_vp, c_vp]),
     "moe_prefill_layer": (c_i32, [ctypes.POINTER(MoeLayer), c_vp, c_i64, c_i64, c_vp, c_vp,
                                   c_vp, c_vp, c_vp, c_vp, c_sz, c_vp, c_vp]),
     "moe_ring_create": (c_i32, [ctypes.POINTER(MoeShape), c_vp, c_i32, ctypes.POINTER(c_vp)]),

@@ -16,6 +16,11 @@ struct moe_ring {
     bool has_release = false;     // `release` has been recorded at least once
     uint64_t release_seq = 0;     // release epoch (per ring, increasing in record order)
     hipStream_t release_stream = nullptr;
+    // A stream that has waited for the line's latest fill (its `ready`), or NULL. A release
+    // recorded on another stream first waits for that fill, so that a later copy into the
+    // line, which waits only for the release, cannot overtake the fill.
+    hipStream_t ready_seen = nullptr;
+    bool ready_seen_valid = false;
   };
   struct Bank {
     const char* base = nullptr;

@@ -171,6 +171,7 @@ moe_status ring_stage(moe_ring* r, int32_t layer, const int32_t* experts, int32_
     }
     moe_ring::Line& ln = r->line[pl.victim];
     ln.has_ready = true;
+    ln.ready_seen_valid = false;           // a new fill: no stream has waited for it yet
     ln.layer = layer;
     ln.expert = e;
     ln.last_use = ++r->clock;
@@ -179,6 +180,8 @@ moe_status ring_stage(moe_ring* r, int32_t layer, const int32_t* experts, int32_
       ln.has_release = true;
       ln.release_seq = ++r->release_counter;
       ln.release_stream = cs;
+      ln.ready_seen = cs;                  // the copy stream is ordered after its own copy
+      ln.ready_seen_valid = true;
     }
     r->where[ring_key(layer, e)] = pl.victim;
     r->stats.misses++;
@@ -198,6 +201,8 @@ moe_status ring_wait_ready(moe_ring* r, const int32_t* lines, int32_t n, hipStre
     hipError_t err = hipStreamWaitEvent(s, r->ready[l], 0);
     if (err != hipSuccess)
       return set_error(MOE_ERR_HIP, "hipStreamWaitEvent(ready): %s", hipGetErrorString(err));
+    r->line[l].ready_seen = s;
+    r->line[l].ready_seen_valid = true;
   }
   return MOE_OK;
 }
@@ -213,6 +218,16 @@ moe_status ring_release(moe_ring* r, const int32_t* lines, int32_t n, hipStream_
     hipError_t err = hipSuccess;
 #if !defined(MOE_PLANT_RELEASE_ONE_STREAM)   // test-only build of the host check: no such wait
     if (ln.has_release && ln.release_stream != s) err = hipStreamWaitEvent(s, r->release[l], 0);
+#endif
+    // A holder that never waited for the line's fill on this stream (a staging released
+    // without moe_ring_wait_ready) must not release it before the fill lands: a later copy
+    // into the line waits only for the release.
+#if !defined(MOE_PLANT_RELEASE_BEFORE_FILL)  // test-only build of the host check: no such wait
+    if (err == hipSuccess && ln.has_ready && !(ln.ready_seen_valid && ln.ready_seen == s)) {
+      err = hipStreamWaitEvent(s, r->ready[l], 0);
+      ln.ready_seen = s;
+      ln.ready_seen_valid = true;
+    }
 #endif
     if (err == hipSuccess) err = hipEventRecord(r->release[l], s);
     if (err != hipSuccess)

@@ -5,14 +5,17 @@
 // happens after everything the stream already holds and everything any event it waited for
 // covered. Copies into ring lines (hipMemcpyAsync) and reads of ring lines (the driver's stand-in
 // for the GEMMs that read a staged expert between moe_ring_wait_ready and moe_ring_release) are
-// logged, and every read is checked:
-//   - the copy that last filled its line (in host order) brought the expert it expects, and
-//     happens before the read;
-//   - every later copy into the same line happens after the read (the copy waited for it).
+// logged, and checked:
+//   - the copy that last filled a read's line (in host order) brought the expert the read
+//     expects, and happens before the read;
+//   - every later copy into the same line happens after the read (the copy waited for it);
+//   - the copies into one line are ordered among themselves (a refill cannot overtake the
+//     fill before it).
 //
 // Modes (argv[1]):
-//   random <seed> <steps>     random stagings, reads on two compute streams, releases on either
-//                             stream (including a line read and released on one stream, then
+//   random <seed> <steps>     random stagings on two copy streams, reads on two compute
+//                             streams, releases on either stream (some without waiting for the
+//                             fill) (including a line read and released on one stream, then
 //                             found as a hit and released on the other), and prefetches
 //   two_streams               the fixed sequence of the last case
 //   model <file>              replay staging waves written by tests/ring_model.py through the
@@ -85,6 +88,12 @@ void fail(const char* what, const void* line, const Op& a, const Op& b) {
 void check_all() {
   for (auto& kv : g_ops) {
     const std::vector<Op>& ops = kv.second;
+    const Op* prev_copy = nullptr;           // copies into one line must be ordered
+    for (size_t i = 0; i < ops.size(); ++i) {
+      if (!ops[i].is_copy) continue;
+      if (prev_copy && !hb(*prev_copy, ops[i])) fail("copy not after the line's previous copy", kv.first, *prev_copy, ops[i]);
+      prev_copy = &ops[i];
+    }
     for (size_t i = 0; i < ops.size(); ++i) {
       if (ops[i].is_copy) continue;
       const Op& r = ops[i];
@@ -196,8 +205,9 @@ struct World {
 int run_random(unsigned seed, int steps) {
   World w(6, 14);
   std::mt19937 rng(seed);
-  hipStream_t copy_s, comp[2];
-  hipStreamCreateWithFlags(&copy_s, 0);
+  hipStream_t copy[2], comp[2];
+  hipStreamCreateWithFlags(&copy[0], 0);
+  hipStreamCreateWithFlags(&copy[1], 0);
   hipStreamCreateWithFlags(&comp[0], 0);
   hipStreamCreateWithFlags(&comp[1], 0);
   struct Held {
@@ -219,7 +229,7 @@ int run_random(unsigned seed, int steps) {
       if (ex.empty()) continue;
       std::vector<int32_t> out(ex.size());
       const moe_status st = moe_stage_experts(w.ring, 0, ex.data(), static_cast<int32_t>(ex.size()),
-                                              copy_s, out.data());
+                                              copy[rng() % 2], out.data());
       if (st == MOE_ERR_RING) continue;        // too few free lines: nothing changed
       if (st != MOE_OK) { fprintf(stderr, "stage: %s\n", moe::last_error_text()); return 2; }
       for (size_t i = 0; i < ex.size(); ++i) held.push_back({out[i], ex[i]});
@@ -228,9 +238,13 @@ int run_random(unsigned seed, int steps) {
       const size_t take = 1 + rng() % held.size();
       std::vector<int32_t> ls;
       for (size_t i = 0; i < take; ++i) ls.push_back(held[i].line);
-      if (moe_ring_wait_ready(w.ring, ls.data(), static_cast<int32_t>(ls.size()), s) != MOE_OK) return 2;
+      // some holders release without waiting for the fill, and then never read
+      const bool waits = rng() % 5 != 0;
+      if (waits &&
+          moe_ring_wait_ready(w.ring, ls.data(), static_cast<int32_t>(ls.size()), s) != MOE_OK)
+        return 2;
       for (size_t i = 0; i < take; ++i)
-        if (rng() % 4) w.read(s, held[i].line, held[i].expert);   // some holders never read
+        if (waits && rng() % 4) w.read(s, held[i].line, held[i].expert);   // some never read
       if (moe_ring_release(w.ring, ls.data(), static_cast<int32_t>(ls.size()), s) != MOE_OK) return 2;
       held.erase(held.begin(), held.begin() + static_cast<long>(take));
     } else {                                   // prefetch an expert that is not held
@@ -238,7 +252,7 @@ int run_random(unsigned seed, int steps) {
       bool dup = false;
       for (const Held& h : held) dup |= h.expert == e;
       if (dup) continue;
-      const moe_status st = moe_ring_prefetch(w.ring, 0, &e, 1, copy_s);
+      const moe_status st = moe_ring_prefetch(w.ring, 0, &e, 1, copy[rng() % 2]);
       if (st != MOE_OK && st != MOE_ERR_RING) { fprintf(stderr, "prefetch: %s\n", moe::last_error_text()); return 2; }
     }
   }

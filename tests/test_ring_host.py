@@ -4,7 +4,8 @@ streams and events with vector clocks (tests/ring_host/). Every read of a staged
 happen after the copy that brought its expert, and every later copy into the line after the
 read; random stagings, reads and releases on two compute streams, prefetches, the staging
 waves of the host ring model, and a planted build whose release covers only its own stream
-(which the check must catch)."""
+and one whose release does not wait for an unwaited fill (both of which
+the check must catch)."""
 import os
 import shutil
 import subprocess
@@ -39,7 +40,9 @@ def _build(tmp, name, defines=()):
 def exes(tmp_path_factory):
     tmp = str(tmp_path_factory.mktemp("ring_host"))
     return {"real": _build(tmp, "ring_check"),
-            "planted": _build(tmp, "ring_check_planted", ["MOE_PLANT_RELEASE_ONE_STREAM=1"])}
+            "planted": _build(tmp, "ring_check_planted", ["MOE_PLANT_RELEASE_ONE_STREAM=1"]),
+            "planted_fill": _build(tmp, "ring_check_planted_fill",
+                                   ["MOE_PLANT_RELEASE_BEFORE_FILL=1"])}
 
 
 def _run(exe, *args):
@@ -67,6 +70,18 @@ def test_release_on_a_second_stream_covers_the_first_reader(exes):
 def test_planted_build_fails_random_sequences(exes):
     bad = sum(_run(exes["planted"], "random", str(s), "3000").returncode == 1 for s in (1, 2, 3))
     assert bad >= 1
+
+
+def test_release_without_waiting_for_the_fill(exes):
+    """A holder may release a staged line without waiting for its copy; the release then waits
+    for the copy itself, so the next copy into the line cannot overtake it. A planted build
+    without that wait is caught: two copies into one line left unordered."""
+    for s in (1, 2, 3):
+        r = _run(exes["real"], "random", str(s), "3000")
+        assert r.returncode == 0, r.stdout[-3000:]
+    outs = [_run(exes["planted_fill"], "random", str(s), "3000") for s in (1, 2, 3)]
+    assert any(o.returncode == 1 and "copy not after the line's previous copy" in o.stdout
+               for o in outs), outs[0].stdout[-3000:]
 
 
 def test_model_waves_replay(exes, tmp_path):

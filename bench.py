@@ -55,6 +55,10 @@ def algorithmic(stage: str, T: int, sh, counts):
         # each prompt row is read once (its reads for its other k - 1 experts are re-reads,
         # not algorithmic bytes), the used experts' gate/up weights once, h written once
         return 2 * Ns * d * 2 * I, used * 2 * I * d * 2 + T * d * 2 + Ns * I * 2
+    if stage == "gu_mixed":                # both gate/up GEMMs in one launch; x read once
+        f1, b1 = algorithmic("gu_routed", T, sh, counts)
+        f2, b2 = algorithmic("gu_shared", T, sh, counts)
+        return f1 + f2, b1 + b2 - T * d * 2
     if stage == "down_routed":
         return 2 * Ns * I * d, used * d * I * 2 + Ns * I * 2 + Ns * d * 4
     if stage == "gu_shared":
@@ -396,7 +400,7 @@ def main():
         if prof3[stage][2] > 0:
             ent["clock_mhz"] = round(prof3[stage][2], 0)
         kernels[stage] = ent
-    gemm = [s for s in ("gu_routed", "down_routed", "gu_shared", "down_shared",
+    gemm = [s for s in ("gu_mixed", "gu_routed", "down_routed", "gu_shared", "down_shared",
                         "down_shared_combine") if prof[s][1] > 0]
     gemm_ms = sum(prof[s][0] for s in gemm) / args.steps
     # GEMM flops only (the fused combine's 2*k*d per token is not matrix work)

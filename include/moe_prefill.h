@@ -311,7 +311,9 @@ enum {
   MOE_STAGE_COMBINE = 11,    /* the combine alone: layers without a shared expert */
   MOE_STAGE_RMSNORM = 12,
   MOE_STAGE_DOWN_SHARED_COMBINE = 13, /* shared down GEMM with the combine in its epilogue */
-  MOE_STAGE_COUNT = 14
+  MOE_STAGE_GU_MIXED = 14,  /* shared and routed gate/up GEMMs in one launch (resident experts,
+                               tall or big routed tiles) */
+  MOE_STAGE_COUNT = 15
 };
 
 typedef struct {

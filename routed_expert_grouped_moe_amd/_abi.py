@@ -38,7 +38,8 @@ class MoeProfile(ctypes.Structure):
 
 
 STAGES = ["router", "topk", "chunk_counts", "table", "hist", "scan", "permute", "gu_shared",
-          "down_shared", "gu_routed", "down_routed", "combine", "rmsnorm", "down_shared_combine"]
+          "down_shared", "gu_routed", "down_routed", "combine", "rmsnorm", "down_shared_combine",
+          "gu_mixed"]
 
 
 COPY_KINDS = ["initial", "ahead", "demand", "cross_layer"]     # MOE_COPY_* order

@@ -293,7 +293,12 @@ moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const i
   // down GEMM runs last, with the combine folded into its epilogue.
   SideStream side;
   hipStream_t ss = offloaded ? nullptr : s;
-  if (sh.inter_shared) {
+  const int bm = routed_tile_rows(n, k, E);
+  // With every expert resident and tall or big routed tiles, the shared GU's units join the
+  // routed GU's launch (launch_gu_mixed), so the compute-bound shared tiles run beside the
+  // weight-streaming routed ones.
+  const bool mixed = !offloaded && sh.inter_shared && gu_mixed_supported(bm);
+  if (sh.inter_shared && !mixed) {
     if (offloaded) {
       MOE_HIP(side.fork(s));
       ss = side.stream;
@@ -307,7 +312,6 @@ moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const i
   int64_t stride = 0;
   const bool uniform = !offloaded && uniform_lines(L->expert_lines, E, &stride);
   if (!uniform) MOE_HIP(launch_upload_ptrs(wtab, L->expert_lines, 0, E, s));
-  const int bm = routed_tile_rows(n, k, E);
   MOE_HIP(launch_bucket(ids + t0 * k, n, k, E, bm, ws, W, s));
   float* y = reinterpret_cast<float*>(ws + W.y);
   if (!offloaded) {
@@ -317,8 +321,12 @@ moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const i
                  reinterpret_cast<const int32_t*>(ws + W.counts), wtab,
                  uniform ? static_cast<const char*>(L->expert_lines[0]) : nullptr, stride, 0,
                  static_cast<int>(n * k / bm + std::min<int64_t>(E, n * k)), bm};
-    MOE_HIP(launch_gu_routed(sh.dtype, x, t0, sh.d, sh.inter, g,
-                             reinterpret_cast<const int32_t*>(ws + W.row_tok), ws + W.h, s));
+    const int32_t* row_tok = reinterpret_cast<const int32_t*>(ws + W.row_tok);
+    if (mixed)
+      MOE_HIP(launch_gu_mixed(sh.dtype, x, t0, n, sh.d, sh.inter, sh.inter_shared,
+                              L->w_gu_shared, ws + W.h_shared, g, row_tok, ws + W.h, s));
+    else
+      MOE_HIP(launch_gu_routed(sh.dtype, x, t0, sh.d, sh.inter, g, row_tok, ws + W.h, s));
     MOE_HIP(launch_down_routed(sh.dtype, ws + W.h, sh.d, sh.inter, g,
                                reinterpret_cast<const int32_t*>(ws + W.row_slot), y, s));
   } else {

@@ -422,16 +422,52 @@ __device__ __forceinline__ const char* line_of(const GemmGroups& g, int e) {
                   : static_cast<const char*>(g.wtab[e]);
 }
 
+// Work units (M-tile x N-tile) of a gate/up launch: grouped units come from the device's
+// M-tile list, dense ones from the row count.
+template <class TL, bool kGrouped>
+__device__ __forceinline__ int gu_units(const GuParams& p) {
+  constexpr int HC = TL::BN / 2;
+  const int NT = (p.I + HC - 1) / HC;
+  const int m_tiles = kGrouped ? max(0, min(p.g.tile_cap, *p.g.n_mtiles - p.g.tile_lo))
+                               : static_cast<int>((p.n + TL::BM - 1) / TL::BM);
+  return m_tiles * NT;
+}
+
+template <typename T, class TL, bool kGrouped>
+__device__ __forceinline__ void gu_tile(const GuParams& p, int t, char* lds);
+
 template <typename T, class TL, bool kGrouped>
 __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(2)))
 void gu_kernel(GuParams p) {
   __shared__ __attribute__((aligned(1024))) char lds[TL::LDS];
+  int t;
+  if (!xcd_tile(gu_units<TL, kGrouped>(p), &t)) return;
+  gu_tile<T, TL, kGrouped>(p, t, lds);
+}
+
+// The shared expert's gate/up units and the routed ones in one launch (shared units first in
+// the unit sequence). Each XCD works through its contiguous slice of that sequence, so while
+// the slices of the routed units stream expert weights from HBM, others run the shared GEMM,
+// whose operands come from the caches: the two overlap on the chip instead of running one
+// after the other, and the shared units fill what would be the routed launch's partial last
+// round. Same tile, instruction and K order as the separate launches: the same bits.
+template <typename T, class TL>
+__global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(2)))
+void gu_mixed_kernel(GuParams shared, GuParams routed) {
+  __shared__ __attribute__((aligned(1024))) char lds[TL::LDS];
+  const int ns = gu_units<TL, false>(shared);
+  int t;
+  if (!xcd_tile(ns + gu_units<TL, true>(routed), &t)) return;
+  if (t < ns)
+    gu_tile<T, TL, false>(shared, t, lds);
+  else
+    gu_tile<T, TL, true>(routed, t - ns, lds);
+}
+
+template <typename T, class TL, bool kGrouped>
+__device__ __forceinline__ void gu_tile(const GuParams& p, int t, char* lds) {
   constexpr int HC = TL::BN / 2;                         // h columns per tile
   const int NT = (p.I + HC - 1) / HC;
-  const int m_tiles = kGrouped ? max(0, min(p.g.tile_cap, *p.g.n_mtiles - p.g.tile_lo))
-                               : static_cast<int>((p.n + TL::BM - 1) / TL::BM);
-  int t;
-  if (!xcd_tile(m_tiles * NT, &t)) return;
   ClockSample clock(p.clk);
   const int mi = t / NT;
   const int n0h = (t % NT) * HC;
@@ -819,6 +855,35 @@ hipError_t launch_gu_routed(int dtype, const void* x, int64_t t0, int d, int I,
   else if (g.tile_rows == MidTile::BM) gu_routed<MidTile>(dtype, p, g, I, s);
   else if (g.tile_rows == DecodeTile::BM) gu_routed<DecodeTile>(dtype, p, g, I, s);
   else gu_routed<SmallTile>(dtype, p, g, I, s);
+  return hipGetLastError();
+}
+
+template <class TL>
+static void gu_mixed(int dtype, const GuParams& ps, const GuParams& pr, hipStream_t s) {
+  constexpr int HC = TL::BN / 2;
+  const int64_t units = (ps.n + TL::BM - 1) / TL::BM * ((ps.I + HC - 1) / HC) +
+                        static_cast<int64_t>(pr.g.tile_cap) * ((pr.I + HC - 1) / HC);
+  const unsigned grid = xcd_grid(units);
+  if (dtype == MOE_BF16) gu_mixed_kernel<uint16_t, TL><<<grid, TL::NT, 0, s>>>(ps, pr);
+  else gu_mixed_kernel<float, TL><<<grid, TL::NT, 0, s>>>(ps, pr);
+}
+
+bool gu_mixed_supported(int tile_rows) {
+  return tile_rows == TallTile::BM || tile_rows == BigTile::BM;
+}
+
+hipError_t launch_gu_mixed(int dtype, const void* x, int64_t t0, int64_t n, int d, int I, int Is,
+                           const void* w_gu_shared, void* h_shared, const GemmGroups& g,
+                           const int32_t* row_tok, void* h, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  ProfScope prof(MOE_STAGE_GU_MIXED, s);
+  GuParams ps{}, pr{};
+  ps.x = x; ps.t0 = t0; ps.n = n; ps.d = d; ps.I = Is; ps.w = w_gu_shared; ps.h = h_shared;
+  ps.clk = prof_clock(MOE_STAGE_GU_MIXED);
+  pr.x = x; pr.t0 = t0; pr.n = 0; pr.d = d; pr.I = I; pr.w = nullptr; pr.g = g;
+  pr.row_tok = row_tok; pr.h = h; pr.clk = ps.clk;
+  if (g.tile_rows == TallTile::BM) gu_mixed<TallTile>(dtype, ps, pr, s);
+  else gu_mixed<BigTile>(dtype, ps, pr, s);
   return hipGetLastError();
 }
 

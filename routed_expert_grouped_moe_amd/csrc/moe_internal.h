@@ -88,6 +88,13 @@ MOE_HIDDEN hipError_t launch_gu_routed(int dtype, const void* x, int64_t t0, int
                                        hipStream_t s);
 MOE_HIDDEN hipError_t launch_gu_dense(int dtype, const void* x, int64_t t0, int64_t n, int d,
                                       int Is, const void* w_gu, void* h, hipStream_t s);
+// The shared expert's gate/up GEMM and the routed one in one launch (routed M-tiles of
+// tile_rows rows, for which gu_mixed_supported holds).
+MOE_HIDDEN bool gu_mixed_supported(int tile_rows);
+MOE_HIDDEN hipError_t launch_gu_mixed(int dtype, const void* x, int64_t t0, int64_t n, int d,
+                                      int I, int Is, const void* w_gu_shared, void* h_shared,
+                                      const GemmGroups& g, const int32_t* row_tok, void* h,
+                                      hipStream_t s);
 MOE_HIDDEN hipError_t launch_down_routed(int dtype, const void* h, int d, int I,
                                          const GemmGroups& g, const int32_t* row_slot,
                                          float* y, hipStream_t s);

@@ -194,8 +194,18 @@ moe_status ring_waves(const moe_layer* L, const void* x, int64_t t0, int64_t n,
   for (int e = 0; e < E; ++e) mt_begin[e + 1] = mt_begin[e] + mtiles_of(cnt[e], bm);
 
   std::vector<int32_t> used;
-  for (int e = 0; e < E; ++e)
+  bool all_offloaded = true;
+  for (int e = 0; e < E; ++e) {
+    all_offloaded &= L->expert_lines[e] == nullptr;
     if (!L->expert_lines[e] && cnt[e] > 0) used.push_back(e);
+  }
+  // Misses are copied by the library's copy kernel when every routed expert of the layer is
+  // offloaded: each wave's GEMMs then cover only the wave's experts and leave CUs free for the
+  // copy workgroups, and kernel-to-kernel dependencies on the release events cost the link
+  // nothing (6 MiB DMA copies behind such waits lose 10-45% of the link: 16,022 tokens through
+  // 64 lines took 412-414 ms against 429-433 ms). With resident experts in the waves' ranges
+  // the GEMMs fill the chip and the copy kernel would stall behind them (the 8-layer stack:
+  // 1,396 ms against 1,345-1,349 ms with DMA copies), so those layers keep hipMemcpyAsync.
   const int per_wave = std::max(1, R->n_lines / 2);
   const int nw = std::max<int>(1, (static_cast<int>(used.size()) + per_wave - 1) / per_wave);
   std::vector<std::vector<int32_t>> wexp(nw), wlines(nw);
@@ -240,7 +250,8 @@ moe_status ring_waves(const moe_layer* L, const void* x, int64_t t0, int64_t n,
       const int kind = staged == 0 ? MOE_COPY_INITIAL
                                    : (staged > i ? MOE_COPY_AHEAD : MOE_COPY_DEMAND);
       st = ring_stage(R, L->layer_id, wexp[ws_].data(), static_cast<int32_t>(wexp[ws_].size()),
-                      cs, wlines[ws_].data(), &later, /*two_streams=*/true, kind);
+                      cs, wlines[ws_].data(), &later, /*two_streams=*/true, kind,
+                      /*hold=*/true, all_offloaded);
       if (st == MOE_ERR_RING && staged > i) { st = MOE_OK; break; }   // retry after release
       if (st != MOE_OK) { release_held(i); return st; }
       ++staged;

@@ -58,6 +58,11 @@ MOE_HIDDEN hipError_t launch_topk(const float* logits, int64_t T, int E, int k, 
 MOE_HIDDEN hipError_t launch_chunk_hist(const int32_t* ids, int64_t T, int k, int E,
                                         int64_t chunk, int32_t* chunk_counts, hipStream_t s);
 
+// Copy `bytes` (a multiple of 16; both pointers 16-byte aligned) from the device mapping of
+// pinned host memory into device memory with a kernel on stream s.
+MOE_HIDDEN hipError_t launch_line_copy(void* dst, const void* src_dev, size_t bytes,
+                                       hipStream_t s);
+
 MOE_HIDDEN hipError_t launch_upload_ptrs(const void** dst_table, const void* const* src,
                                          int first, int n, hipStream_t s);
 MOE_HIDDEN hipError_t launch_upload_pairs(const void** table, const int32_t* idx,

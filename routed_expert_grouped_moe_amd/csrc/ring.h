@@ -24,6 +24,10 @@ struct moe_ring {
   };
   struct Bank {
     const char* base = nullptr;
+    // The device's address of the pinned bank (hipHostGetDevicePointer), when it has one and
+    // it is 16-byte aligned: misses are then copied by the library's copy kernel, else by
+    // hipMemcpyAsync.
+    const char* dev_base = nullptr;
     std::vector<int32_t> slot;    // bank slot of each expert, -1 = resident
   };
 
@@ -68,11 +72,13 @@ inline int64_t ring_key(int32_t layer, int32_t expert) {
 // kind: MOE_COPY_* category the staging's requested and copied bytes are counted under.
 // hold: the lines stay held until ring_release (else each miss's release is recorded on its
 // copy stream right behind the copy, and no line stays held).
+// kernel_copy: misses are copied by the library's copy kernel (when the bank has a device
+// mapping) instead of hipMemcpyAsync.
 MOE_HIDDEN moe_status ring_stage(moe_ring* r, int32_t layer, const int32_t* experts, int32_t n,
                                  hipStream_t copy_stream, int32_t* lines_out,
                                  const std::vector<char>* later = nullptr,
                                  bool two_streams = false, int kind = MOE_COPY_DEMAND,
-                                 bool hold = true);
+                                 bool hold = true, bool kernel_copy = false);
 MOE_HIDDEN moe_status ring_wait_ready(moe_ring* r, const int32_t* lines, int32_t n,
                                       hipStream_t stream);
 MOE_HIDDEN moe_status ring_release(moe_ring* r, const int32_t* lines, int32_t n,

@@ -38,7 +38,7 @@ void clear_error() { g_last_error.clear(); }
 
 moe_status ring_stage(moe_ring* r, int32_t layer, const int32_t* experts, int32_t n,
                       hipStream_t cs0, int32_t* lines_out, const std::vector<char>* later,
-                      bool two_streams, int kind, bool hold) {
+                      bool two_streams, int kind, bool hold, bool kernel_copy) {
   if (kind < 0 || kind >= MOE_COPY_KINDS) kind = MOE_COPY_DEMAND;
   auto bit = r->banks.find(layer);
   if (bit == r->banks.end())
@@ -159,9 +159,12 @@ moe_status ring_stage(moe_ring* r, int32_t layer, const int32_t* experts, int32_
     const Planned& pl = plan[q];
     hipStream_t cs = pl.sj ? r->copy2 : cs0;
     const int e = experts[pl.i];
-    const char* src = bank.base + static_cast<size_t>(bank.slot[e]) * r->line_bytes;
+    const size_t src_off = static_cast<size_t>(bank.slot[e]) * r->line_bytes;
     char* dst = r->lines + static_cast<size_t>(pl.victim) * r->line_bytes;
-    hipError_t err = hipMemcpyAsync(dst, src, r->line_bytes, hipMemcpyHostToDevice, cs);
+    hipError_t err = (kernel_copy && bank.dev_base)
+                         ? launch_line_copy(dst, bank.dev_base + src_off, r->line_bytes, cs)
+                         : hipMemcpyAsync(dst, bank.base + src_off, r->line_bytes,
+                                          hipMemcpyHostToDevice, cs);
     if (err == hipSuccess) err = hipEventRecord(r->ready[pl.victim], cs);
     // not held: the copy stream itself is the line's last reader so far
     if (err == hipSuccess && !hold) err = hipEventRecord(r->release[pl.victim], cs);
@@ -319,6 +322,19 @@ moe_status moe_ring_bind_bank(moe_ring* r, int32_t layer_id, const void* pinned_
   }
   moe_ring::Bank& b = r->banks[layer_id];
   b.base = static_cast<const char*>(pinned_bank);
+  b.dev_base = nullptr;
+  // The copy kernel reads the bank through the device's mapping of the pinned memory; it is
+  // used only where that mapping is the host address itself (unified addressing) and 16-byte
+  // aligned, else the copies stay with hipMemcpyAsync.
+  if (pinned_bank) {
+    void* dev = nullptr;
+    if (hipHostGetDevicePointer(&dev, const_cast<void*>(pinned_bank), 0) == hipSuccess &&
+        dev == pinned_bank && (reinterpret_cast<uintptr_t>(dev) & 15u) == 0 &&
+        (r->line_bytes & 15u) == 0)
+      b.dev_base = static_cast<const char*>(dev);
+    else
+      (void)hipGetLastError();        // leave no error behind for the next launch check
+  }
   b.slot.assign(bank_slot_of_expert, bank_slot_of_expert + E);
   return MOE_OK;
 }

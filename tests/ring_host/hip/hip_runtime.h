@@ -30,3 +30,4 @@ hipError_t hipEventRecord(hipEvent_t e, hipStream_t s);
 hipError_t hipEventSynchronize(hipEvent_t e);
 hipError_t hipMemcpyAsync(void* dst, const void* src, size_t bytes, hipMemcpyKind kind,
                           hipStream_t s);
+hipError_t hipHostGetDevicePointer(void** dev, void* host, unsigned flags);

@@ -158,6 +158,16 @@ hipError_t hipMemcpyAsync(void* dst, const void* src, size_t, hipMemcpyKind, hip
   g_ops[dst].push_back(enqueue(s, static_cast<const char*>(src), true));
   return hipSuccess;
 }
+// Pinned memory is mapped at its host address (the library then copies with its kernel).
+hipError_t hipHostGetDevicePointer(void** dev, void* host, unsigned) {
+  *dev = host;
+  return hipSuccess;
+}
+namespace moe {
+hipError_t launch_line_copy(void* dst, const void* src_dev, size_t bytes, hipStream_t s) {
+  return hipMemcpyAsync(dst, src_dev, bytes, hipMemcpyHostToDevice, s);
+}
+}  // namespace moe
 
 // moe_ring_create sizes a line from the shape after checking it; the shape checks live with
 // the workspace layout in the GPU part of the library, so this check stands in for them.

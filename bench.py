@@ -90,15 +90,19 @@ def _place(wl, layer=0, offloaded=(), ring=None, params=None):
     return params, moe.Layer.from_params(params, _shape(wl), "cuda", offloaded, ring, layer)
 
 
-def time_steps(fn, steps, warmup):
+def time_steps(fn, steps, warmup, gate=False):
     """(mean ms per step over the K steps, wall ms per step, per-step ms list). HIP events on
-    the current stream bracket the K steps, and each step separately."""
+    the current stream bracket the K steps, and each step separately. gate: the GPU first
+    spins for about 50 ms while the host enqueues the K steps behind it, so no kernel of the
+    timed steps waits on the host (per-launch event timings then hold kernel time only)."""
     import torch
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     w0 = time.perf_counter()
+    if gate:
+        torch.cuda._sleep(100_000_000)
     ev[0].record()
     for i in range(steps):
         fn()
@@ -193,7 +197,143 @@ def stack_variant(steps: int):
             "pass_ms": spread(per), "ring_hit_rate": round(st["hits"] / max(1, looks), 4),
             "ring_lookups_per_pass": looks // steps,
             "h2d_gb_per_pass": round(st["bytes_h2d"] / steps / 1e9, 2),
+            "h2d_gb_per_pass_by_kind": {k: round(v / steps / 1e9, 3)
+                                        for k, v in st["copied_bytes"].items()},
+            "requested_gb_per_pass_by_kind": {k: round(v / steps / 1e9, 3)
+                                              for k, v in st["requested_bytes"].items()},
             "h2d_gbps": round(st["bytes_h2d"] / steps / (wall / 1e3) / 1e9, 2)}
+
+
+def ring_variant(moe, wl, params, x, bufs, t_gemm):
+    """The layer as the config specifies it: all 512 experts in a pinned bank, streamed
+    through a 64-line ring at chunk 2,048 (one untimed pass, three timed). t_gemm: the same
+    layer's resident time at chunk 2,048 (ms), the compute alone."""
+    import torch
+    T = wl.T
+    log("[bench] ring variant: all 512 experts in a pinned bank, 64 lines, chunk 2048")
+    sh = _shape(wl)
+    ring = moe.Ring(sh, 64)
+    _, Lr = _place(wl, offloaded=range(sh.n_experts), ring=ring, params=params)
+    br = moe.layer_buffers(Lr, T, 2048)
+    cs = torch.cuda.Stream()
+    ring_step = lambda: moe.moe_prefill_layer(Lr, x, 2048, bufs=br, copy_stream=cs)
+    ring_step()
+    torch.cuda.synchronize()
+    ring.reset_stats()
+    r_ms, r_wall, r_per = time_steps(ring_step, 3, 0)
+    ok = torch.equal(br["out"].view(torch.int16), bufs["out"].view(torch.int16))
+    st = ring.stats()
+    per_step_bytes = st["bytes_h2d"] / 3
+    link = h2d_probe(1 << 30, 3)
+    line_rate = h2d_line_probe(ring.line_bytes, 64)
+    # the copies at the link rate of one 1 GiB pinned copy: a floor the 6 MiB line copies of
+    # the ring do not reach, so the compute share below is a lower bound
+    t_copy = per_step_bytes / (link * 1e9) * 1e3
+    # the same bytes as 6 MiB line copies alternating two streams with nothing else on the
+    # GPU (the ring's copy pattern): the copy time the ring would take without compute
+    t_lines = per_step_bytes / (line_rate * 1e9) * 1e3
+    hidden = (t_copy + t_gemm - r_wall) / t_gemm
+    hidden_lines = (t_lines + t_gemm - r_wall) / t_gemm
+    res = {
+        "tokens_per_s": round(T / (r_wall / 1e3), 1), "ms_per_step": round(r_wall, 2),
+        "step_ms": spread(r_per),
+        "h2d_gb_per_step": round(per_step_bytes / 1e9, 3),
+        "h2d_gbps": round(per_step_bytes / (r_wall / 1e3) / 1e9, 2),
+        "h2d_link_gbps_measured": round(link, 2),
+        "link_floor_ms": round(t_copy, 2),
+        "ring_over_link_floor": round(r_wall / t_copy, 4),
+        "compute_alone_ms": t_gemm,
+        "ring_hit_rate": round(st["hits"] / max(1, st["hits"] + st["misses"]), 4),
+        "copy_waits_per_step": st["copy_waits"] // 3,
+        "copied_bytes_per_step_by_kind": {k: v // 3 for k, v in st["copied_bytes"].items()},
+        "compute_hidden_frac_vs_link_floor": round(max(0.0, min(1.0, hidden)), 3),
+        "h2d_line_copy_gbps_measured": round(line_rate, 2),
+        "line_copies_alone_ms": round(t_lines, 2),
+        "compute_hidden_frac_vs_line_copies": round(max(0.0, min(1.0, hidden_lines)), 3),
+        "bit_identical_to_batched": bool(ok)}
+    del br, Lr
+    ring.close()
+    return res
+
+
+def _union(iv):
+    out = []
+    for a, b in sorted(iv):
+        if out and a <= out[-1][1]:
+            out[-1][1] = max(out[-1][1], b)
+        else:
+            out.append([a, b])
+    return out
+
+
+def _cover(u):
+    return sum(b - a for a, b in u)
+
+
+def _meet(u, v):
+    """Length of the intersection of two interval unions (each sorted and disjoint)."""
+    i = j = 0
+    tot = 0
+    while i < len(u) and j < len(v):
+        lo, hi = max(u[i][0], v[j][0]), min(u[i][1], v[j][1])
+        tot += max(0, hi - lo)
+        if u[i][1] < v[j][1]:
+            i += 1
+        else:
+            j += 1
+    return tot
+
+
+def overlap_from_trace(d: str) -> dict:
+    """Copy/compute overlap of the ring passes in a rocprofv3 trace of a bench.py run
+    (`rocprofv3 --kernel-trace --memory-copy-trace --output-format csv`).
+
+    Copies are the library's line-copy kernels when the run has any (the all-offloaded ring
+    layer), else the host-to-device DMA copies; the window runs from the first copy after the
+    first router launch to the end of the last copy, so it covers the ring passes of a run
+    with `--variants ring` or `--variants stack` and nothing of the input set-up. Inside it: the share of time some copy is in flight, and the share
+    of the GEMM kernels' busy time (and of all library kernels' busy time) that runs while a
+    copy is in flight, measured from the timeline rather than bounded from separate runs."""
+    import csv
+    import glob
+    kt = sorted(glob.glob(os.path.join(d, "**", "*kernel_trace.csv"), recursive=True))
+    mt = sorted(glob.glob(os.path.join(d, "**", "*memory_copy_trace.csv"), recursive=True))
+    if not kt:
+        raise SystemExit(f"no *kernel_trace.csv under {d}")
+    kernels = []
+    for path in kt:
+        for r in csv.DictReader(open(path)):
+            kernels.append((r["Kernel_Name"], int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    copies = []
+    for path in mt:
+        for r in csv.DictReader(open(path)):
+            if any("HOST_TO_DEVICE" in str(v) for v in r.values()):
+                copies.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"])))
+    lib = [k for k in kernels if "moe::" in k[0]]
+    kcopies = [(a, b) for n, a, b in lib if "line_copy_kernel" in n]
+    if kcopies:     # a ring run whose copies are kernels; DMA copies are the later link probes
+        copies = kcopies
+    first_router = min((a for n, a, b in lib if "router_kernel" in n), default=None)
+    if first_router is None or not copies:
+        return {"trace": d, "error": "no router launch or no host-to-device copies in the trace"}
+    copies = [c for c in copies if c[0] >= first_router]
+    if not copies:
+        return {"trace": d, "error": "no copies after the first router launch"}
+    w0, w1 = min(a for a, _ in copies), max(b for _, b in copies)
+    inside = lambda a, b: a >= w0 and b <= w1
+    cu = _union(copies)
+    comp = [k for k in lib if "line_copy_kernel" not in k[0] and inside(k[1], k[2])]
+    gemm = _union([(a, b) for n, a, b in comp if "gu_" in n or "down_kernel" in n])
+    allk = _union([(a, b) for _, a, b in comp])
+    win = w1 - w0
+    res = {"trace": d, "window_ms": round(win / 1e6, 3), "copies": len(copies),
+           "link_busy_frac": round(_cover(cu) / win, 4),
+           "gemm_busy_ms": round(_cover(gemm) / 1e6, 3),
+           "gemm_under_copy_frac": round(_meet(gemm, cu) / max(1, _cover(gemm)), 4),
+           "kernels_busy_ms": round(_cover(allk) / 1e6, 3),
+           "kernels_under_copy_frac": round(_meet(allk, cu) / max(1, _cover(allk)), 4),
+           "copy_kind": "kernel" if kcopies else "dma"}
+    return res
 
 
 def kernel_source_sha() -> str:
@@ -325,7 +465,20 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain fp32 copy kernel (out = in * 1) over BYTES bytes "
                          "5 times and print its bandwidth (calibrates HBM byte counters)")
+    ap.add_argument("--variants", default="chunks,small,ring,stack",
+                    help="comma list of the variants to run beside the headline pass "
+                         "(chunks, small, ring, stack)")
+    ap.add_argument("--overlap-from-trace", metavar="DIR", default="",
+                    help="no GPU work: read a rocprofv3 kernel and memory-copy trace (csv) of a "
+                         "bench.py run from DIR and print the copy/compute overlap of its ring "
+                         "passes")
     args = ap.parse_args()
+    if args.overlap_from_trace:
+        print(json.dumps(overlap_from_trace(args.overlap_from_trace)), flush=True)
+        return
+    chosen = set() if args.no_variants else {v for v in args.variants.split(",") if v}
+    if args.no_stack:
+        chosen.discard("stack")
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         log("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -349,7 +502,7 @@ def main():
     # host-link rate measured about 15% lower (1.57 s against 1.35 s per pass) while alone,
     # or after any one of them, it holds 52-53 GB/s.
     stack = None
-    if not args.no_variants and not args.no_stack:
+    if "stack" in chosen:
         log("[bench] stack variant: 8 layers, T=32,700, 128-line ring")
         stack = stack_variant(1)
         torch.cuda.empty_cache()
@@ -369,7 +522,7 @@ def main():
 
     moe.moe_profile_read(reset=True)
     moe.moe_profile_enable(True)
-    ms_prof, _, _ = time_steps(step, args.steps, 0)
+    ms_prof, _, _ = time_steps(step, args.steps, 0, gate=True)
     moe.moe_profile_enable(False)
     prof3 = moe.moe_profile_read(reset=True, clocks=True)
     prof = {k: (v[0], v[1]) for k, v in prof3.items()}
@@ -433,61 +586,27 @@ def main():
         roof["mfma_peak_at_sustained_clock_tflops"] = round(2500.0 * clk / 2400.0, 1)
 
     variants = {}
-    if not args.no_variants:
-        for c in (2048, 4096, 8192):
-            b2 = moe.layer_buffers(L, T, c)
-            v_ms, _, v_per = time_steps(lambda: moe.moe_prefill_layer(L, x, c, bufs=b2),
-                                        max(3, args.steps // 2), 2)
-            ok = torch.equal(b2["out"].view(torch.int16), bufs["out"].view(torch.int16))
-            variants[f"resident_chunk{c}"] = {"tokens_per_s": round(T / (v_ms / 1e3), 1),
-                                              "ms_per_step": round(v_ms, 3), "step_ms": spread(v_per),
-                                              "bit_identical_to_batched": bool(ok)}
-            del b2
+    for c in ((2048, 4096, 8192) if "chunks" in chosen else ()):
+        b2 = moe.layer_buffers(L, T, c)
+        v_ms, _, v_per = time_steps(lambda: moe.moe_prefill_layer(L, x, c, bufs=b2),
+                                    max(3, args.steps // 2), 2)
+        ok = torch.equal(b2["out"].view(torch.int16), bufs["out"].view(torch.int16))
+        variants[f"resident_chunk{c}"] = {"tokens_per_s": round(T / (v_ms / 1e3), 1),
+                                          "ms_per_step": round(v_ms, 3), "step_ms": spread(v_per),
+                                          "bit_identical_to_batched": bool(ok)}
+        del b2
+    if "small" in chosen:
         variants["small_call_T8"] = small_call_variant(L, mi, wl)
-        log("[bench] ring variant: all 512 experts in a pinned bank, 64 lines, chunk 2048")
-        ring = moe.Ring(sh, 64)
-        _, Lr = _place(wl, offloaded=range(sh.n_experts), ring=ring, params=params)
-        br = moe.layer_buffers(Lr, T, 2048)
-        cs = torch.cuda.Stream()
-        ring_step = lambda: moe.moe_prefill_layer(Lr, x, 2048, bufs=br, copy_stream=cs)
-        ring_step()
-        torch.cuda.synchronize()
-        ring.reset_stats()
-        r_ms, r_wall, r_per = time_steps(ring_step, 3, 0)
-        ok = torch.equal(br["out"].view(torch.int16), bufs["out"].view(torch.int16))
-        st = ring.stats()
-        per_step_bytes = st["bytes_h2d"] / 3
-        link = h2d_probe(1 << 30, 3)
-        line_rate = h2d_line_probe(ring.line_bytes, 64)
-        # the copies at the link rate of one 1 GiB pinned copy: a floor the 6 MiB line copies of
-        # the ring do not reach, so the compute share below is a lower bound
-        t_copy = per_step_bytes / (link * 1e9) * 1e3
-        # the same bytes as 6 MiB line copies alternating two streams with nothing else on the
-        # GPU (the ring's copy pattern): the copy time the ring would take without compute
-        t_lines = per_step_bytes / (line_rate * 1e9) * 1e3
-        t_gemm = variants["resident_chunk2048"]["ms_per_step"]        # ms, compute alone
-        hidden = (t_copy + t_gemm - r_wall) / t_gemm
-        hidden_lines = (t_lines + t_gemm - r_wall) / t_gemm
-        variants["offload_ring64_chunk2048"] = {
-            "tokens_per_s": round(T / (r_wall / 1e3), 1), "ms_per_step": round(r_wall, 2),
-            "step_ms": spread(r_per),
-            "h2d_gb_per_step": round(per_step_bytes / 1e9, 3),
-            "h2d_gbps": round(per_step_bytes / (r_wall / 1e3) / 1e9, 2),
-            "h2d_link_gbps_measured": round(link, 2),
-            "link_floor_ms": round(t_copy, 2),
-            "ring_over_link_floor": round(r_wall / t_copy, 4),
-            "compute_alone_ms": t_gemm,
-            "ring_hit_rate": round(st["hits"] / max(1, st["hits"] + st["misses"]), 4),
-            "copy_waits_per_step": st["copy_waits"] // 3,
-            "compute_hidden_frac_vs_link_floor": round(max(0.0, min(1.0, hidden)), 3),
-            "h2d_line_copy_gbps_measured": round(line_rate, 2),
-            "line_copies_alone_ms": round(t_lines, 2),
-            "compute_hidden_frac_vs_line_copies": round(max(0.0, min(1.0, hidden_lines)), 3),
-            "bit_identical_to_batched": bool(ok)}
-        del br, Lr
-        ring.close()
-        if stack is not None:
-            variants["stack"] = stack
+    if "ring" in chosen:
+        if "resident_chunk2048" in variants:
+            t_gemm = variants["resident_chunk2048"]["ms_per_step"]    # ms, compute alone
+        else:
+            b2 = moe.layer_buffers(L, T, 2048)
+            t_gemm = round(time_steps(lambda: moe.moe_prefill_layer(L, x, 2048, bufs=b2), 3, 2)[0], 3)
+            del b2
+        variants["offload_ring64_chunk2048"] = ring_variant(moe, wl, params, x, bufs, t_gemm)
+    if stack is not None:
+        variants["stack"] = stack
 
     copy_gbps = copy_probe(1 << 30, 5)
     cpu = None

@@ -204,6 +204,42 @@ def stack_variant(steps: int):
             "h2d_gbps": round(st["bytes_h2d"] / steps / (wall / 1e3) / 1e9, 2)}
 
 
+def fused_variant(moe, L, x, bufs, T, steps):
+    """The layer at chunks whose routed tiles are 64 rows (1,024 and 2,048 tokens: 16 and 32
+    rows per expert) with the routed GEMMs as two launches and as the fused launch
+    (MOE_OPT_FUSED_GU_DOWN, h kept in LDS): layer time, routed-GEMM time per layer from the
+    library's launch timings, and bit-identity with the batched pass."""
+    import torch
+    res = {}
+    for c in (1024, 2048):
+        b2 = moe.layer_buffers(L, T, c)
+        ent = {}
+        for name, on in (("separate", 0), ("fused", 1)):
+            moe.moe_set_option("fused_gu_down", on)
+            try:
+                run = lambda: moe.moe_prefill_layer(L, x, c, bufs=b2)
+                v_ms, _, v_per = time_steps(run, max(3, steps // 2), 2)
+                moe.moe_profile_read(reset=True)
+                moe.moe_profile_enable(True)
+                time_steps(run, 3, 0, gate=True)
+                moe.moe_profile_enable(False)
+                prof = moe.moe_profile_read(reset=True)
+            finally:
+                moe.moe_set_option("fused_gu_down", 0)
+                moe.moe_profile_enable(False)
+            routed = sum(prof[s][0] for s in ("gu_routed", "down_routed", "gu_down_fused")) / 3
+            ok = torch.equal(b2["out"].view(torch.int16), bufs["out"].view(torch.int16))
+            ent[name] = {"ms_per_step": round(v_ms, 3), "step_ms": spread(v_per),
+                         "routed_gemm_ms_per_step": round(routed, 3),
+                         "stage_ms_per_step": {k: round(v[0] / 3, 3) for k, v in prof.items()
+                                               if v[1]},
+                         "fused_launches_per_step": prof["gu_down_fused"][1] // 3,
+                         "bit_identical_to_batched": bool(ok)}
+        res[f"chunk{c}"] = ent
+        del b2
+    return res
+
+
 def ring_variant(moe, wl, params, x, bufs, t_gemm):
     """The layer as the config specifies it: all 512 experts in a pinned bank, streamed
     through a 64-line ring at chunk 2,048 (one untimed pass, three timed). t_gemm: the same
@@ -465,9 +501,9 @@ def main():
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run a plain fp32 copy kernel (out = in * 1) over BYTES bytes "
                          "5 times and print its bandwidth (calibrates HBM byte counters)")
-    ap.add_argument("--variants", default="chunks,small,ring,stack",
+    ap.add_argument("--variants", default="chunks,small,fused,ring,stack",
                     help="comma list of the variants to run beside the headline pass "
-                         "(chunks, small, ring, stack)")
+                         "(chunks, small, fused, ring, stack)")
     ap.add_argument("--overlap-from-trace", metavar="DIR", default="",
                     help="no GPU work: read a rocprofv3 kernel and memory-copy trace (csv) of a "
                          "bench.py run from DIR and print the copy/compute overlap of its ring "
@@ -597,6 +633,8 @@ def main():
         del b2
     if "small" in chosen:
         variants["small_call_T8"] = small_call_variant(L, mi, wl)
+    if "fused" in chosen:
+        variants["fused_gu_down"] = fused_variant(moe, L, x, bufs, T, args.steps)
     if "ring" in chosen:
         if "resident_chunk2048" in variants:
             t_gemm = variants["resident_chunk2048"]["ms_per_step"]    # ms, compute alone

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 4
+#define MOE_ABI_VERSION 5
 
 typedef enum {
   MOE_OK = 0,
@@ -115,7 +115,9 @@ size_t moe_workspace_bytes(const moe_shape* shape, int64_t max_chunk_tokens);
  *   h_shared dtype [n, I_s] the same for the shared expert, one row per chunk token
  *   y        fp32 [n*k, d] each routed expert's output, unweighted, at row t*k + j
  * With a ring, h and y of a row hold its expert's results only once the expert's wave has run
- * (all of them after the call's work completes). For inspection and tests. */
+ * (all of them after the call's work completes). With MOE_OPT_FUSED_GU_DOWN on, the chunks
+ * that take the fused launch keep h on chip and leave the h region unwritten. For inspection
+ * and tests. */
 typedef struct {
   size_t counts;
   size_t offsets;
@@ -288,6 +290,22 @@ moe_status moe_ring_invalidate(moe_ring* ring);
  * ring. NULL-safe. */
 void moe_ring_destroy(moe_ring* ring);
 
+/* Process-wide options, read when a call enqueues its work; every option is 0 (off) until
+ * set. Unknown options are MOE_ERR_INVALID.
+ *   MOE_OPT_FUSED_GU_DOWN  1: a chunk whose routed M-tiles are 64 rows tall (experts averaging
+ *     16 to 48 rows), in bf16, with I a multiple of 128 up to 512, runs both routed GEMMs of
+ *     each M-tile in one workgroup and keeps h in LDS instead of writing it to the workspace
+ *     and reading it back (the byte trimming of the deep-prefill chunk buffers the page "Flash
+ *     Next EXL3: exact deep prefill" defers, section "Performance work is deferred on
+ *     purpose"); other chunks run as with 0. The output bytes are the same either way. On
+ *     MI355X the fused launch times within 2% of the two separate launches and does not
+ *     shorten the layer (one workgroup per CU streams its expert's whole gate/up and down
+ *     weights alone), so it is off by default. */
+enum { MOE_OPT_FUSED_GU_DOWN = 1 };
+moe_status moe_set_option(int32_t option, int32_t value);
+/* *value = the option's current value. */
+moe_status moe_get_option(int32_t option, int32_t* value);
+
 /* Per-kernel timing with HIP events. While enabled, every launch the library enqueues is
  * bracketed by two timing events recorded on the launch's own stream; moe_profile_read waits
  * for the recorded events and adds their elapsed times to per-stage totals. The GEMM kernels
@@ -313,7 +331,9 @@ enum {
   MOE_STAGE_DOWN_SHARED_COMBINE = 13, /* shared down GEMM with the combine in its epilogue */
   MOE_STAGE_GU_MIXED = 14,  /* shared and routed gate/up GEMMs in one launch (resident experts,
                                tall or big routed tiles) */
-  MOE_STAGE_COUNT = 15
+  MOE_STAGE_GU_DOWN_FUSED = 15, /* routed gate/up and down GEMMs in one launch, h kept on chip
+                                   (MOE_OPT_FUSED_GU_DOWN) */
+  MOE_STAGE_COUNT = 16
 };
 
 typedef struct {

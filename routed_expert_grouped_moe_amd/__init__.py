@@ -21,6 +21,7 @@ __all__ = [
     "moe_prefill_route", "moe_prefill_chunk", "moe_prefill_layer", "moe_stage_experts",
     "moe_add_rmsnorm", "moe_abi_version", "line_elems", "moe_workspace_offsets",
     "layer_buffers", "moe_profile_enable", "moe_profile_read", "moe_prefill_stack",
+    "moe_set_option", "moe_get_option",
 ]
 
 
@@ -363,6 +364,19 @@ def moe_prefill_stack(layers: Sequence[Layer], x, chunk: int, eps: float, stream
         moe_add_rmsnorm(xs, r["out"], eps, x_out=xs, normed=normed, stream=stream)
     res["out"] = xs
     return res
+
+
+def moe_set_option(name: str, value: int) -> None:
+    """moe_set_option by name: "fused_gu_down" (MOE_OPT_FUSED_GU_DOWN)."""
+    from ._abi import OPTIONS
+    check(lib().moe_set_option(OPTIONS[name], int(value)), "moe_set_option")
+
+
+def moe_get_option(name: str) -> int:
+    from ._abi import OPTIONS
+    v = ctypes.c_int32(0)
+    check(lib().moe_get_option(OPTIONS[name], ctypes.byref(v)), "moe_get_option")
+    return int(v.value)
 
 
 def moe_profile_enable(on: bool = True) -> None:

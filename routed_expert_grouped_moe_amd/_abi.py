@@ -39,7 +39,9 @@ class MoeProfile(ctypes.Structure):
 
 STAGES = ["router", "topk", "chunk_counts", "table", "hist", "scan", "permute", "gu_shared",
           "down_shared", "gu_routed", "down_routed", "combine", "rmsnorm", "down_shared_combine",
-          "gu_mixed"]
+          "gu_mixed", "gu_down_fused"]
+
+OPTIONS = {"fused_gu_down": 1}       # MOE_OPT_* of include/moe_prefill.h
 
 
 COPY_KINDS = ["initial", "ahead", "demand", "cross_layer"]     # MOE_COPY_* order
@@ -80,6 +82,8 @@ SIGNATURES = {
     "moe_ring_invalidate": (c_i32, [c_vp]),
     "moe_ring_destroy": (None, [c_vp]),
     "moe_profile_enable": (c_i32, [c_i32]),
+    "moe_set_option": (c_i32, [c_i32, c_i32]),
+    "moe_get_option": (c_i32, [c_i32, ctypes.POINTER(c_i32)]),
     "moe_profile_read": (c_i32, [ctypes.POINTER(MoeProfile), c_i32]),
     "moe_add_rmsnorm": (c_i32, [c_vp, c_vp, c_i64, c_i32, c_i32, c_f32, c_vp, c_vp, c_vp]),
 }
@@ -87,7 +91,7 @@ SIGNATURES = {
 _lib = None
 
 
-ABI_VERSION = 4     # MOE_ABI_VERSION of include/moe_prefill.h
+ABI_VERSION = 5     # MOE_ABI_VERSION of include/moe_prefill.h
 
 
 def lib():

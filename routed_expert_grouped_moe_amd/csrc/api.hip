@@ -6,11 +6,15 @@
 #include <unordered_map>
 #include <vector>
 
+#include <atomic>
+
 #include "ring.h"
 
 namespace moe {
 
 namespace {
+
+std::atomic<int32_t> g_opt_fused_gu_down{0};
 
 constexpr size_t kAlign = 256;
 inline size_t align_up(size_t v) { return (v + kAlign - 1) & ~(kAlign - 1); }
@@ -157,6 +161,19 @@ moe_status route_impl(const moe_layer* L, const void* x, int64_t T, int64_t chun
   return MOE_OK;
 }
 
+// The routed GEMMs of the M-tiles g covers: gate/up then down, or both in one fused launch
+// when MOE_OPT_FUSED_GU_DOWN is on and the tiles allow it (the same h and Y bits).
+hipError_t launch_routed(const moe_shape& sh, const void* x, int64_t t0, const GemmGroups& g,
+                         const int32_t* row_tok, const int32_t* row_slot, void* h, float* y,
+                         hipStream_t s) {
+  if (g_opt_fused_gu_down.load(std::memory_order_relaxed) &&
+      gu_down_fused_supported(sh.dtype, g.tile_rows, sh.inter))
+    return launch_gu_down_fused(x, t0, sh.d, sh.inter, g, row_tok, row_slot, y, s);
+  hipError_t err = launch_gu_routed(sh.dtype, x, t0, sh.d, sh.inter, g, row_tok, h, s);
+  if (err == hipSuccess) err = launch_down_routed(sh.dtype, h, sh.d, sh.inter, g, row_slot, y, s);
+  return err;
+}
+
 // Routed GEMMs of a chunk whose experts come partly from the ring: the chunk's used
 // offloaded experts, in ascending id, are cut into waves of at most n_lines/2 experts; wave w
 // covers the expert-id range [lo_w, hi_w) (resident experts in that range run with it). The
@@ -265,9 +282,7 @@ moe_status ring_waves(const moe_layer* L, const void* x, int64_t t0, int64_t n,
     g.tile_lo = static_cast<int>(mt_begin[lo[w]]);
     g.tile_cap = static_cast<int>(mt_begin[hi[w]] - mt_begin[lo[w]]);
     if (st == MOE_OK && err == hipSuccess)
-      err = launch_gu_routed(sh.dtype, x, t0, sh.d, sh.inter, g, row_tok, h, s);
-    if (st == MOE_OK && err == hipSuccess)
-      err = launch_down_routed(sh.dtype, h, sh.d, sh.inter, g, row_slot, y, s);
+      err = launch_routed(sh, x, t0, g, row_tok, row_slot, h, y, s);
     // The wave's table entries go back to NULL: a tile outside the planned waves (only
     // possible with caller counts that differ from the chunk's own) then finds no line and
     // writes NaN, instead of reading a line a later copy may be refilling.
@@ -333,13 +348,14 @@ moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const i
                  uniform ? static_cast<const char*>(L->expert_lines[0]) : nullptr, stride, 0,
                  static_cast<int>(n * k / bm + std::min<int64_t>(E, n * k)), bm};
     const int32_t* row_tok = reinterpret_cast<const int32_t*>(ws + W.row_tok);
-    if (mixed)
+    const int32_t* row_slot = reinterpret_cast<const int32_t*>(ws + W.row_slot);
+    if (mixed) {
       MOE_HIP(launch_gu_mixed(sh.dtype, x, t0, n, sh.d, sh.inter, sh.inter_shared,
                               L->w_gu_shared, ws + W.h_shared, g, row_tok, ws + W.h, s));
-    else
-      MOE_HIP(launch_gu_routed(sh.dtype, x, t0, sh.d, sh.inter, g, row_tok, ws + W.h, s));
-    MOE_HIP(launch_down_routed(sh.dtype, ws + W.h, sh.d, sh.inter, g,
-                               reinterpret_cast<const int32_t*>(ws + W.row_slot), y, s));
+      MOE_HIP(launch_down_routed(sh.dtype, ws + W.h, sh.d, sh.inter, g, row_slot, y, s));
+    } else {
+      MOE_HIP(launch_routed(sh, x, t0, g, row_tok, row_slot, ws + W.h, y, s));
+    }
   } else {
     moe_status st = ring_waves(L, x, t0, n, counts_host, ws, W, s, cs ? cs : s);
     // Join even on failure, so the caller's stream never runs ahead of the side work.
@@ -438,6 +454,23 @@ using moe::set_error;
 extern "C" {
 
 int32_t moe_abi_version(void) { return MOE_ABI_VERSION; }
+
+moe_status moe_set_option(int32_t option, int32_t value) {
+  moe::clear_error();
+  if (option != MOE_OPT_FUSED_GU_DOWN)
+    return moe::set_error(MOE_ERR_INVALID, "unknown option %d", option);
+  moe::g_opt_fused_gu_down.store(value != 0 ? 1 : 0, std::memory_order_relaxed);
+  return MOE_OK;
+}
+
+moe_status moe_get_option(int32_t option, int32_t* value) {
+  moe::clear_error();
+  if (!value) return moe::set_error(MOE_ERR_INVALID, "value is NULL");
+  if (option != MOE_OPT_FUSED_GU_DOWN)
+    return moe::set_error(MOE_ERR_INVALID, "unknown option %d", option);
+  *value = moe::g_opt_fused_gu_down.load(std::memory_order_relaxed);
+  return MOE_OK;
+}
 
 const char* moe_status_string(moe_status s) {
   switch (s) {

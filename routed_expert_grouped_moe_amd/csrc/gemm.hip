@@ -721,6 +721,190 @@ void down_kernel(DownParams p) {
   clock.finish();
 }
 
+// ---------------------------------------------------------------- fused gate/up -> down
+// One workgroup per routed M-tile of at most 64 rows (the small tile's height) runs both of the
+// tile's GEMMs, and h never leaves the CU:
+//   1. gate/up over I / 128 N-chunks, each with the small tile's mainloop (the same loads,
+//      instruction, K order and lane mapping as the separate gate/up launch), its epilogue
+//      writing silu(gate) * up, rounded to bf16, into an LDS copy of the tile's h rows;
+//   2. down over the d / 256 N-chunks, the weight rows staged through two LDS buffers in one
+//      pipeline across the chunks and h read from LDS as the A operand, in the K order and lane
+//      mapping of the separate down launch; each chunk's Y goes out as there.
+// So h and Y are bit for bit those of the two launches. One pipeline carried through both steps
+// (no refill between the gate/up chunks) measured 3% slower than this with per-block fragment
+// reads, and 10-12% slower with all of a K step's fragments read before its MFMAs. LDS: the
+// small tile's 80 KB of stage buffers (in step 2 two 32 KB weight stages and the 16 KB output
+// staging), then h (64 rows x I bf16, I <= 512), then the output-slot table.
+using FusedTile = SmallTile;
+constexpr int kFusedMaxI = 512;
+constexpr int kFusedHOff = FusedTile::LDS;
+constexpr int kFusedTabOff = kFusedHOff + FusedTile::BM * kFusedMaxI * 2;
+constexpr int kFusedLds = kFusedTabOff + FusedTile::NW * FusedTile::FM * 16 * 4;
+constexpr int kFusedBStage = FusedTile::BN * FusedTile::RB;        // 256 weight rows x 128 B
+static_assert(2 * kFusedBStage + 16 * FusedTile::TN * 4 * FusedTile::NW <= FusedTile::LDS,
+              "two weight stages and the output staging fit in the stage buffers");
+static_assert(kFusedLds <= 160 * 1024, "LDS of one CU");
+
+struct FusedParams {
+  GuParams gu;            // prompt rows, d, I, groups, row_tok (gu.h unused)
+  int64_t line_down_off;  // element offset of W_down inside a line (2*I*d)
+  const int32_t* row_slot;
+  float* y;               // Y [n*k, d]
+};
+
+// Byte offset of h element (r, c) in the LDS copy: row r holds I bf16 in 128-byte K stages,
+// 16-byte segment g of a stage at g ^ (r & 7), the swizzle of the staged operand rows.
+__device__ __forceinline__ int fused_h_off(int r, int c, int I) {
+  return r * I * 2 + (c >> 6) * 128 + ((((c >> 3) & 7) ^ (r & 7)) << 4) + (c & 7) * 2;
+}
+
+__global__ __launch_bounds__(FusedTile::NT)
+void gu_down_fused_kernel(FusedParams p) {
+  using TL = FusedTile;
+  using T = uint16_t;
+  using F = Frag<T>;
+  __shared__ __attribute__((aligned(1024))) char lds[kFusedLds];
+  const GuParams& q = p.gu;
+  const int m_tiles = max(0, min(q.g.tile_cap, *q.g.n_mtiles - q.g.tile_lo));
+  int t;
+  if (!xcd_tile(m_tiles, &t)) return;
+  ClockSample clock(q.clk);
+  const MTile mt = q.g.mtiles[q.g.tile_lo + t];
+  const int64_t row0 = static_cast<int64_t>(q.g.offsets[mt.group]) + mt.m0;
+  const int rows = min(TL::BM, q.g.counts[mt.group] - mt.m0);
+  const char* line = line_of(q.g, mt.group);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wn = wave % TL::WN, kq = lane >> 4, l16 = lane & 15;
+  const int I = q.I, d = q.d;
+  char* hl = lds + kFusedHOff;
+
+  // output slot of each tile row, one copy per wave (read before any store needs it)
+  int* tab = reinterpret_cast<int*>(lds + kFusedTabOff) + wave * (TL::FM * 16);
+  for (int idx = lane; idx < TL::FM * 16; idx += 64)
+    tab[idx] = idx < rows ? p.row_slot[row0 + idx] : -1;
+  __builtin_amdgcn_wave_barrier();
+  auto row_of = [&](int sr) -> int64_t { return tab[sr]; };     // sr = block * 16 + row
+  auto store_y = [&](auto val, int c) {
+    const int col0 = c * TL::BN + wn * TL::TN;
+    store_slab<TL, float, TL::TN, true>(lds + 2 * kFusedBStage, val, row_of, p.y, d, col0,
+                                        min(TL::TN, d - col0));
+  };
+  const int n_dc = (d + TL::BN - 1) / TL::BN;
+  if (line == nullptr) {        // offloaded expert that was not staged: its Y rows are NaN
+    for (int c = 0; c < n_dc; ++c)
+      store_y([&](int, int, int) { return __builtin_nanf(""); }, c);
+    clock.finish();
+    return;
+  }
+
+  // 1. gate/up, h into LDS
+  constexpr int HC = TL::BN / 2;
+  const size_t rowb = static_cast<size_t>(d) * sizeof(T);
+  f32x4_t acc[TL::FM][TL::FN];
+  for (int n0h = 0; n0h < I; n0h += HC) {
+    const char* src[TL::LPW];
+#pragma unroll
+    for (int qq = 0; qq < TL::LPW; ++qq) {
+      const int r = stage_row<TL>(qq);
+      const char* base;
+      if (r < TL::BM) {
+        const int ar = r < rows ? r : 0;
+        base = static_cast<const char*>(q.x) + (q.t0 + q.row_tok[row0 + ar]) * rowb;
+      } else {
+        const int br = r - TL::BM;
+        const int hc = n0h + (br < HC ? br : br - HC);
+        base = line + static_cast<int64_t>((hc < I ? hc : n0h) + (br < HC ? 0 : I)) * rowb;
+      }
+      src[qq] = base + 16 * stage_seg<TL>();
+    }
+    mainloop<T, TL, true>(src, stages<T, TL>(d), lds, acc, rows);
+    constexpr int H = TL::FN / 2;
+#pragma unroll
+    for (int i = 0; i < TL::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < H; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int row = block_row<TL>(i, 0) + 4 * kq + r;
+          const int col = n0h + wn * (TL::TN / 2) + j * 16 + l16;
+          *reinterpret_cast<T*>(hl + fused_h_off(row, col, I)) =
+              h_store<T>(silu_f32(acc[i][j][r]) * acc[i][j + H][r]);
+        }
+  }
+  __syncthreads();              // h complete; the stage buffers are free
+
+  // 2. down: weight rows of N-chunk c, K stage s, through buffer (c * nk + s) % 2
+  const int nk = stages<T, TL>(I);
+  const int G = n_dc * nk;
+  const char* wdown = line + p.line_down_off * static_cast<int64_t>(sizeof(T));
+  const size_t rowk = static_cast<size_t>(I) * sizeof(T);
+  constexpr int LPB = kFusedBStage / 1024 / TL::NW;     // load instructions per wave and stage
+  typedef __attribute__((address_space(3))) char lds_char;
+  const uint32_t wave_lds = __builtin_amdgcn_readfirstlane(
+      static_cast<uint32_t>((uintptr_t)(lds_char*)lds) + static_cast<uint32_t>(wave * 1024));
+  const int seg16 = 16 * stage_seg<TL>();
+  auto issue_b = [&](int g) {
+    const int c = g / nk, ko = (g % nk) * TL::RB;
+    const uint32_t dst = wave_lds + static_cast<uint32_t>((g & 1) * kFusedBStage);
+#pragma unroll
+    for (int qq = 0; qq < LPB; ++qq) {
+      const int wr = c * TL::BN + (wave + TL::NW * qq) * TL::RPL + lane / TL::SPR;
+      const char* src = wdown + static_cast<int64_t>(wr < d ? wr : c * TL::BN) * rowk + ko + seg16;
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, off"
+                   :
+                   : "s"(__builtin_amdgcn_readfirstlane(dst + static_cast<uint32_t>(qq * TL::NW * 1024))),
+                     "v"(src)
+                   : "memory", "m0");
+#pragma clang diagnostic pop
+    }
+  };
+  const int sw = swz<TL>(l16);
+  int hrow[TL::FM], brow[TL::FN];
+#pragma unroll
+  for (int i = 0; i < TL::FM; ++i) hrow[i] = (block_row<TL>(i, 0) + l16) * I * 2;
+#pragma unroll
+  for (int j = 0; j < TL::FN; ++j) brow[j] = (wn * TL::TN + j * 16 + l16) * TL::RB;
+  const int nbusy = busy_blocks<TL>(rows, 0);
+#pragma unroll
+  for (int i = 0; i < TL::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < TL::FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  issue_b(0);
+  for (int g = 0; g < G; ++g) {
+    wait_vmcnt<0>();            // this wave's share of stage g (and earlier Y stores) landed
+    __syncthreads();            // everyone's; everyone also left stage g - 1
+    if (g + 1 < G) issue_b(g + 1);
+    const int s = g % nk;
+    const char* bbuf = lds + (g & 1) * kFusedBStage;
+    const char* hbase = hl + s * TL::RB;
+    constexpr int kSteps = TL::RB / F::kStepBytes;
+#pragma unroll
+    for (int ks = 0; ks < kSteps; ++ks) {
+      typename F::V b[TL::FN];
+#pragma unroll
+      for (int j = 0; j < TL::FN; ++j) b[j] = F::load(bbuf + brow[j], ks, kq, sw);
+#pragma unroll
+      for (int i = 0; i < TL::FM; ++i) {
+        if (i < nbusy) {
+          const typename F::V a = F::load(hbase + hrow[i], ks, kq, sw);
+#pragma unroll
+          for (int j = 0; j < TL::FN; ++j) acc[i][j] = F::mma(a, b[j], acc[i][j]);
+        }
+      }
+    }
+    if (s == nk - 1) {          // chunk done: its Y rows out, accumulators reset
+      store_y([&](int i, int j, int r) { return acc[i][j][r]; }, g / nk);
+#pragma unroll
+      for (int i = 0; i < TL::FM; ++i)
+#pragma unroll
+        for (int j = 0; j < TL::FN; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+  }
+  clock.finish();
+}
+
 struct RouterParams {
   const void* x;
   const void* w;
@@ -952,6 +1136,24 @@ hipError_t launch_down_routed(int dtype, const void* h, int d, int I, const Gemm
   else if (g.tile_rows == MidTile::BM) down_routed<MidTile>(dtype, p, g, d, s);
   else if (g.tile_rows == DecodeTile::BM) down_routed<DecodeTile>(dtype, p, g, d, s);
   else down_routed<SmallTile>(dtype, p, g, d, s);
+  return hipGetLastError();
+}
+
+bool gu_down_fused_supported(int dtype, int tile_rows, int I) {
+  return dtype == MOE_BF16 && tile_rows == FusedTile::BM && I > 0 && I <= kFusedMaxI &&
+         I % (FusedTile::BN / 2) == 0;
+}
+
+hipError_t launch_gu_down_fused(const void* x, int64_t t0, int d, int I, const GemmGroups& g,
+                                const int32_t* row_tok, const int32_t* row_slot, float* y,
+                                hipStream_t s) {
+  if (g.tile_cap <= 0) return hipSuccess;
+  ProfScope prof(MOE_STAGE_GU_DOWN_FUSED, s);
+  FusedParams p{};
+  p.gu.x = x; p.gu.t0 = t0; p.gu.n = 0; p.gu.d = d; p.gu.I = I; p.gu.w = nullptr; p.gu.g = g;
+  p.gu.row_tok = row_tok; p.gu.h = nullptr; p.gu.clk = prof_clock(MOE_STAGE_GU_DOWN_FUSED);
+  p.line_down_off = 2LL * I * d; p.row_slot = row_slot; p.y = y;
+  gu_down_fused_kernel<<<xcd_grid(g.tile_cap), FusedTile::NT, 0, s>>>(p);
   return hipGetLastError();
 }
 

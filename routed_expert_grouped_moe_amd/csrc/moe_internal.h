@@ -103,6 +103,12 @@ MOE_HIDDEN hipError_t launch_gu_mixed(int dtype, const void* x, int64_t t0, int6
 MOE_HIDDEN hipError_t launch_down_routed(int dtype, const void* h, int d, int I,
                                          const GemmGroups& g, const int32_t* row_slot,
                                          float* y, hipStream_t s);
+// Both routed GEMMs of each M-tile in one workgroup, h kept in LDS (bf16, 64-row tiles, I a
+// multiple of 128 up to 512: gu_down_fused_supported); writes Y only, not h.
+MOE_HIDDEN bool gu_down_fused_supported(int dtype, int tile_rows, int I);
+MOE_HIDDEN hipError_t launch_gu_down_fused(const void* x, int64_t t0, int d, int I,
+                                           const GemmGroups& g, const int32_t* row_tok,
+                                           const int32_t* row_slot, float* y, hipStream_t s);
 // The shared expert's down GEMM with the combine folded in: out rows t0 .. t0 + n - 1.
 MOE_HIDDEN hipError_t launch_down_combine(int dtype, const void* h, int64_t n, int d, int Is,
                                           const void* w_down, const float* y,

@@ -48,10 +48,24 @@ def test_ctypes_table_matches_header(abi):
 
 def test_version_and_status_strings(abi):
     L = abi.lib()
-    assert L.moe_abi_version() == 4
+    assert L.moe_abi_version() == 5
     assert L.moe_status_string(abi.MOE_OK) == b"MOE_OK"
     assert L.moe_status_string(abi.MOE_ERR_WORKSPACE) == b"MOE_ERR_WORKSPACE"
     assert L.moe_status_string(99) == b"MOE_ERR_UNKNOWN"
+
+
+def test_options(abi):
+    L = abi.lib()
+    v = ctypes.c_int32(-1)
+    assert L.moe_get_option(abi.OPTIONS["fused_gu_down"], ctypes.byref(v)) == abi.MOE_OK
+    assert v.value == 0                     # off until set
+    assert L.moe_set_option(abi.OPTIONS["fused_gu_down"], 7) == abi.MOE_OK
+    assert L.moe_get_option(abi.OPTIONS["fused_gu_down"], ctypes.byref(v)) == abi.MOE_OK
+    assert v.value == 1
+    assert L.moe_set_option(abi.OPTIONS["fused_gu_down"], 0) == abi.MOE_OK
+    assert L.moe_set_option(99, 1) == abi.MOE_ERR_INVALID
+    assert b"option" in L.moe_last_error()
+    assert L.moe_get_option(abi.OPTIONS["fused_gu_down"], None) == abi.MOE_ERR_INVALID
 
 
 def _shape(abi, d=128, E=8, k=2, I=64, Is=64, dt=0):

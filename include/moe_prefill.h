@@ -150,7 +150,9 @@ moe_status moe_prefill_route(const moe_layer* layer, const void* x, int64_t T, i
  * fused silu(gate)*up epilogue and its down GEMM (grouped, bf16 MFMA, fp32 accumulation), the
  * shared expert over all n rows, then the fixed-order combine into out rows t0..t0+n-1. With a
  * shared expert its down GEMM runs last and forms the combine in its epilogue (same operations
- * in the same order as the stand-alone combine, so the same bits).
+ * in the same order as the stand-alone combine, so the same bits); for chunks of at most 16
+ * tokens with every expert resident, the shared expert's tiles run instead inside the routed
+ * gate/up and down launches, the down writing S, and the stand-alone combine follows.
  *   x, ids, weights: the whole prompt's tensors as passed to / returned by moe_prefill_route
  *   counts_host  HOST [E] int32 expert counts of this chunk, or NULL. Only used with a ring: if
  *                NULL the call copies the counts to the host and waits for them (its only
@@ -309,10 +311,11 @@ moe_status moe_get_option(int32_t option, int32_t* value);
 /* Per-kernel timing with HIP events. While enabled, every launch the library enqueues is
  * bracketed by two timing events recorded on the launch's own stream; moe_profile_read waits
  * for the recorded events and adds their elapsed times to per-stage totals. The GEMM kernels
- * also sample the shader clock (thread 0 of every workgroup, start to last store) into 256
+ * also sample the shader clock (thread 0 of every workgroup, start to last store) into 512
  * bytes of counters held in the library's own device code object (one copy per device; no
  * allocation). Process-wide and thread-safe; off by default (then nothing is recorded).
- * Version 2 of moe_profile_t adds clock_mhz. */
+ * Version 2 of moe_profile_t added clock_mhz; version 3 has MOE_PROFILE_SLOTS entries per
+ * array. */
 enum {
   MOE_STAGE_ROUTER = 0,     /* router GEMM */
   MOE_STAGE_TOPK = 1,       /* top-k + weights */
@@ -322,8 +325,9 @@ enum {
   MOE_STAGE_SCAN = 5,       /* expert offsets and M-tile list */
   MOE_STAGE_PERMUTE = 6,    /* stable member-list permute */
   MOE_STAGE_GU_SHARED = 7,
-  MOE_STAGE_DOWN_SHARED = 8,  /* shared down GEMM alone (S); unused by the layer calls since
-                                 version 3, which fold it into the combine (stage 13) */
+  MOE_STAGE_DOWN_SHARED = 8,  /* shared down GEMM alone (S); unused by the layer calls, which
+                                 fold it into the combine (stage 13) or, for chunks of at most
+                                 16 tokens, into the routed down launch (stage 16) */
   MOE_STAGE_GU_ROUTED = 9,
   MOE_STAGE_DOWN_ROUTED = 10,
   MOE_STAGE_COMBINE = 11,    /* the combine alone: layers without a shared expert */
@@ -333,15 +337,18 @@ enum {
                                tall or big routed tiles) */
   MOE_STAGE_GU_DOWN_FUSED = 15, /* routed gate/up and down GEMMs in one launch, h kept on chip
                                    (MOE_OPT_FUSED_GU_DOWN) */
-  MOE_STAGE_COUNT = 16
+  MOE_STAGE_DOWN_MIXED = 16, /* the shared expert's down GEMM (S alone) and the routed down GEMM
+                                in one launch (chunks of at most 16 tokens, experts resident) */
+  MOE_STAGE_COUNT = 17
 };
+#define MOE_PROFILE_SLOTS 32    /* entries per array of moe_profile_t (>= MOE_STAGE_COUNT) */
 
 typedef struct {
-  int32_t version;          /* 1 */
+  int32_t version;          /* 3 (version 2 had 16 entries per array) */
   int32_t n_stages;         /* MOE_STAGE_COUNT */
-  double ms[16];            /* summed kernel time per stage, milliseconds */
-  int64_t launches[16];     /* launches per stage */
-  double clock_mhz[16];     /* GEMM stages: mean shader clock over their workgroups' lifetimes,
+  double ms[MOE_PROFILE_SLOTS];       /* summed kernel time per stage, milliseconds */
+  int64_t launches[MOE_PROFILE_SLOTS];/* launches per stage */
+  double clock_mhz[MOE_PROFILE_SLOTS];/* GEMM stages: mean shader clock over their workgroups' lifetimes,
                                sampled with s_memtime against s_memrealtime (100 MHz); 0 when
                                not sampled */
 } moe_profile_t;

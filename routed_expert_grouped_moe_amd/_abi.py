@@ -33,13 +33,13 @@ class MoeWsOffsets(ctypes.Structure):
 
 
 class MoeProfile(ctypes.Structure):
-    _fields_ = [("version", c_i32), ("n_stages", c_i32), ("ms", ctypes.c_double * 16),
-                ("launches", c_i64 * 16), ("clock_mhz", ctypes.c_double * 16)]
+    _fields_ = [("version", c_i32), ("n_stages", c_i32), ("ms", ctypes.c_double * 32),
+                ("launches", c_i64 * 32), ("clock_mhz", ctypes.c_double * 32)]
 
 
 STAGES = ["router", "topk", "chunk_counts", "table", "hist", "scan", "permute", "gu_shared",
           "down_shared", "gu_routed", "down_routed", "combine", "rmsnorm", "down_shared_combine",
-          "gu_mixed", "gu_down_fused"]
+          "gu_mixed", "gu_down_fused", "down_mixed"]
 
 OPTIONS = {"fused_gu_down": 1}       # MOE_OPT_* of include/moe_prefill.h
 

@@ -132,6 +132,21 @@ struct SideStream {
   hipError_t join(hipStream_t s) { return hipStreamWaitEvent(s, done_ev, 0); }
 };
 
+// Joins the side work into the caller's stream on every early return after it was forked, so
+// the caller's stream never runs ahead of work that still writes the workspace.
+struct JoinOnExit {
+  SideStream& side;
+  hipStream_t s;
+  bool armed = false;
+  ~JoinOnExit() {
+    if (armed) (void)side.join(s);
+  }
+  hipError_t join() {
+    armed = false;
+    return side.join(s);
+  }
+};
+
 // True when line e is at lines[0] + e * stride for every e (one block of E lines).
 bool uniform_lines(const void* const* lines, int E, int64_t* stride) {
   const uintptr_t b = reinterpret_cast<uintptr_t>(lines[0]);
@@ -318,12 +333,17 @@ moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const i
   // (joined before the last kernel), filling the time the routed GEMMs wait for copies. Its
   // down GEMM runs last, with the combine folded into its epilogue.
   SideStream side;
+  JoinOnExit pending{side, s};
   hipStream_t ss = offloaded ? nullptr : s;
   const int bm = routed_tile_rows(n, k, E);
   // With every expert resident and tall or big routed tiles, the shared GU's units join the
   // routed GU's launch (launch_gu_mixed), so the compute-bound shared tiles run beside the
-  // weight-streaming routed ones.
-  const bool mixed = !offloaded && sh.inter_shared && gu_mixed_supported(bm);
+  // weight-streaming routed ones. A chunk of at most kSmallChunkRows tokens (decode tiles)
+  // does the same with both shared GEMMs: alone, each would fill a few dozen CUs and wait on
+  // load latency. Its shared down GEMM then writes S to the workspace and the stand-alone
+  // combine follows (the same operations in the same order as the folded one, the same bits).
+  const bool mixed = !offloaded && sh.inter_shared && gu_mixed_supported(bm, n);
+  const bool small = mixed && n <= kSmallChunkRows && bm == kSmallChunkRows;
   if (sh.inter_shared && !mixed) {
     if (offloaded) {
       MOE_HIP(side.fork(s));
@@ -331,7 +351,10 @@ moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const i
     }
     MOE_HIP(launch_gu_dense(sh.dtype, x, t0, n, sh.d, sh.inter_shared, L->w_gu_shared,
                             ws + W.h_shared, ss));
-    if (offloaded) MOE_HIP(side.record_done());
+    if (offloaded) {
+      MOE_HIP(side.record_done());
+      pending.armed = true;
+    }
   }
   // Resident lines at a uniform stride (one block of E lines) need no table; otherwise the
   // table is uploaded to the workspace (offloaded entries are filled per wave).
@@ -349,6 +372,16 @@ moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const i
                  static_cast<int>(n * k / bm + std::min<int64_t>(E, n * k)), bm};
     const int32_t* row_tok = reinterpret_cast<const int32_t*>(ws + W.row_tok);
     const int32_t* row_slot = reinterpret_cast<const int32_t*>(ws + W.row_slot);
+    if (small) {
+      float* s_small = reinterpret_cast<float*>(ws + W.s_small);
+      MOE_HIP(launch_gu_mixed(sh.dtype, x, t0, n, sh.d, sh.inter, sh.inter_shared,
+                              L->w_gu_shared, ws + W.h_shared, g, row_tok, ws + W.h, s));
+      MOE_HIP(launch_down_mixed(sh.dtype, ws + W.h_shared, n, sh.d, sh.inter_shared,
+                                L->w_down_shared, s_small, ws + W.h, sh.inter, g, row_slot, y,
+                                s));
+      MOE_HIP(launch_combine(sh.dtype, y, s_small, weights, t0, n, k, sh.d, out, s));
+      return MOE_OK;
+    }
     if (mixed) {
       MOE_HIP(launch_gu_mixed(sh.dtype, x, t0, n, sh.d, sh.inter, sh.inter_shared,
                               L->w_gu_shared, ws + W.h_shared, g, row_tok, ws + W.h, s));
@@ -359,7 +392,7 @@ moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const i
   } else {
     moe_status st = ring_waves(L, x, t0, n, counts_host, ws, W, s, cs ? cs : s);
     // Join even on failure, so the caller's stream never runs ahead of the side work.
-    if (sh.inter_shared) MOE_HIP(side.join(s));
+    if (pending.armed) MOE_HIP(pending.join());
     if (st != MOE_OK) return st;
   }
   if (sh.inter_shared)
@@ -439,6 +472,7 @@ bool ws_layout(const moe_shape& sh, int64_t max_n, WsLayout* L) {
   L->h = take(elt * rows * I);
   L->h_shared = take(elt * max_n * Is);
   L->y = take(sizeof(float) * rows * d);
+  L->s_small = take(Is ? sizeof(float) * std::min<int64_t>(max_n, kSmallChunkRows) * d : 0);
   L->total = off;
   L->max_n = max_n;
   L->max_rows = rows;

@@ -103,10 +103,10 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       const int c = c0 + 1024 * u;
       if (shared) {
         const float4 s = *reinterpret_cast<const float4*>(shared + t * d + c);
-        acc[u].x += s.x;
-        acc[u].y += s.y;
-        acc[u].z += s.z;
-        acc[u].w += s.w;
+        acc[u].x = routed_sum<T>(acc[u].x) + s.x;
+        acc[u].y = routed_sum<T>(acc[u].y) + s.y;
+        acc[u].z = routed_sum<T>(acc[u].z) + s.z;
+        acc[u].w = routed_sum<T>(acc[u].w) + s.w;
       }
       Pack4<T>::store(out + (t0 + t) * d + c, acc[u]);
     }

@@ -631,27 +631,59 @@ struct DownParams {
   GemmGroups g;           // grouped: routed experts (down part of each line)
   int64_t line_down_off;  // grouped: element offset of W_down inside a line (2*I*d)
   const int32_t* row_slot;// grouped: output row (t*k + j) of each permuted row
-  float* out;             // grouped: Y [n*k, d]
+  float* out;             // grouped: Y [n*k, d]; dense without cout: S [n, d]
   unsigned long long* clk;   // profiling clock counters of the stage, or NULL
   // dense (the shared expert), with the combine in the epilogue; S stays in registers:
   const float* y;         // Y [n*k, d], unweighted fp32 rows of the routed experts
   const float* wts;       // [T, k] slot weights, row t0 + t for chunk token t
   int64_t t0;             // first prompt row of the chunk
   int k;                  // slots per token
-  void* cout;             // [T, d] layer output (dtype), rows t0 .. t0 + n - 1 written
+  void* cout;             // [T, d] layer output (dtype), rows t0 .. t0 + n - 1 written; NULL:
+                          // the dense GEMM writes S to `out` instead
 };
+
+// Work units (M-tile x N-tile) of a down launch; a tile-list entry taller than this tile shape
+// is worked as tile_rows / BM stacked tiles.
+template <class TL, bool kGrouped>
+__device__ __forceinline__ int down_units(const DownParams& p) {
+  const int NT = (p.d + TL::BN - 1) / TL::BN;
+  const int sub = kGrouped ? p.g.tile_rows / TL::BM : 1;
+  const int m_tiles = kGrouped ? max(0, min(p.g.tile_cap, *p.g.n_mtiles - p.g.tile_lo)) * sub
+                               : static_cast<int>((p.n + TL::BM - 1) / TL::BM);
+  return m_tiles * NT;
+}
+
+template <typename T, class TL, bool kGrouped>
+__device__ __forceinline__ void down_tile(const DownParams& p, int t, char* lds);
 
 template <typename T, class TL, bool kGrouped>
 __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(2)))
 void down_kernel(DownParams p) {
   __shared__ __attribute__((aligned(1024))) char lds[TL::LDS];
-  const int NT = (p.d + TL::BN - 1) / TL::BN;
-  // a tile-list entry taller than this tile shape is worked as `sub` stacked tiles
-  const int sub = kGrouped ? p.g.tile_rows / TL::BM : 1;
-  const int m_tiles = kGrouped ? max(0, min(p.g.tile_cap, *p.g.n_mtiles - p.g.tile_lo)) * sub
-                               : static_cast<int>((p.n + TL::BM - 1) / TL::BM);
   int t;
-  if (!xcd_tile(m_tiles * NT, &t)) return;
+  if (!xcd_tile(down_units<TL, kGrouped>(p), &t)) return;
+  down_tile<T, TL, kGrouped>(p, t, lds);
+}
+
+// The shared expert's down units (S alone) and the routed ones in one launch (shared units
+// first), as gu_mixed_kernel does for the gate/up GEMMs: the same tiles, so the same bits.
+template <typename T, class TL>
+__global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(2)))
+void down_mixed_kernel(DownParams shared, DownParams routed) {
+  __shared__ __attribute__((aligned(1024))) char lds[TL::LDS];
+  const int ns = down_units<TL, false>(shared);
+  int t;
+  if (!xcd_tile(ns + down_units<TL, true>(routed), &t)) return;
+  if (t < ns)
+    down_tile<T, TL, false>(shared, t, lds);
+  else
+    down_tile<T, TL, true>(routed, t - ns, lds);
+}
+
+template <typename T, class TL, bool kGrouped>
+__device__ __forceinline__ void down_tile(const DownParams& p, int t, char* lds) {
+  const int NT = (p.d + TL::BN - 1) / TL::BN;
+  const int sub = kGrouped ? p.g.tile_rows / TL::BM : 1;
   ClockSample clock(p.clk);
   const int mi = t / NT;
   const int n0 = (t % NT) * TL::BN;
@@ -714,9 +746,15 @@ void down_kernel(DownParams p) {
     __builtin_amdgcn_wave_barrier();  // a wave's LDS writes land before its later LDS reads
     auto row_of = [&](int sr) -> int64_t { return tab[sr]; };   // sr = block * 16 + row
     store_slab<TL, float, TL::TN, true>(lds, val, row_of, p.out, p.d, col0, min(TL::TN, p.d - col0));
-  } else {
+  } else if (p.cout) {
     combine_slab<TL, T>(lds, val, wm, row0, rows, p.y, p.wts, p.t0, p.k, p.d,
                         static_cast<T*>(p.cout), col0, min(TL::TN, p.d - col0));
+  } else {                      // the shared expert's S alone (fp32), for the stand-alone combine
+    auto row_of = [&](int sr) -> int64_t {
+      const int tr = block_row<TL>(sr >> 4, wm) + (sr & 15);
+      return tr < rows ? row0 + tr : -1;
+    };
+    store_slab<TL, float, TL::TN>(lds, val, row_of, p.out, p.d, col0, min(TL::TN, p.d - col0));
   }
   clock.finish();
 }
@@ -1052,8 +1090,9 @@ static void gu_mixed(int dtype, const GuParams& ps, const GuParams& pr, hipStrea
   else gu_mixed_kernel<float, TL><<<grid, TL::NT, 0, s>>>(ps, pr);
 }
 
-bool gu_mixed_supported(int tile_rows) {
-  return tile_rows == TallTile::BM || tile_rows == BigTile::BM;
+bool gu_mixed_supported(int tile_rows, int64_t n) {
+  return tile_rows == TallTile::BM || tile_rows == BigTile::BM ||
+         (tile_rows == DecodeTile::BM && n <= DecodeTile::BM);
 }
 
 hipError_t launch_gu_mixed(int dtype, const void* x, int64_t t0, int64_t n, int d, int I, int Is,
@@ -1067,7 +1106,29 @@ hipError_t launch_gu_mixed(int dtype, const void* x, int64_t t0, int64_t n, int 
   pr.x = x; pr.t0 = t0; pr.n = 0; pr.d = d; pr.I = I; pr.w = nullptr; pr.g = g;
   pr.row_tok = row_tok; pr.h = h; pr.clk = ps.clk;
   if (g.tile_rows == TallTile::BM) gu_mixed<TallTile>(dtype, ps, pr, s);
-  else gu_mixed<BigTile>(dtype, ps, pr, s);
+  else if (g.tile_rows == BigTile::BM) gu_mixed<BigTile>(dtype, ps, pr, s);
+  else if (g.tile_rows == DecodeTile::BM && n <= DecodeTile::BM) gu_mixed<DecodeTile>(dtype, ps, pr, s);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+hipError_t launch_down_mixed(int dtype, const void* h_shared, int64_t n, int d, int Is,
+                             const void* w_down_shared, float* s_out, const void* h, int I,
+                             const GemmGroups& g, const int32_t* row_slot, float* y,
+                             hipStream_t s) {
+  using TL = DecodeTile;
+  if (n <= 0) return hipSuccess;
+  if (g.tile_rows != TL::BM || n > TL::BM) return hipErrorInvalidValue;
+  ProfScope prof(MOE_STAGE_DOWN_MIXED, s);
+  DownParams ps{}, pr{};
+  ps.h = h_shared; ps.n = n; ps.d = d; ps.K = Is; ps.w = w_down_shared; ps.out = s_out;
+  ps.clk = prof_clock(MOE_STAGE_DOWN_MIXED);
+  pr.h = h; pr.n = 0; pr.d = d; pr.K = I; pr.w = nullptr; pr.g = g;
+  pr.line_down_off = 2LL * I * d; pr.row_slot = row_slot; pr.out = y; pr.clk = ps.clk;
+  const int64_t nt = (d + TL::BN - 1) / TL::BN;
+  const unsigned grid = xcd_grid((n + TL::BM - 1) / TL::BM * nt + static_cast<int64_t>(g.tile_cap) * nt);
+  if (dtype == MOE_BF16) down_mixed_kernel<uint16_t, TL><<<grid, TL::NT, 0, s>>>(ps, pr);
+  else down_mixed_kernel<float, TL><<<grid, TL::NT, 0, s>>>(ps, pr);
   return hipGetLastError();
 }
 
@@ -1157,15 +1218,8 @@ hipError_t launch_gu_down_fused(const void* x, int64_t t0, int d, int I, const G
   return hipGetLastError();
 }
 
-hipError_t launch_down_combine(int dtype, const void* h, int64_t n, int d, int Is,
-                               const void* w_down, const float* y, const float* weights,
-                               int64_t t0, int k, void* out, hipStream_t s) {
-  if (n <= 0 || Is <= 0) return hipSuccess;
-  ProfScope prof(MOE_STAGE_DOWN_SHARED_COMBINE, s);
-  DownParams p{};
-  p.h = h; p.n = n; p.d = d; p.K = Is; p.w = w_down; p.line_down_off = 0;
-  p.row_slot = nullptr; p.out = nullptr; p.clk = prof_clock(MOE_STAGE_DOWN_SHARED_COMBINE);
-  p.y = y; p.wts = weights; p.t0 = t0; p.k = k; p.cout = out;
+// Tile choice of the dense (shared-expert) down GEMM, with or without the combine.
+static void down_dense(int dtype, const DownParams& p, int64_t n, int d, hipStream_t s) {
   const int64_t nt_big = (d + BigTile::BN - 1) / BigTile::BN;
   if (n <= DecodeTile::BM) {
     const unsigned grid = xcd_grid((d + DecodeTile::BN - 1) / DecodeTile::BN);
@@ -1200,6 +1254,18 @@ hipError_t launch_down_combine(int dtype, const void* h, int64_t n, int d, int I
     if (dtype == MOE_BF16) down_kernel<uint16_t, SmallTile, false><<<grid, SmallTile::NT, 0, s>>>(p);
     else down_kernel<float, SmallTile, false><<<grid, SmallTile::NT, 0, s>>>(p);
   }
+}
+
+hipError_t launch_down_combine(int dtype, const void* h, int64_t n, int d, int Is,
+                               const void* w_down, const float* y, const float* weights,
+                               int64_t t0, int k, void* out, hipStream_t s) {
+  if (n <= 0 || Is <= 0) return hipSuccess;
+  ProfScope prof(MOE_STAGE_DOWN_SHARED_COMBINE, s);
+  DownParams p{};
+  p.h = h; p.n = n; p.d = d; p.K = Is; p.w = w_down; p.line_down_off = 0;
+  p.row_slot = nullptr; p.out = nullptr; p.clk = prof_clock(MOE_STAGE_DOWN_SHARED_COMBINE);
+  p.y = y; p.wts = weights; p.t0 = t0; p.k = k; p.cout = out;
+  down_dense(dtype, p, n, d, s);
   return hipGetLastError();
 }
 

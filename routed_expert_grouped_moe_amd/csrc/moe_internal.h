@@ -15,6 +15,9 @@ namespace moe {
 // ------------------------------------------------------------------ tiling constants
 constexpr int kMinTileRows = 16;  // smallest M-tile height of the routed GEMMs
 constexpr int kTokBlock = 256;    // tokens per block of the bucketing kernels
+// Chunks of at most this many tokens (one decode tile) run the shared expert's tiles inside
+// the routed launches and the stand-alone combine after them.
+constexpr int kSmallChunkRows = 16;
 
 // ------------------------------------------------------------------ device-side records
 struct MTile {                    // one M-tile of a routed expert: rows [m0, m0 + tile rows)
@@ -25,7 +28,7 @@ struct MTile {                    // one M-tile of a routed expert: rows [m0, m0
 // Workspace layout for chunks of up to max_n tokens (all offsets 256-byte aligned).
 struct WsLayout {
   size_t wtab, blk_counts, blk_base, counts, offsets, meta, mtiles, row_tok, row_slot;
-  size_t h, h_shared, y, total;
+  size_t h, h_shared, y, s_small, total;
   int64_t max_n, max_rows, max_mtiles, n_blocks;
 };
 MOE_HIDDEN bool ws_layout(const moe_shape& sh, int64_t max_n, WsLayout* out);
@@ -94,8 +97,9 @@ MOE_HIDDEN hipError_t launch_gu_routed(int dtype, const void* x, int64_t t0, int
 MOE_HIDDEN hipError_t launch_gu_dense(int dtype, const void* x, int64_t t0, int64_t n, int d,
                                       int Is, const void* w_gu, void* h, hipStream_t s);
 // The shared expert's gate/up GEMM and the routed one in one launch (routed M-tiles of
-// tile_rows rows, for which gu_mixed_supported holds).
-MOE_HIDDEN bool gu_mixed_supported(int tile_rows);
+// tile_rows rows for a chunk of n tokens, for which gu_mixed_supported holds: tall or big
+// tiles, or decode tiles when the chunk itself fits one).
+MOE_HIDDEN bool gu_mixed_supported(int tile_rows, int64_t n);
 MOE_HIDDEN hipError_t launch_gu_mixed(int dtype, const void* x, int64_t t0, int64_t n, int d,
                                       int I, int Is, const void* w_gu_shared, void* h_shared,
                                       const GemmGroups& g, const int32_t* row_tok, void* h,
@@ -114,6 +118,12 @@ MOE_HIDDEN hipError_t launch_down_combine(int dtype, const void* h, int64_t n, i
                                           const void* w_down, const float* y,
                                           const float* weights, int64_t t0, int k, void* out,
                                           hipStream_t s);
+// The shared expert's down GEMM (S alone) and the routed one in one launch, for a chunk of at
+// most 16 tokens on decode tiles (g.tile_rows == 16).
+MOE_HIDDEN hipError_t launch_down_mixed(int dtype, const void* h_shared, int64_t n, int d,
+                                        int Is, const void* w_down_shared, float* s_out,
+                                        const void* h, int I, const GemmGroups& g,
+                                        const int32_t* row_slot, float* y, hipStream_t s);
 MOE_HIDDEN hipError_t launch_combine(int dtype, const float* y, const float* shared,
                                      const float* weights, int64_t t0, int64_t n, int k, int d,
                                      void* out, hipStream_t s);

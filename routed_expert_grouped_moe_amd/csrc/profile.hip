@@ -18,15 +18,17 @@ std::mutex g_mu;
 bool g_on = false;
 std::vector<Pending> g_pending;
 std::vector<hipEvent_t> g_pool;
-double g_ms[16];
-int64_t g_n[16];
-double g_clk[16], g_rt[16];                        // summed clock samples read back so far
-std::unordered_map<int, unsigned long long*> g_clk_dev;   // per device: [16][2] counters
+double g_ms[MOE_PROFILE_SLOTS];
+int64_t g_n[MOE_PROFILE_SLOTS];
+double g_clk[MOE_PROFILE_SLOTS], g_rt[MOE_PROFILE_SLOTS];                        // summed clock samples read back so far
+std::unordered_map<int, unsigned long long*> g_clk_dev;   // per device: [slots][2] counters
 
 // The clock counters live in a device array of the library's own code object (each device
 // holds its own copy), so profiling allocates no device memory. In host code the array's name
 // is only a stand-in: its device address comes from hipGetSymbolAddress, once per device.
-__device__ __align__(256) unsigned long long g_clk_counters[16 * 2];
+__device__ __align__(256) unsigned long long g_clk_counters[MOE_PROFILE_SLOTS * 2];
+
+static_assert(MOE_STAGE_COUNT <= MOE_PROFILE_SLOTS, "a profile slot per stage");
 
 hipEvent_t take_event() {   // caller holds g_mu
   if (!g_pool.empty()) {
@@ -43,14 +45,14 @@ hipEvent_t take_event() {   // caller holds g_mu
 
 unsigned long long* prof_clock(int stage) {
   std::lock_guard<std::mutex> lk(g_mu);
-  if (!g_on || stage < 0 || stage >= 16) return nullptr;
+  if (!g_on || stage < 0 || stage >= MOE_PROFILE_SLOTS) return nullptr;
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return nullptr;
   unsigned long long*& buf = g_clk_dev[dev];
   if (!buf) {
     void* p = nullptr;
     if (hipGetSymbolAddress(&p, HIP_SYMBOL(g_clk_counters)) != hipSuccess || !p) return nullptr;
-    if (hipMemset(p, 0, 16 * 2 * sizeof(unsigned long long)) != hipSuccess) return nullptr;
+    if (hipMemset(p, 0, MOE_PROFILE_SLOTS * 2 * sizeof(unsigned long long)) != hipSuccess) return nullptr;
     buf = static_cast<unsigned long long*>(p);
   }
   return buf + 2 * stage;
@@ -107,7 +109,7 @@ moe_status moe_profile_read(moe_profile_t* out, int32_t reset) {
   moe::g_pending.clear();
   for (auto& kv : moe::g_clk_dev) {              // every launch read above has completed
     if (!kv.second) continue;
-    unsigned long long h[32];
+    unsigned long long h[MOE_PROFILE_SLOTS * 2];
     int cur = 0;
     hipError_t err = hipGetDevice(&cur);
     if (err == hipSuccess) err = hipSetDevice(kv.first);
@@ -118,14 +120,14 @@ moe_status moe_profile_read(moe_profile_t* out, int32_t reset) {
       if (st == MOE_OK) st = moe::set_error(MOE_ERR_HIP, "profile clocks: %s", hipGetErrorString(err));
       continue;
     }
-    for (int i = 0; i < 16; ++i) {
+    for (int i = 0; i < MOE_PROFILE_SLOTS; ++i) {
       moe::g_clk[i] += static_cast<double>(h[2 * i]);
       moe::g_rt[i] += static_cast<double>(h[2 * i + 1]);
     }
   }
-  out->version = 2;
+  out->version = 3;
   out->n_stages = MOE_STAGE_COUNT;
-  for (int i = 0; i < 16; ++i) {
+  for (int i = 0; i < MOE_PROFILE_SLOTS; ++i) {
     out->ms[i] = moe::g_ms[i];
     out->launches[i] = moe::g_n[i];
     out->clock_mhz[i] = moe::g_rt[i] > 0 ? moe::g_clk[i] / moe::g_rt[i] * 100.0 : 0.0;

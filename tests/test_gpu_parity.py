@@ -412,16 +412,43 @@ def test_profile_times_and_clocks(moe):
     assert all(v[1] == 0 for v in moe.moe_profile_read(reset=True).values())
 
 
-def test_graph_capture_resident_layer(moe):
+def test_small_chunks_mix_the_shared_expert_in(moe):
+    """Chunks of at most 16 tokens run the shared expert's tiles inside the routed gate/up and
+    down launches and the stand-alone combine after them; larger chunks fold the combine into
+    the shared down GEMM. Both give the batched pass's bytes."""
+    wl = mi.custom_workload("side", T=100, d=256, E=32, k=4, inter=128, inter_shared=256,
+                            zipf_s=1.1, seed=19)
+    params, L = place(wl)
+    x = mi.make_x(wl, device="cuda")
+    base = _run(moe, L, x, wl.T)
+    for chunk in (16, 17, 5):
+        moe.moe_profile_read(reset=True)
+        moe.moe_profile_enable(True)
+        try:
+            got = _run(moe, L, x, chunk)
+            torch.cuda.synchronize()
+        finally:
+            moe.moe_profile_enable(False)
+        prof = moe.moe_profile_read(reset=True)
+        sizes = [min(chunk, wl.T - t0) for t0 in range(0, wl.T, chunk)]
+        n_small = sum(n <= 16 for n in sizes)
+        assert prof["gu_mixed"][1] == n_small and prof["down_mixed"][1] == n_small
+        assert prof["combine"][1] == n_small and prof["down_shared"][1] == 0
+        assert prof["down_shared_combine"][1] == len(sizes) - n_small
+        assert torch.equal(bits(got["out"]), bits(base["out"])), chunk
+
+
+@pytest.mark.parametrize("T,chunk", [(600, 128), (40, 8)])
+def test_graph_capture_resident_layer(moe, T, chunk):
     """With every expert resident a layer call enqueues kernels only (no allocation, host
     synchronisation or memset), so the whole call (route + 5 chunks) can be captured in a HIP
-    graph. Replays, with eager work and synchronisation between them, give the eager bytes
+    graph (chunks of 128 tokens, and of 8, whose shared expert runs inside the routed
+    launches). Replays, with eager work and synchronisation between them, give the eager bytes
     every time."""
-    wl = mi.custom_workload("graph", T=600, d=256, E=32, k=4, inter=128, inter_shared=256,
+    wl = mi.custom_workload("graph", T=T, d=256, E=32, k=4, inter=128, inter_shared=256,
                             zipf_s=1.1, seed=17)
     params, L = place(wl)
     x = mi.make_x(wl, device="cuda")
-    chunk = 128
     eager = _run(moe, L, x, chunk)
     bufs = moe.layer_buffers(L, wl.T, chunk)
     side = torch.cuda.Stream()

@@ -170,8 +170,13 @@ moe_status route_impl(const moe_layer* L, const void* x, int64_t T, int64_t chun
   const moe_shape& sh = L->shape;
   MOE_HIP(launch_router_gemm(sh.dtype, x, L->w_router, L->router_bias, T, sh.d, sh.n_experts,
                              logits, s));
-  MOE_HIP(launch_topk(logits, T, sh.n_experts, sh.top_k, ids, weights, chunk_counts,
-                      (T + chunk - 1) / chunk * sh.n_experts, s));
+  const int64_t n_cc = (T + chunk - 1) / chunk * sh.n_experts;
+  if (topk_counts_fused(T)) {
+    MOE_HIP(launch_topk_counts_small(logits, T, sh.n_experts, sh.top_k, ids, weights, chunk,
+                                     chunk_counts, n_cc, s));
+    return MOE_OK;
+  }
+  MOE_HIP(launch_topk(logits, T, sh.n_experts, sh.top_k, ids, weights, chunk_counts, n_cc, s));
   MOE_HIP(launch_chunk_hist(ids, T, sh.top_k, sh.n_experts, chunk, chunk_counts, s));
   return MOE_OK;
 }

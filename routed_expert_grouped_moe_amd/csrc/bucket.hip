@@ -164,7 +164,10 @@ __global__ __launch_bounds__(kTokBlock) void permute_kernel(const int32_t* __res
 // (at 16 blocks the serial sums over the block histograms cost more than the launch they save:
 // 85 against 79 us per layer at 4,096-token chunks; at 8 and 4 blocks 124 against 152 and 214
 // against 303 us)
+// kOneBlock: a chunk of one token block counts its experts from its own LDS masks (the
+// popcount of expert e's mask is the block's rows of e), so it needs no histogram launch.
 constexpr int kScanBlocks = 8;
+template <bool kOneBlock>
 __global__ __launch_bounds__(kTokBlock) void permute_scan_kernel(
     const int32_t* __restrict__ ids, int64_t n, int k, int E, int bm, int nb,
     const int32_t* __restrict__ blk_counts, int32_t* __restrict__ counts,
@@ -178,17 +181,36 @@ __global__ __launch_bounds__(kTokBlock) void permute_scan_kernel(
   __shared__ uint32_t mask[kMaxE * (kTokBlock / 32)];
   const int tid = threadIdx.x, b = blockIdx.x;
   for (int w = tid; w < E * (kTokBlock / 32); w += kTokBlock) mask[w] = 0u;
+  const int64_t t = static_cast<int64_t>(b) * kTokBlock + tid;
+  const bool valid = t < n;
+  const int word = tid >> 5;
+  const uint32_t bit = 1u << (tid & 31);
+  uint64_t kept = 0;
+  auto mark = [&]() {
+    if (valid)
+      for (int j = 0; j < k; ++j)
+        if (mark_slot(mask, ids[t * k + j], E, tid) && j < 64) kept |= uint64_t{1} << j;
+  };
+  if constexpr (kOneBlock) {
+    __syncthreads();
+    mark();
+    __syncthreads();
+  }
   int32_t rows[PER], tiles[PER], rsum = 0, tsum = 0;
 #pragma unroll
   for (int q = 0; q < PER; ++q) {
     const int e = tid * PER + q;
     int32_t tot = 0, pre = 0;
-    if (e < E)
+    if (kOneBlock && e < E) {
+#pragma unroll
+      for (int w = 0; w < kTokBlock / 32; ++w) tot += __popc(mask[e * (kTokBlock / 32) + w]);
+    } else if (e < E) {
       for (int bb = 0; bb < nb; ++bb) {
         const int32_t c = blk_counts[static_cast<int64_t>(bb) * E + e];
         tot += c;
         if (bb < b) pre += c;
       }
+    }
     s_tot[e] = tot;
     s_pre[e] = pre;
     rows[q] = tot;
@@ -225,15 +247,8 @@ __global__ __launch_bounds__(kTokBlock) void permute_scan_kernel(
     meta[kMetaMTiles] = toff;
     meta[kMetaRows] = roff;
   }
-  const int64_t t = static_cast<int64_t>(b) * kTokBlock + tid;
-  const bool valid = t < n;
-  const int word = tid >> 5;
-  const uint32_t bit = 1u << (tid & 31);
-  uint64_t kept = 0;
-  if (valid)
-    for (int j = 0; j < k; ++j)
-      if (mark_slot(mask, ids[t * k + j], E, tid) && j < 64) kept |= uint64_t{1} << j;
-  __syncthreads();
+  if constexpr (!kOneBlock) mark();
+  __syncthreads();              // s_off (and the masks) complete before any thread reads them
   if (!valid) return;
   for (int j = 0; j < k; ++j) {
     const int e = ids[t * k + j];
@@ -304,6 +319,14 @@ hipError_t launch_bucket(const int32_t* ids_chunk, int64_t n, int k, int E, int 
   int32_t* meta = reinterpret_cast<int32_t*>(ws + L.meta);
   MTile* mtiles = reinterpret_cast<MTile*>(ws + L.mtiles);
   hipError_t err;
+  if (nb == 1) {                // one launch: the block counts from its own masks
+    ProfScope prof(MOE_STAGE_PERMUTE, s);
+    permute_scan_kernel<true><<<1, kTokBlock, 0, s>>>(ids_chunk, n, k, E, tile_rows, nb,
+                                                      blk_counts, counts, offsets, mtiles, meta,
+                                                      reinterpret_cast<int32_t*>(ws + L.row_tok),
+                                                      reinterpret_cast<int32_t*>(ws + L.row_slot));
+    return hipGetLastError();
+  }
   {
     ProfScope prof(MOE_STAGE_HIST, s);
     block_hist_kernel<<<nb, kTokBlock, 0, s>>>(ids_chunk, n, k, E, blk_counts);
@@ -312,10 +335,10 @@ hipError_t launch_bucket(const int32_t* ids_chunk, int64_t n, int k, int E, int 
   if (err != hipSuccess) return err;
   if (nb <= kScanBlocks) {
     ProfScope prof(MOE_STAGE_PERMUTE, s);
-    permute_scan_kernel<<<nb, kTokBlock, 0, s>>>(ids_chunk, n, k, E, tile_rows, nb, blk_counts,
-                                                 counts, offsets, mtiles, meta,
-                                                 reinterpret_cast<int32_t*>(ws + L.row_tok),
-                                                 reinterpret_cast<int32_t*>(ws + L.row_slot));
+    permute_scan_kernel<false><<<nb, kTokBlock, 0, s>>>(ids_chunk, n, k, E, tile_rows, nb,
+                                                        blk_counts, counts, offsets, mtiles, meta,
+                                                        reinterpret_cast<int32_t*>(ws + L.row_tok),
+                                                        reinterpret_cast<int32_t*>(ws + L.row_slot));
     return hipGetLastError();
   }
   {

@@ -57,6 +57,13 @@ MOE_HIDDEN hipError_t launch_router_gemm(int dtype, const void* x, const void* w
 // Also zeroes n_zero ints at `zero` (the per-chunk counts launch_chunk_hist then adds to).
 MOE_HIDDEN hipError_t launch_topk(const float* logits, int64_t T, int E, int k, int32_t* ids,
                                   float* weights, int32_t* zero, int64_t n_zero, hipStream_t s);
+// Top-k and the per-chunk counts of a prompt of at most 16 tokens in one launch
+// (topk_counts_fused(T)); zeroes the n_cc counts itself.
+MOE_HIDDEN bool topk_counts_fused(int64_t T);
+MOE_HIDDEN hipError_t launch_topk_counts_small(const float* logits, int64_t T, int E, int k,
+                                               int32_t* ids, float* weights, int64_t chunk,
+                                               int32_t* chunk_counts, int64_t n_cc,
+                                               hipStream_t s);
 // chunk_counts must be zero on entry (launch_topk zeroes them).
 MOE_HIDDEN hipError_t launch_chunk_hist(const int32_t* ids, int64_t T, int k, int E,
                                         int64_t chunk, int32_t* chunk_counts, hipStream_t s);

@@ -40,6 +40,34 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
   topk_select<NJ, 1>(x, E, k, act, idr, wr, exr);
 }
 
+// A prompt of at most 16 tokens in one workgroup: one wavefront per token as above, then the
+// same workgroup zeroes the per-chunk counts and adds every slot to them (one launch instead
+// of two; integer counts, so the order of the adds is free).
+constexpr int kSmallTopkTokens = 16;
+template <int NJ>
+__global__ __launch_bounds__(64 * kSmallTopkTokens) void topk_counts_small_kernel(
+    const float* __restrict__ logits, int64_t T, int E, int k, int32_t* __restrict__ ids,
+    float* __restrict__ weights, int64_t chunk, int32_t* __restrict__ cc, int64_t n_cc) {
+  __shared__ float ex[kSmallTopkTokens][1024];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int64_t t = wv;
+  float x[1][NJ];
+#pragma unroll
+  for (int j = 0; j < NJ; ++j) {
+    const int e = lane + 64 * j;
+    x[0][j] = (t < T && e < E) ? logits[t * E + e] : -INFINITY;
+  }
+  const bool act[1] = {t < T};
+  int32_t* const idr[1] = {ids + t * k};
+  float* const wr[1] = {weights + t * k};
+  float* const exr[1] = {ex[wv]};
+  topk_select<NJ, 1>(x, E, k, act, idr, wr, exr);
+  for (int64_t i = threadIdx.x; i < n_cc; i += blockDim.x) cc[i] = 0;
+  __syncthreads();              // ids written and counts zeroed, for the whole workgroup
+  for (int64_t i = threadIdx.x; i < T * k; i += blockDim.x)
+    atomicAdd(&cc[(i / k / chunk) * E + ids[i]], 1);
+}
+
 // Per-chunk expert counts. Block b covers tokens [256 b, 256 b + 256); when the chunks it
 // spans fit an LDS histogram it counts there and adds each nonzero bin to the global counts
 // once, else it adds every slot directly. Integer counts, so the order of the adds is free.
@@ -93,6 +121,23 @@ hipError_t launch_topk(const float* logits, int64_t T, int E, int k, int32_t* id
   else if (nj <= 4) topk_kernel<4><<<blocks, 256, 0, s>>>(logits, T, E, k, ids, weights, zero, n_zero);
   else if (nj <= 8) topk_kernel<8><<<blocks, 256, 0, s>>>(logits, T, E, k, ids, weights, zero, n_zero);
   else topk_kernel<16><<<blocks, 256, 0, s>>>(logits, T, E, k, ids, weights, zero, n_zero);
+  return hipGetLastError();
+}
+
+bool topk_counts_fused(int64_t T) { return T > 0 && T <= kSmallTopkTokens; }
+
+hipError_t launch_topk_counts_small(const float* logits, int64_t T, int E, int k, int32_t* ids,
+                                    float* weights, int64_t chunk, int32_t* chunk_counts,
+                                    int64_t n_cc, hipStream_t s) {
+  if (!topk_counts_fused(T)) return hipErrorInvalidValue;
+  ProfScope prof(MOE_STAGE_TOPK, s);
+  const unsigned threads = static_cast<unsigned>(64 * T);
+  const int nj = (E + 63) / 64;
+  if (nj <= 1) topk_counts_small_kernel<1><<<1, threads, 0, s>>>(logits, T, E, k, ids, weights, chunk, chunk_counts, n_cc);
+  else if (nj <= 2) topk_counts_small_kernel<2><<<1, threads, 0, s>>>(logits, T, E, k, ids, weights, chunk, chunk_counts, n_cc);
+  else if (nj <= 4) topk_counts_small_kernel<4><<<1, threads, 0, s>>>(logits, T, E, k, ids, weights, chunk, chunk_counts, n_cc);
+  else if (nj <= 8) topk_counts_small_kernel<8><<<1, threads, 0, s>>>(logits, T, E, k, ids, weights, chunk, chunk_counts, n_cc);
+  else topk_counts_small_kernel<16><<<1, threads, 0, s>>>(logits, T, E, k, ids, weights, chunk, chunk_counts, n_cc);
   return hipGetLastError();
 }
 

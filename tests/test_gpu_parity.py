@@ -351,12 +351,18 @@ def test_decode_sized_call_equals_batched(moe):
     params, L = place(wl)
     x = mi.make_x(wl, device="cuda")
     base = _run(moe, L, x, wl.T)
-    for t0, n in ((0, 1), (5, 8), (2990, 11)):
+    E = wl.shape.n_experts
+    for t0, n, chunk in ((0, 1, 1), (5, 8, 8), (2990, 11, 11), (100, 16, 5)):
         xs = x[t0:t0 + n].contiguous()
-        got = _run(moe, L, xs, n)
+        got = _run(moe, L, xs, chunk)
         torch.cuda.synchronize()
+        ids = got["ids"].cpu().numpy()
         assert torch.equal(got["ids"], base["ids"][t0:t0 + n]), (t0, n)
         assert torch.equal(bits(got["out"]), bits(base["out"][t0:t0 + n])), (t0, n)
+        # per-chunk counts (the top-k of at most 16 tokens counts them in the same launch)
+        want = np.stack([np.bincount(ids[c:c + chunk].ravel(), minlength=E)
+                         for c in range(0, n, chunk)])
+        assert np.array_equal(got["chunk_counts"].cpu().numpy(), want), (t0, n, chunk)
 
 
 def test_chunk_gate_4099(moe):

@@ -191,10 +191,13 @@ def stack_variant(steps: int):
     _, wall, per = time_steps(run, steps, 0)
     st = ring.stats()
     ring.close()
-    looks = st["hits"] + st["misses"]
+    looks = st["hits"] + st["misses"] + st["pinned_uses"]
     return {"workload": f"stack_{wl.n_layers}x_T{wl.T}_zipf1.5_ring{wl.ring_lines}_chunk2048",
             "tokens_per_s": round(wl.T / (wall / 1e3), 1), "ms_per_pass": round(wall, 1),
-            "pass_ms": spread(per), "ring_hit_rate": round(st["hits"] / max(1, looks), 4),
+            "pass_ms": spread(per),
+            # experts served without a copy: staged hits and uses of lines pinned for a layer
+            "ring_hit_rate": round((st["hits"] + st["pinned_uses"]) / max(1, looks), 4),
+            "pinned_uses_per_pass": st["pinned_uses"] // steps,
             "ring_lookups_per_pass": looks // steps,
             "h2d_gb_per_pass": round(st["bytes_h2d"] / steps / 1e9, 2),
             "h2d_gb_per_pass_by_kind": {k: round(v / steps / 1e9, 3)
@@ -279,7 +282,8 @@ def ring_variant(moe, wl, params, x, bufs, t_gemm):
         "link_floor_ms": round(t_copy, 2),
         "ring_over_link_floor": round(r_wall / t_copy, 4),
         "compute_alone_ms": t_gemm,
-        "ring_hit_rate": round(st["hits"] / max(1, st["hits"] + st["misses"]), 4),
+        "ring_hit_rate": round((st["hits"] + st["pinned_uses"]) /
+                               max(1, st["hits"] + st["misses"] + st["pinned_uses"]), 4),
         "copy_waits_per_step": st["copy_waits"] // 3,
         "copied_bytes_per_step_by_kind": {k: v // 3 for k, v in st["copied_bytes"].items()},
         "compute_hidden_frac_vs_link_floor": round(max(0.0, min(1.0, hidden)), 3),

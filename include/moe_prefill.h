@@ -201,7 +201,12 @@ moe_status moe_prefill_chunk_noalloc(const moe_layer* layer, const void* x, cons
 
 /* Whole-prompt convenience: route, then moe_prefill_chunk over [c*chunk, min((c+1)*chunk, T))
  * for every chunk in order. With a ring, the per-chunk counts come from one device-to-host copy
- * of chunk_counts (one synchronisation per call). Arguments as in the two calls above;
+ * of chunk_counts (one synchronisation per call). With a ring and several chunks, the call may
+ * pin the offloaded experts most of its chunks use: it stages them first (kind
+ * MOE_COPY_INITIAL), keeps their lines held through the last chunk and streams only the
+ * other experts through the remaining lines (a quarter, half or three quarters of the ring,
+ * or nothing, whichever a least-recently-used estimate over the known chunk counts says
+ * copies least); the output bytes are the same either way. Arguments as in the two calls above;
  * ws must hold moe_workspace_bytes(shape, min(chunk, T)). */
 moe_status moe_prefill_layer(const moe_layer* layer, const void* x, int64_t T, int64_t chunk,
                              int32_t* ids, float* weights, int32_t* chunk_counts, float* logits,
@@ -268,7 +273,7 @@ enum {
 
 /* Ring counters (all cumulative since creation or moe_ring_reset_stats). */
 typedef struct {
-  int32_t version;            /* set to 2 by the library */
+  int32_t version;            /* set to 3 by the library */
   int32_t n_lines;
   int64_t hits;               /* staged experts already present in a line */
   int64_t misses;             /* staged experts copied from a bank */
@@ -280,6 +285,11 @@ typedef struct {
    * (hits and misses) and of those copied (misses); copied_bytes sum to bytes_h2d */
   int64_t requested_bytes[MOE_COPY_KINDS];
   int64_t copied_bytes[MOE_COPY_KINDS];
+  /* version 3: chunk uses of experts a moe_prefill_layer call keeps pinned in held lines for
+   * all its chunks (served without a staging; the pinning itself is one staging of kind
+   * MOE_COPY_INITIAL). hits + pinned_uses over hits + misses + pinned_uses is the share of
+   * requested experts served without a copy. */
+  int64_t pinned_uses;
 } moe_ring_stats_t;
 
 moe_status moe_ring_stats(const moe_ring* ring, moe_ring_stats_t* stats_out);

@@ -50,7 +50,8 @@ COPY_KINDS = ["initial", "ahead", "demand", "cross_layer"]     # MOE_COPY_* orde
 class MoeRingStats(ctypes.Structure):
     _fields_ = [("version", c_i32), ("n_lines", c_i32), ("hits", c_i64), ("misses", c_i64),
                 ("bytes_h2d", c_i64), ("copy_waits", c_i64), ("waves", c_i64),
-                ("requested_bytes", c_i64 * 4), ("copied_bytes", c_i64 * 4)]
+                ("requested_bytes", c_i64 * 4), ("copied_bytes", c_i64 * 4),
+                ("pinned_uses", c_i64)]
 
 
 # name -> (restype, argtypes); every function declared in include/moe_prefill.h

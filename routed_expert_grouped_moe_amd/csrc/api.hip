@@ -181,6 +181,83 @@ moe_status route_impl(const moe_layer* L, const void* x, int64_t T, int64_t chun
   return MOE_OK;
 }
 
+// Experts held in the ring for a whole layer call, and their lines.
+struct Pinned {
+  std::vector<int32_t> experts;   // ascending
+  std::vector<int32_t> lines;
+};
+
+// Copies a layer call would make if the H experts used by the most chunks (by_freq[0..H))
+// stayed pinned and the others streamed through the remaining lines, least recently used
+// first, each chunk pass walking its experts upward or downward in turn from sweep0 (holds
+// ignored: an estimate for choosing H, not the ring's exact count).
+int64_t estimate_copies(const std::vector<std::vector<int32_t>>& used,
+                        const std::vector<int32_t>& by_freq, int H, int cap, uint64_t sweep0,
+                        int E) {
+  std::vector<char> hot(E, 0);
+  for (int i = 0; i < H; ++i) hot[by_freq[i]] = 1;
+  std::vector<int64_t> last(E, -1);            // -1: not in the streaming lines
+  int resident = 0;
+  int64_t clock = 0, copies = H;
+  for (size_t c = 0; c < used.size(); ++c) {
+    const std::vector<int32_t>& u = used[c];
+    const bool down = ((sweep0 + c) & 1) != 0;
+    for (size_t i = 0; i < u.size(); ++i) {
+      const int e = u[down ? u.size() - 1 - i : i];
+      if (hot[e]) continue;
+      if (last[e] < 0) {
+        ++copies;
+        if (resident == cap) {                 // evict the least recently used
+          int v = -1;
+          for (int f = 0; f < E; ++f)
+            if (last[f] >= 0 && (v < 0 || last[f] < last[v])) v = f;
+          last[v] = -1;
+          --resident;
+        }
+        ++resident;
+      }
+      last[e] = ++clock;
+    }
+  }
+  return copies;
+}
+
+// The experts of a layer call to pin: H of n_lines in {0, n/4, n/2, 3n/4}, the most chunks'
+// experts first (ties to the lower id), H chosen by estimate_copies (ties to the smaller H).
+// A skewed routing, whose hot experts recur in every chunk, keeps them in the ring for the
+// call instead of streaming them in and out once per chunk; a uniform one pins nothing.
+std::vector<int32_t> choose_pinned(const moe_layer* L, const int32_t* hc, int64_t n_chunks) {
+  const int E = L->shape.n_experts;
+  const int n = L->ring->n_lines;
+  std::vector<std::vector<int32_t>> used(static_cast<size_t>(n_chunks));
+  std::vector<int32_t> freq(E, 0);
+  for (int64_t c = 0; c < n_chunks; ++c)
+    for (int e = 0; e < E; ++e)
+      if (!L->expert_lines[e] && hc[c * E + e] > 0) {
+        used[c].push_back(e);
+        ++freq[e];
+      }
+  std::vector<int32_t> by_freq;
+  for (int e = 0; e < E; ++e)
+    if (freq[e] > 0) by_freq.push_back(e);
+  std::stable_sort(by_freq.begin(), by_freq.end(),
+                   [&](int a, int b) { return freq[a] > freq[b]; });
+  int best_h = 0;
+  int64_t best = -1;
+  for (int q = 0; q < 4; ++q) {
+    const int H = std::min<int>(q * n / 4, static_cast<int>(by_freq.size()));
+    if (q > 0 && H == 0) continue;
+    const int64_t c = estimate_copies(used, by_freq, H, n - H, L->ring->sweeps, E);
+    if (best < 0 || c < best) {
+      best = c;
+      best_h = H;
+    }
+  }
+  std::vector<int32_t> pin(by_freq.begin(), by_freq.begin() + best_h);
+  std::sort(pin.begin(), pin.end());
+  return pin;
+}
+
 // The routed GEMMs of the M-tiles g covers: gate/up then down, or both in one fused launch
 // when MOE_OPT_FUSED_GU_DOWN is on and the tiles allow it (the same h and Y bits).
 hipError_t launch_routed(const moe_shape& sh, const void* x, int64_t t0, const GemmGroups& g,
@@ -206,7 +283,7 @@ hipError_t launch_routed(const moe_shape& sh, const void* x, int64_t t0, const G
 // and the combine sums in ascending expert id.
 moe_status ring_waves(const moe_layer* L, const void* x, int64_t t0, int64_t n,
                       const int32_t* counts_host, char* ws, const WsLayout& W, hipStream_t s,
-                      hipStream_t cs) {
+                      hipStream_t cs, const Pinned* pin) {
   const moe_shape& sh = L->shape;
   const int E = sh.n_experts, k = sh.top_k;
   moe_ring* R = L->ring;
@@ -230,11 +307,14 @@ moe_status ring_waves(const moe_layer* L, const void* x, int64_t t0, int64_t n,
   std::vector<int64_t> mt_begin(E + 1, 0);
   for (int e = 0; e < E; ++e) mt_begin[e + 1] = mt_begin[e] + mtiles_of(cnt[e], bm);
 
+  std::vector<char> pinned(E, 0);
+  const int n_pin = pin ? static_cast<int>(pin->experts.size()) : 0;
+  for (int i = 0; i < n_pin; ++i) pinned[pin->experts[i]] = 1;
   std::vector<int32_t> used;
   bool all_offloaded = true;
   for (int e = 0; e < E; ++e) {
     all_offloaded &= L->expert_lines[e] == nullptr;
-    if (!L->expert_lines[e] && cnt[e] > 0) used.push_back(e);
+    if (!L->expert_lines[e] && cnt[e] > 0 && !pinned[e]) used.push_back(e);
   }
   // Misses are copied by the library's copy kernel when every routed expert of the layer is
   // offloaded: each wave's GEMMs then cover only the wave's experts and leave CUs free for the
@@ -243,7 +323,9 @@ moe_status ring_waves(const moe_layer* L, const void* x, int64_t t0, int64_t n,
   // 64 lines took 412-414 ms against 429-433 ms). With resident experts in the waves' ranges
   // the GEMMs fill the chip and the copy kernel would stall behind them (the 8-layer stack:
   // 1,396 ms against 1,345-1,349 ms with DMA copies), so those layers keep hipMemcpyAsync.
-  const int per_wave = std::max(1, R->n_lines / 2);
+  // pinned experts sit in their held lines for the whole layer call and run with whichever
+  // wave's expert-id range covers them, as resident experts do
+  const int per_wave = std::max(1, (R->n_lines - n_pin) / 2);
   const int nw = std::max<int>(1, (static_cast<int>(used.size()) + per_wave - 1) / per_wave);
   std::vector<std::vector<int32_t>> wexp(nw), wlines(nw);
   std::vector<int32_t> lo(nw), hi(nw);
@@ -270,6 +352,14 @@ moe_status ring_waves(const moe_layer* L, const void* x, int64_t t0, int64_t n,
   const int32_t* row_slot = reinterpret_cast<const int32_t*>(ws + W.row_slot);
   char* h = ws + W.h;
   float* y = reinterpret_cast<float*>(ws + W.y);
+  for (int i = 0; i < n_pin; ++i) R->stats.pinned_uses += cnt[pin->experts[i]] > 0 ? 1 : 0;
+  if (n_pin > 0) {                             // this chunk's table entries of the pinned lines
+    std::vector<const void*> pp(n_pin);
+    for (int i = 0; i < n_pin; ++i) pp[i] = moe_ring_line_ptr(R, pin->lines[i]);
+    moe_status pst = ring_wait_ready(R, pin->lines.data(), n_pin, s);
+    if (pst != MOE_OK) return pst;
+    MOE_HIP(launch_upload_pairs(wtab, pin->experts.data(), pp.data(), n_pin, s));
+  }
 
   int staged = 0;                              // waves staged, in processing order
   moe_status st = MOE_OK;
@@ -322,7 +412,8 @@ moe_status ring_waves(const moe_layer* L, const void* x, int64_t t0, int64_t n,
 
 moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const int32_t* ids,
                       const float* weights, int64_t t0, int64_t n, const int32_t* counts_host,
-                      void* out, void* ws_v, size_t ws_bytes, hipStream_t s, hipStream_t cs) {
+                      void* out, void* ws_v, size_t ws_bytes, hipStream_t s, hipStream_t cs,
+                      const Pinned* pin = nullptr) {
   const moe_shape& sh = L->shape;
   const int E = sh.n_experts, k = sh.top_k;
   WsLayout W;
@@ -395,7 +486,7 @@ moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const i
       MOE_HIP(launch_routed(sh, x, t0, g, row_tok, row_slot, ws + W.h, y, s));
     }
   } else {
-    moe_status st = ring_waves(L, x, t0, n, counts_host, ws, W, s, cs ? cs : s);
+    moe_status st = ring_waves(L, x, t0, n, counts_host, ws, W, s, cs ? cs : s, pin);
     // Join even on failure, so the caller's stream never runs ahead of the side work.
     if (pending.armed) MOE_HIP(pending.join());
     if (st != MOE_OK) return st;
@@ -619,14 +710,36 @@ moe_status moe_prefill_layer(const moe_layer* layer, const void* x, int64_t T, i
     if (err != hipSuccess)
       return set_error(MOE_ERR_HIP, "chunk counts to host: %s", hipGetErrorString(err));
   }
+  // With a ring and several chunks, the experts most chunks use stay in held lines for the
+  // whole call (staged up front, released after the last chunk).
+  moe::Pinned pin;
+  if (offloaded && n_chunks >= 2) {
+    pin.experts = moe::choose_pinned(layer, hc.data(), n_chunks);
+    if (!pin.experts.empty()) {
+      bool all_offloaded = true;
+      for (int e = 0; e < E; ++e) all_offloaded &= layer->expert_lines[e] == nullptr;
+      pin.lines.resize(pin.experts.size());
+      st = moe::ring_stage(layer->ring, layer->layer_id, pin.experts.data(),
+                           static_cast<int32_t>(pin.experts.size()), cs ? cs : s,
+                           pin.lines.data(), nullptr, /*two_streams=*/true, MOE_COPY_INITIAL,
+                           /*hold=*/true, all_offloaded);
+      if (st != MOE_OK) return st;
+    }
+  }
   for (int64_t c = 0; c < n_chunks; ++c) {
     const int64_t t0 = c * chunk;
     const int64_t n = std::min(chunk, T - t0);
     st = moe::chunk_impl(layer, offloaded, x, ids, weights, t0, n,
-                         offloaded ? hc.data() + c * E : nullptr, out, ws, ws_bytes, s, cs);
-    if (st != MOE_OK) return st;
+                         offloaded ? hc.data() + c * E : nullptr, out, ws, ws_bytes, s, cs,
+                         pin.experts.empty() ? nullptr : &pin);
+    if (st != MOE_OK) break;
   }
-  return MOE_OK;
+  if (!pin.experts.empty()) {
+    moe_status rst = moe::ring_release(layer->ring, pin.lines.data(),
+                                       static_cast<int32_t>(pin.lines.size()), s);
+    if (st == MOE_OK) st = rst;
+  }
+  return st;
 }
 
 moe_status moe_add_rmsnorm(const void* x, const void* delta, int64_t T, int32_t d,

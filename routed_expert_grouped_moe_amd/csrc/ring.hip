@@ -291,7 +291,7 @@ moe_status moe_ring_create(const moe_shape* shape, void* device_lines, int32_t n
     delete r;
     return set_error(MOE_ERR_HIP, "hipEventCreateWithFlags: %s", hipGetErrorString(err));
   }
-  r->stats.version = 2;
+  r->stats.version = 3;
   r->stats.n_lines = n_lines;
   *out = r;
   return MOE_OK;
@@ -384,7 +384,7 @@ moe_status moe_ring_reset_stats(moe_ring* r) {
   if (!r) return set_error(MOE_ERR_INVALID, "ring is NULL");
   const int32_t nl = r->stats.n_lines;
   r->stats = moe_ring_stats_t{};
-  r->stats.version = 2;
+  r->stats.version = 3;
   r->stats.n_lines = nl;
   return MOE_OK;
 }

@@ -3,12 +3,56 @@ stages them through the ring, for tests that predict the ring's hit and miss cou
 Test infrastructure only.
 
 Per chunk pass: the offloaded experts the chunk uses, ascending, are cut into waves of at most
-n_lines // 2; even passes run the waves in ascending order, odd passes in descending order
-(and stage each wave's experts top-down). Before wave i runs, waves i and i + 1 are staged
-(the second only if enough lines are free); wave i is released after its GEMMs. Staging marks
-hits first; each miss evicts the least recently used unheld line that holds no expert a later
-wave of the same pass asks for, else the least recently used unheld line."""
+(n_lines - pinned) // 2; even passes run the waves in ascending order, odd passes in descending
+order (and stage each wave's experts top-down). Before wave i runs, waves i and i + 1 are
+staged (the second only if enough lines are free); wave i is released after its GEMMs. Staging
+marks hits first; each miss evicts the least recently used unheld line that holds no expert a
+later wave of the same pass asks for, else the least recently used unheld line.
+
+Per layer call of several chunks (layer()): the experts to pin are chosen from every chunk's
+expert set as the library chooses them (choose_pinned), staged first and held until the last
+chunk is done; the chunks stream only the others."""
 from __future__ import annotations
+
+
+def estimate_copies(used, by_freq, H, cap, sweep0):
+    """Copies with by_freq[:H] pinned and the rest streaming through cap lines, least recently
+    used first, chunk passes alternating direction from sweep0, holds ignored."""
+    hot = set(by_freq[:H])
+    last = {}
+    clock, copies = 0, H
+    for c, u in enumerate(used):
+        seq = u[::-1] if (sweep0 + c) & 1 else u
+        for e in seq:
+            if e in hot:
+                continue
+            if e not in last:
+                copies += 1
+                if len(last) == cap:
+                    del last[min(last, key=last.get)]
+            clock += 1
+            last[e] = clock
+    return copies
+
+
+def choose_pinned(used, n_lines, sweep0):
+    """The experts a layer call of several chunks pins (ascending): H in {0, n/4, n/2, 3n/4},
+    the experts most chunks use first (ties to the lower id), H with the fewest estimated
+    copies (ties to the smaller H)."""
+    freq = {}
+    for u in used:
+        for e in u:
+            freq[e] = freq.get(e, 0) + 1
+    by_freq = sorted(freq, key=lambda e: (-freq[e], e))
+    best_h, best = 0, None
+    for q in range(4):
+        H = min(q * n_lines // 4, len(by_freq))
+        if q > 0 and H == 0:
+            continue
+        c = estimate_copies(used, by_freq, H, n_lines - H, sweep0)
+        if best is None or c < best:
+            best, best_h = c, H
+    return sorted(by_freq[:best_h])
 
 
 class RingModel:
@@ -21,6 +65,7 @@ class RingModel:
         self.sweeps = 0
         self.hits = 0
         self.misses = 0
+        self.pinned_uses = 0                # chunk uses of experts pinned for a layer call
         self.copied = [0, 0, 0, 0]          # misses by kind: initial, ahead, demand, cross-layer
         self.requested = [0, 0, 0, 0]
         self.log = []                       # ("stage", kind, experts, later) / ("release", experts)
@@ -64,9 +109,30 @@ class RingModel:
             out[i] = v
         return out
 
-    def chunk(self, layer: int, used: list[int]):
+    def layer(self, layer: int, used_chunks: list[list[int]]):
+        """A layer call over chunks with these (ascending) offloaded experts each."""
+        pin = choose_pinned(used_chunks, self.n, self.sweeps) if len(used_chunks) >= 2 else []
+        lines = []
+        if pin:
+            m0 = self.misses
+            lines = self._stage(layer, pin, set())
+            assert lines is not None, "the model could not pin its experts"
+            self.log.append(("stage", 0, list(pin), []))
+            self.copied[0] += self.misses - m0
+            self.requested[0] += len(pin)
+        pinset = set(pin)
+        for u in used_chunks:
+            self.pinned_uses += sum(1 for e in u if e in pinset)
+            self.chunk(layer, [e for e in u if e not in pinset], n_pinned=len(pin))
+        for l in lines:
+            self.held[l] = False
+        if pin:
+            self.log.append(("release", list(pin)))
+        return pin
+
+    def chunk(self, layer: int, used: list[int], n_pinned: int = 0):
         """One chunk pass over the (ascending) offloaded experts the chunk uses."""
-        per = max(1, self.n // 2)
+        per = max(1, (self.n - n_pinned) // 2)
         nw = max(1, (len(used) + per - 1) // per)
         waves = [list(used[w * per:(w + 1) * per]) for w in range(nw)]
         down = self.sweeps & 1

@@ -47,14 +47,23 @@ def test_ring_equals_resident(moe, n_lines, offload, chunk):
     torch.cuda.synchronize()
     assert torch.equal(bits(got["out"]), bits(ref["out"]))
     st = ring.stats()
-    # every (chunk, used offloaded expert) pair is either a hit or a copy
+    # the host model of the plan (pinned experts, waves) predicts every count exactly
+    from tests.ring_model import RingModel
     cc = ref["chunk_counts"].cpu().numpy()
     offset = np.zeros(E, bool)
     offset[list(off)] = True
+    model = RingModel(n_lines)
+    pin = model.layer(0, [[int(e) for e in np.nonzero(row)[0] if offset[e]] for row in cc])
+    print(f"[ring] {n_lines} lines, {offload}, chunk {chunk}: pinned {len(pin)}; hits "
+          f"{st['hits']} misses {st['misses']} pinned uses {st['pinned_uses']}", flush=True)
+    assert (st["hits"], st["misses"], st["pinned_uses"]) == (
+        model.hits, model.misses, model.pinned_uses)
+    # every (chunk, used offloaded expert) pair is a hit, a copy or a use of a pinned line;
+    # the pinning itself is one more staging per pinned expert
     needed = int(((cc > 0) & offset[None, :]).sum())
-    assert st["hits"] + st["misses"] == needed
+    assert st["hits"] + st["misses"] + st["pinned_uses"] == needed + len(pin)
     assert st["bytes_h2d"] == st["misses"] * ring.line_bytes
-    assert st["misses"] >= min(needed, len(set(np.nonzero(cc.sum(0) * offset)[0])))
+    assert st["misses"] >= len(set(np.nonzero(cc.sum(0) * offset)[0]))
     ring.close()
 
 
@@ -98,11 +107,12 @@ def test_ring_passes_alternate_direction(moe):
     st = ring.stats()
     model = RingModel(8)
     cc = got["chunk_counts"].cpu().numpy()
-    for row in cc:
-        model.chunk(0, [int(e) for e in np.nonzero(row)[0]])
-    print(f"[ring] sweep: library hits {st['hits']} misses {st['misses']}; model "
-          f"{model.hits}/{model.misses}", flush=True)
-    assert (st["hits"], st["misses"]) == (model.hits, model.misses)
+    model.layer(0, [[int(e) for e in np.nonzero(row)[0]] for row in cc])
+    print(f"[ring] sweep: library hits {st['hits']} misses {st['misses']} pinned uses "
+          f"{st['pinned_uses']}; model {model.hits}/{model.misses}/{model.pinned_uses}",
+          flush=True)
+    assert (st["hits"], st["misses"], st["pinned_uses"]) == (
+        model.hits, model.misses, model.pinned_uses)
     # one fixed direction with plain LRU (the model with every pass ascending)
     lru = RingModel(8)
     for row in cc:
@@ -234,8 +244,8 @@ def test_copy_categories_match_the_model(moe):
         torch.cuda.synchronize()
         st = ring.stats()
         model = RingModel(n_lines)
-        for row in got["chunk_counts"].cpu().numpy():
-            model.chunk(0, [int(e) for e in np.nonzero(row)[0]])
+        model.layer(0, [[int(e) for e in np.nonzero(row)[0]]
+                        for row in got["chunk_counts"].cpu().numpy()])
         lb = ring.line_bytes
         kinds = ["initial", "ahead", "demand", "cross_layer"]
         print(f"[ring] kinds, {n_lines} lines: copied {[st['copied_bytes'][k] // lb for k in kinds]}"

@@ -105,3 +105,27 @@ def test_model_waves_replay(exes, tmp_path):
     assert (hits, misses) == (model.hits, model.misses)
     assert copied == model.copied and line[-1] == "0"
     assert model.copied[0] > 0 and model.copied[1] > 0
+
+
+def test_model_pinned_layer_replay(exes, tmp_path):
+    """A layer call of the host model with skewed routing pins the experts most chunks use
+    (held through every chunk, then released) and streams the rest; replayed through the
+    library's staging and release calls: the same hits and misses, and no race."""
+    from tests.ring_model import RingModel
+    rng = np.random.default_rng(11)
+    E, n_lines = 48, 16
+    hot = list(range(10))
+    model = RingModel(n_lines)
+    for _ in range(3):
+        chunks = [sorted(set(hot) | set(rng.choice(np.arange(10, E), size=int(rng.integers(4, 20)),
+                                                 replace=False).tolist()))
+                  for _ in range(12)]
+        pin = model.layer(0, chunks)
+        assert pin, "skewed chunks pin their hot experts"
+    path = str(tmp_path / "plan.txt")
+    model.write_log(path, E)
+    r = _run(exes["real"], "model", path)
+    assert r.returncode == 0, r.stdout[-3000:]
+    line = [l for l in r.stdout.splitlines() if l.startswith("model hits")][0].split()
+    assert (int(line[2]), int(line[4])) == (model.hits, model.misses)
+    assert [int(v) for v in line[6:10]] == model.copied and line[-1] == "0"

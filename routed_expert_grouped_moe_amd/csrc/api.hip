@@ -181,27 +181,42 @@ moe_status route_impl(const moe_layer* L, const void* x, int64_t T, int64_t chun
   return MOE_OK;
 }
 
+// Shares of the ring's lines a layer call may pin, in sixteenths. On the 8-layer stack
+// (Zipf 1.5, 128 lines) allowing 14/16 and 15/16 besides 0..12/16 took a pass from
+// 1,182-1,189 to 1,147-1,154 and 1,127-1,139 ms: fewer bytes, though in more, smaller waves.
+constexpr int kPinSixteenths[] = {0, 4, 8, 12, 14, 15};
+// A wave (a staging with its GEMM launches) costs about an eighth of a line copy in the
+// same measurement (953 more waves per pass for 258 fewer copies saved 12-20 ms); the
+// estimate weighs copies by 8 and waves by 1.
+constexpr int64_t kCopyPerWave = 8;
+constexpr int kPinChoices = sizeof(kPinSixteenths) / sizeof(kPinSixteenths[0]);
+
 // Experts held in the ring for a whole layer call, and their lines.
 struct Pinned {
   std::vector<int32_t> experts;   // ascending
   std::vector<int32_t> lines;
 };
 
-// Copies a layer call would make if the H experts used by the most chunks (by_freq[0..H))
-// stayed pinned and the others streamed through the remaining lines, least recently used
-// first, each chunk pass walking its experts upward or downward in turn from sweep0 (holds
-// ignored: an estimate for choosing H, not the ring's exact count).
-int64_t estimate_copies(const std::vector<std::vector<int32_t>>& used,
-                        const std::vector<int32_t>& by_freq, int H, int cap, uint64_t sweep0,
-                        int E) {
+// Cost of a layer call if the H experts used by the most chunks (by_freq[0..H)) stayed pinned
+// and the others streamed through the remaining cap lines, least recently used first, each
+// chunk pass walking its experts upward or downward in turn from sweep0, in waves of cap/2:
+// kCopyPerWave per copy plus one per wave (holds ignored: an estimate for choosing H, not the
+// ring's exact count).
+int64_t estimate_cost(const std::vector<std::vector<int32_t>>& used,
+                      const std::vector<int32_t>& by_freq, int H, int cap, uint64_t sweep0,
+                      int E) {
   std::vector<char> hot(E, 0);
   for (int i = 0; i < H; ++i) hot[by_freq[i]] = 1;
   std::vector<int64_t> last(E, -1);            // -1: not in the streaming lines
   int resident = 0;
-  int64_t clock = 0, copies = H;
+  int64_t clock = 0, copies = H, waves = 0;
+  const int per_wave = std::max(1, cap / 2);
   for (size_t c = 0; c < used.size(); ++c) {
     const std::vector<int32_t>& u = used[c];
     const bool down = ((sweep0 + c) & 1) != 0;
+    int streamed = 0;
+    for (int e : u) streamed += hot[e] ? 0 : 1;
+    waves += std::max(1, (streamed + per_wave - 1) / per_wave);
     for (size_t i = 0; i < u.size(); ++i) {
       const int e = u[down ? u.size() - 1 - i : i];
       if (hot[e]) continue;
@@ -219,11 +234,11 @@ int64_t estimate_copies(const std::vector<std::vector<int32_t>>& used,
       last[e] = ++clock;
     }
   }
-  return copies;
+  return kCopyPerWave * copies + waves;
 }
 
-// The experts of a layer call to pin: H of n_lines in {0, n/4, n/2, 3n/4}, the most chunks'
-// experts first (ties to the lower id), H chosen by estimate_copies (ties to the smaller H).
+// The experts of a layer call to pin: H = n_lines * kPinSixteenths / 16, the most chunks'
+// experts first (ties to the lower id), H chosen by estimate_cost (ties to the smaller H).
 // A skewed routing, whose hot experts recur in every chunk, keeps them in the ring for the
 // call instead of streaming them in and out once per chunk; a uniform one pins nothing.
 std::vector<int32_t> choose_pinned(const moe_layer* L, const int32_t* hc, int64_t n_chunks) {
@@ -244,10 +259,10 @@ std::vector<int32_t> choose_pinned(const moe_layer* L, const int32_t* hc, int64_
                    [&](int a, int b) { return freq[a] > freq[b]; });
   int best_h = 0;
   int64_t best = -1;
-  for (int q = 0; q < 4; ++q) {
-    const int H = std::min<int>(q * n / 4, static_cast<int>(by_freq.size()));
+  for (int q = 0; q < kPinChoices; ++q) {
+    const int H = std::min<int>(n * kPinSixteenths[q] / 16, static_cast<int>(by_freq.size()));
     if (q > 0 && H == 0) continue;
-    const int64_t c = estimate_copies(used, by_freq, H, n - H, L->ring->sweeps, E);
+    const int64_t c = estimate_cost(used, by_freq, H, n - H, L->ring->sweeps, E);
     if (best < 0 || c < best) {
       best = c;
       best_h = H;

@@ -15,13 +15,21 @@ chunk is done; the chunks stream only the others."""
 from __future__ import annotations
 
 
-def estimate_copies(used, by_freq, H, cap, sweep0):
-    """Copies with by_freq[:H] pinned and the rest streaming through cap lines, least recently
-    used first, chunk passes alternating direction from sweep0, holds ignored."""
+PIN_SIXTEENTHS = (0, 4, 8, 12, 14, 15)    # shares of the lines a layer call may pin
+COPY_PER_WAVE = 8                         # a copy weighs 8 waves in the estimate
+
+
+def estimate_cost(used, by_freq, H, cap, sweep0):
+    """COPY_PER_WAVE x copies + waves with by_freq[:H] pinned and the rest streaming through
+    cap lines in waves of cap // 2, least recently used first, chunk passes alternating
+    direction from sweep0, holds ignored."""
     hot = set(by_freq[:H])
     last = {}
-    clock, copies = 0, H
+    clock, copies, waves = 0, H, 0
+    per = max(1, cap // 2)
     for c, u in enumerate(used):
+        streamed = sum(1 for e in u if e not in hot)
+        waves += max(1, (streamed + per - 1) // per)
         seq = u[::-1] if (sweep0 + c) & 1 else u
         for e in seq:
             if e in hot:
@@ -32,24 +40,24 @@ def estimate_copies(used, by_freq, H, cap, sweep0):
                     del last[min(last, key=last.get)]
             clock += 1
             last[e] = clock
-    return copies
+    return COPY_PER_WAVE * copies + waves
 
 
 def choose_pinned(used, n_lines, sweep0):
-    """The experts a layer call of several chunks pins (ascending): H in {0, n/4, n/2, 3n/4},
-    the experts most chunks use first (ties to the lower id), H with the fewest estimated
-    copies (ties to the smaller H)."""
+    """The experts a layer call of several chunks pins (ascending): H = n * PIN_SIXTEENTHS / 16,
+    the experts most chunks use first (ties to the lower id), H with the lowest estimated
+    cost (ties to the smaller H)."""
     freq = {}
     for u in used:
         for e in u:
             freq[e] = freq.get(e, 0) + 1
     by_freq = sorted(freq, key=lambda e: (-freq[e], e))
     best_h, best = 0, None
-    for q in range(4):
-        H = min(q * n_lines // 4, len(by_freq))
+    for q, sx in enumerate(PIN_SIXTEENTHS):
+        H = min(n_lines * sx // 16, len(by_freq))
         if q > 0 and H == 0:
             continue
-        c = estimate_copies(used, by_freq, H, n_lines - H, sweep0)
+        c = estimate_cost(used, by_freq, H, n_lines - H, sweep0)
         if best is None or c < best:
             best, best_h = c, H
     return sorted(by_freq[:best_h])

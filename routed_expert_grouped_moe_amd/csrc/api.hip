@@ -738,6 +738,12 @@ moe_status moe_prefill_layer(const moe_layer* layer, const void* x, int64_t T, i
                            static_cast<int32_t>(pin.experts.size()), cs ? cs : s,
                            pin.lines.data(), nullptr, /*two_streams=*/true, MOE_COPY_INITIAL,
                            /*hold=*/true, all_offloaded);
+      if (st == MOE_ERR_RING) {   // lines held elsewhere (public staging calls): no pinning
+        moe::clear_error();
+        pin.experts.clear();
+        pin.lines.clear();
+        st = MOE_OK;
+      }
       if (st != MOE_OK) return st;
     }
   }

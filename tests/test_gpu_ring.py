@@ -122,6 +122,45 @@ def test_ring_passes_alternate_direction(moe):
     ring.close()
 
 
+def test_pinning_falls_back_when_lines_are_held(moe):
+    """A layer call that cannot pin (lines held by a caller's own staging of another layer)
+    streams every expert instead: the same bytes as the all-resident layer, nothing pinned.
+    The held count leaves fewer free lines than the call would pin, but room for its waves."""
+    from tests.ring_model import choose_pinned
+    wl = mi.custom_workload("pinfb", T=1200, d=64, E=256, k=8, inter=64, inter_shared=64,
+                            zipf_s=1.5, seed=13)
+    params, L_res = place(wl)
+    x = mi.make_x(wl, device="cuda")
+    ref = moe.moe_prefill_layer(L_res, x, 100)
+    torch.cuda.synchronize()
+    n_lines = 16
+    cc = ref["chunk_counts"].cpu().numpy()
+    want = choose_pinned([[int(e) for e in np.nonzero(r)[0]] for r in cc], n_lines, 0)
+    print(f"[ring] this routing pins {len(want)} of {n_lines} lines", flush=True)
+    assert len(want) > n_lines // 2, "this routing is meant to pin more than half the lines"
+    held = n_lines - len(want) + 1                # one line short of the pinning
+    ring = moe.Ring(L_res.shape, n_lines)
+    _, L = place(wl, offloaded=range(256), ring=ring, params=params, layer=0)
+    place(wl, offloaded=range(256), ring=ring, params=params, layer=1)
+    cs = torch.cuda.Stream()
+    lines = moe.moe_stage_experts(ring, 1, list(range(held)), copy_stream=cs)
+    got = moe.moe_prefill_layer(L, x, 100, copy_stream=cs)
+    torch.cuda.synchronize()
+    ring.release(lines)
+    assert torch.equal(bits(got["out"]), bits(ref["out"]))
+    st = ring.stats()
+    print(f"[ring] pin wanted {len(want)} of {n_lines} lines with {held} held elsewhere: "
+          f"pinned uses {st['pinned_uses']}", flush=True)
+    assert st["pinned_uses"] == 0
+    # and with nothing held the same call pins
+    ring.reset_stats()
+    got = moe.moe_prefill_layer(L, x, 100, copy_stream=cs)
+    torch.cuda.synchronize()
+    assert torch.equal(bits(got["out"]), bits(ref["out"]))
+    assert ring.stats()["pinned_uses"] > 0
+    ring.close()
+
+
 def test_stage_api_direct(moe):
     """moe_stage_experts copies exactly the bank's line into the ring line it returns."""
     wl = mi.custom_workload("stage", T=8, d=64, E=8, k=2, inter=64, inter_shared=0, seed=3)

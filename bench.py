@@ -160,9 +160,15 @@ def small_call_variant(L, mi, wl, T: int = 8, steps: int = 50):
         call()
     g_ms, g_wall, _ = time_steps(g.replay, steps, 5)
     ok = torch.equal(bufs["out"].view(torch.int16), ref.view(torch.int16))
+    # the same calls enqueued behind a GPU spin: the GPU's own time per call, without the
+    # host's launch work between calls
+    eg_ms, _, _ = time_steps(call, steps, 0, gate=True)
+    gg_ms, _, _ = time_steps(g.replay, steps, 0, gate=True)
     return {"tokens": T, "eager_ms_per_call": round(e_wall, 4),
             "graph_ms_per_call": round(g_wall, 4),
             "eager_gpu_ms": round(e_ms, 4), "graph_gpu_ms": round(g_ms, 4),
+            "eager_gpu_ms_host_ahead": round(eg_ms, 4),
+            "graph_gpu_ms_host_ahead": round(gg_ms, 4),
             "graph_equals_eager": bool(ok)}
 
 

@@ -535,17 +535,19 @@ __device__ __forceinline__ void gu_tile(const GuParams& p, int t, char* lds) {
 //   acc = 0; acc = fma(w_j, y_j, acc) for j = 0 .. k-1 (ascending expert); acc += S;
 //   out = round(acc)
 // with the operations and their order of combine_kernel, so the bits do not depend on which
-// of the two formed them. A lane handles two 4-column chunks at a time, with the Y loads of
-// both in flight before their FMAs.
+// of the two formed them. A lane handles U 4-column chunks at a time, with the Y loads of all
+// k slots of them in flight before their FMAs: two chunks, or one where the wave's accumulators
+// already take 128 registers (the 64 x 128 wave tile), since two chunks' loads beside them
+// would exceed 256 registers and spill (the reloads cost 7% of the 256 x 256 tile's time).
 template <class TL, typename T, class Val>
 __device__ __forceinline__ void combine_slab(char* lds, Val val, int wm, int64_t row0, int rows,
                                              const float* __restrict__ y,
                                              const float* __restrict__ wts, int64_t t0, int k,
                                              int d, T* __restrict__ out, int col0, int cols) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  constexpr int NCOL = TL::TN, RB = NCOL * 4, CPR = RB / 16, U = 2;
+  constexpr int NCOL = TL::TN, RB = NCOL * 4, CPR = RB / 16, U = TL::FM * TL::FN * 4 >= 128 ? 1 : 2;
   static_assert(16 * RB * TL::NW <= TL::LDS, "staging fits in LDS");
-  static_assert((16 * CPR) % (64 * U) == 0, "whole chunk pairs per block");
+  static_assert((16 * CPR) % (64 * U) == 0, "whole groups of U chunks per block");
   float* stg = reinterpret_cast<float*>(lds + wave * (16 * RB));
 #pragma unroll
   for (int i = 0; i < TL::FM; ++i) {

@@ -721,6 +721,23 @@ __device__ __forceinline__ void down_tile(const DownParams& p, int t, char* lds)
     }
     src[q] = base + 16 * stage_seg<TL>();
   }
+  // The output row (token slot) of each of the wave's rows, loaded before the mainloop so its
+  // latency hides behind the first stage, and written to LDS beside the staging area after it
+  // (the stage buffers hold that space until then). Looked up per store instead, each lookup
+  // would wait on a global load, and that wait (vmcnt) also waits for every store the wave has
+  // issued before it.
+  constexpr int kTab = TL::FM * 16;
+  constexpr int kTabPerLane = (kTab + 63) / 64;
+  int slot_of[kTabPerLane];
+  if (kGrouped) {
+    const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) / TL::WN;
+#pragma unroll
+    for (int q = 0; q < kTabPerLane; ++q) {
+      const int idx = lane + 64 * q;
+      const int tr = block_row<TL>(idx >> 4, wm) + (idx & 15);
+      slot_of[q] = (idx < kTab && tr < rows) ? p.row_slot[row0 + tr] : -1;
+    }
+  }
   f32x4_t acc[TL::FM][TL::FN];
   if (!missing)
     mainloop<T, TL, false>(src, stages<T, TL>(p.K), lds, acc, rows);
@@ -732,19 +749,13 @@ __device__ __forceinline__ void down_tile(const DownParams& p, int t, char* lds)
   };
   const int col0 = n0 + wn * TL::TN;
   if (kGrouped) {
-    // The output row (token slot) of each of the wave's rows, read once into LDS beside the
-    // staging area. Looked up per store instead, each lookup would wait on a global load, and
-    // that wait (vmcnt) also waits for every store the wave has issued before it.
     const int lane = threadIdx.x & 63;
-    constexpr int kTab = TL::FM * 16;
     constexpr int kStage = 16 * TL::TN * static_cast<int>(sizeof(float)) * TL::NW;
     static_assert(kStage + TL::NW * kTab * 4 <= TL::LDS, "slot table fits in LDS");
     int* tab = reinterpret_cast<int*>(lds + kStage) + wave * kTab;
 #pragma unroll
-    for (int idx = lane; idx < kTab; idx += 64) {
-      const int tr = block_row<TL>(idx >> 4, wm) + (idx & 15);
-      tab[idx] = tr < rows ? p.row_slot[row0 + tr] : -1;
-    }
+    for (int q = 0; q < kTabPerLane; ++q)
+      if (lane + 64 * q < kTab) tab[lane + 64 * q] = slot_of[q];
     __builtin_amdgcn_wave_barrier();  // a wave's LDS writes land before its later LDS reads
     auto row_of = [&](int sr) -> int64_t { return tab[sr]; };   // sr = block * 16 + row
     store_slab<TL, float, TL::TN, true>(lds, val, row_of, p.out, p.d, col0, min(TL::TN, p.d - col0));

@@ -12,8 +12,31 @@
 namespace moe {
 namespace {
 
-// One wavefront per token (topk_select); lane l loads the logits of experts l, l + 64, ...
-// (one token per wavefront measured faster than two interleaved: occupancy hides the latency)
+// Lane `lane`'s logits of token t: experts lane*NJ .. lane*NJ+NJ-1, -inf past E or T. 16-byte
+// loads where all of them exist and their address is 16-byte aligned.
+template <int NJ>
+__device__ __forceinline__ void load_logits(const float* __restrict__ logits, int64_t T, int E,
+                                            int64_t t, int lane, float (&x)[NJ]) {
+  const int64_t off = t * E + static_cast<int64_t>(lane) * NJ;
+  if constexpr (NJ % 4 == 0) {
+    if (t < T && lane * NJ + NJ <= E && (reinterpret_cast<uintptr_t>(logits + off) & 15) == 0) {
+#pragma unroll
+      for (int q = 0; q < NJ / 4; ++q) {
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(logits + off + 4 * q);
+        x[4 * q] = v[0];
+        x[4 * q + 1] = v[1];
+        x[4 * q + 2] = v[2];
+        x[4 * q + 3] = v[3];
+      }
+      return;
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < NJ; ++j)
+    x[j] = (t < T && lane * NJ + j < E) ? logits[off + j] : -INFINITY;
+}
+
+// One wavefront per token (topk_select); lane l loads the logits of experts l*NJ .. l*NJ+NJ-1.
 // The kernel also zeroes n_zero ints at `zero` (the per-chunk counts the next kernel adds
 // to), so that needs no launch of its own.
 template <int NJ>
@@ -21,23 +44,15 @@ __global__ __launch_bounds__(256) void topk_kernel(const float* __restrict__ log
                                                    int E, int k, int32_t* __restrict__ ids,
                                                    float* __restrict__ weights,
                                                    int32_t* __restrict__ zero, int64_t n_zero) {
-  __shared__ float ex[4][1024];
+  __shared__ uint64_t lst[4][topk_lds_words<NJ>()];
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n_zero;
        i += static_cast<int64_t>(gridDim.x) * 256)
     zero[i] = 0;
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t t = static_cast<int64_t>(blockIdx.x) * 4 + wv;
-  float x[1][NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int e = lane + 64 * j;
-    x[0][j] = (t < T && e < E) ? logits[t * E + e] : -INFINITY;
-  }
-  const bool act[1] = {t < T};
-  int32_t* const idr[1] = {ids + t * k};
-  float* const wr[1] = {weights + t * k};
-  float* const exr[1] = {ex[wv]};
-  topk_select<NJ, 1>(x, E, k, act, idr, wr, exr);
+  float x[NJ];
+  load_logits<NJ>(logits, T, E, t, lane, x);
+  topk_select<NJ>(x, E, k, t < T, ids + t * k, weights + t * k, lst[wv]);
 }
 
 // A prompt of at most 16 tokens in one workgroup: one wavefront per token as above, then the
@@ -48,20 +63,12 @@ template <int NJ>
 __global__ __launch_bounds__(64 * kSmallTopkTokens) void topk_counts_small_kernel(
     const float* __restrict__ logits, int64_t T, int E, int k, int32_t* __restrict__ ids,
     float* __restrict__ weights, int64_t chunk, int32_t* __restrict__ cc, int64_t n_cc) {
-  __shared__ float ex[kSmallTopkTokens][1024];
+  __shared__ uint64_t lst[kSmallTopkTokens][topk_lds_words<NJ>()];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int64_t t = wv;
-  float x[1][NJ];
-#pragma unroll
-  for (int j = 0; j < NJ; ++j) {
-    const int e = lane + 64 * j;
-    x[0][j] = (t < T && e < E) ? logits[t * E + e] : -INFINITY;
-  }
-  const bool act[1] = {t < T};
-  int32_t* const idr[1] = {ids + t * k};
-  float* const wr[1] = {weights + t * k};
-  float* const exr[1] = {ex[wv]};
-  topk_select<NJ, 1>(x, E, k, act, idr, wr, exr);
+  float x[NJ];
+  load_logits<NJ>(logits, T, E, t, lane, x);
+  topk_select<NJ>(x, E, k, t < T, ids + t * k, weights + t * k, lst[wv]);
   for (int64_t i = threadIdx.x; i < n_cc; i += blockDim.x) cc[i] = 0;
   __syncthreads();              // ids written and counts zeroed, for the whole workgroup
   for (int64_t i = threadIdx.x; i < T * k; i += blockDim.x)

@@ -12,7 +12,7 @@ import torch
 
 import moe_inputs as mi
 import oracle.moe_oracle as orc
-from tests.parity import as_f64, oracle_params, place, rel_err, routing_gates
+from tests.parity import as_f64, logit_bound, oracle_params, place, rel_err, routing_gates
 
 pytestmark = pytest.mark.gpu
 
@@ -261,7 +261,8 @@ def test_offload_16022_ring64(moe):
     xs = mi.to_numpy_exact(x)[rows]
     ref_logits = orc.router_logits(xs, op["w_router"], op["router_bias"])
     ids_use, _ = routing_gates(got["logits"].cpu().numpy()[rows], got["ids"].cpu().numpy()[rows],
-                               got["weights"].cpu().numpy()[rows], ref_logits, wl.shape.top_k)
+                               got["weights"].cpu().numpy()[rows], ref_logits, wl.shape.top_k,
+                               logit_bound(xs, op["w_router"], ref_logits, wl.shape.dtype))
     err = rel_err(as_f64(got["out"])[rows], orc.moe_layer(xs, op, ids=ids_use)["out"])
     print(f"[ring] sampled rel err {err:.3e}")
     assert err <= 2e-2

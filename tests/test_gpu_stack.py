@@ -13,7 +13,7 @@ import torch
 
 import moe_inputs as mi
 import oracle.moe_oracle as orc
-from tests.parity import as_f64, oracle_params, place, rel_err, routing_gates
+from tests.parity import as_f64, logit_bound, oracle_params, place, rel_err, routing_gates
 
 pytestmark = pytest.mark.gpu
 
@@ -64,7 +64,9 @@ def _run_stack(moe, wl, rows, chunk):
         logits = res["logits"][l].cpu().numpy()[rows]
         ref_logits = orc.router_logits(h, ops[l]["w_router"], ops[l]["router_bias"])
         ids_use, _ = routing_gates(logits, res["ids"][l].cpu().numpy()[rows],
-                                   res["weights"][l].cpu().numpy()[rows], ref_logits, k)
+                                   res["weights"][l].cpu().numpy()[rows], ref_logits, k,
+                                   logit_bound(h, ops[l]["w_router"], ref_logits,
+                                               wl.shape.dtype))
         err = rel_err(as_f64(res["outs"][l])[rows], orc.moe_layer(h, ops[l], ids=ids_use)["out"])
         worst = max(worst, err)
         assert err <= 2e-2, (l, err)

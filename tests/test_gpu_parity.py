@@ -111,6 +111,16 @@ def test_largest_dims(moe, case):
         st._int_bit_exact(moe, wl, params, x, t0, n, sample=None)
 
 
+def test_k_above_64(moe):
+    """k = 100 of E = 130 experts: top-k rounds past the first 64, the bucketing's check of a
+    token's later slots against its earlier ids (slots 64 and up), and combines of 100 terms.
+    Routing, chunks of 1, 13 and 40 tokens bit-identical, element-wise stage parity."""
+    wl = mi.custom_workload("k100", T=40, d=128, E=130, k=100, inter=64, inter_shared=64,
+                            seed=13)
+    _full_parity(moe, wl, BF16_TOL, chunks=(1, 13, 40))
+    _stage_parity(moe, wl)
+
+
 def _stage_parity(moe, wl):
     """Element-wise stage parity of the batched pass (tests/stage_checks.py): h, Y and out
     of every expert and token against the oracle's stages within derived bounds. Used where

@@ -527,7 +527,7 @@ def main():
         chosen.discard("stack")
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        log("bench.py runs on one GPU only: this build has no multi-GPU path "
+        log("bench.py runs on one GPU only: the library has no multi-GPU path "
             "(no collectives or sharding); run it with --gpus 1.")
         sys.exit(2)
 

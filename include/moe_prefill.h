@@ -48,7 +48,7 @@ typedef enum {
   MOE_ERR_WORKSPACE = 2,   /* workspace smaller than moe_workspace_bytes(shape, n) */
   MOE_ERR_RING = 3,        /* ring missing, too small, or no bank bound for an offloaded expert */
   MOE_ERR_HIP = 4,         /* a HIP runtime call failed; outputs of this call are undefined */
-  MOE_ERR_UNSUPPORTED = 5  /* valid request this build does not handle */
+  MOE_ERR_UNSUPPORTED = 5  /* valid request this library does not handle */
 } moe_status;
 
 typedef enum { MOE_BF16 = 0, MOE_F32 = 1 } moe_dtype;

@@ -22,7 +22,7 @@ def _build(tmp, name, defines=()):
     gxx = shutil.which("g++")
     if gxx is None:
         pytest.skip("g++ not found")
-    # the ring source is copied to a .cpp of its own: this build is host code only
+    # the ring source is copied to a .cpp of its own and compiled as host code only
     src = os.path.join(tmp, "ring_host_copy.cpp")
     shutil.copyfile(RING_SRC, src)
     exe = os.path.join(tmp, name)

@@ -201,15 +201,26 @@ struct Pinned {
 // and the others streamed through the remaining cap lines, least recently used first, each
 // chunk pass walking its experts upward or downward in turn from sweep0, in waves of cap/2:
 // kCopyPerWave per copy plus one per wave (holds ignored: an estimate for choosing H, not the
-// ring's exact count).
+// ring's exact count). The lines' experts form a recency list (most recent first), so a
+// lookup or an eviction is O(1): the call is planned on the host while the GPU waits.
 int64_t estimate_cost(const std::vector<std::vector<int32_t>>& used,
                       const std::vector<int32_t>& by_freq, int H, int cap, uint64_t sweep0,
                       int E) {
-  std::vector<char> hot(E, 0);
+  std::vector<char> hot(E, 0), in(E, 0);
   for (int i = 0; i < H; ++i) hot[by_freq[i]] = 1;
-  std::vector<int64_t> last(E, -1);            // -1: not in the streaming lines
-  int resident = 0;
-  int64_t clock = 0, copies = H, waves = 0;
+  std::vector<int32_t> prv(E, -1), nxt(E, -1);
+  int head = -1, tail = -1, resident = 0;
+  auto unlink = [&](int e) {
+    (prv[e] >= 0 ? nxt[prv[e]] : head) = nxt[e];
+    (nxt[e] >= 0 ? prv[nxt[e]] : tail) = prv[e];
+  };
+  auto push_front = [&](int e) {
+    prv[e] = -1;
+    nxt[e] = head;
+    (head >= 0 ? prv[head] : tail) = e;
+    head = e;
+  };
+  int64_t copies = H, waves = 0;
   const int per_wave = std::max(1, cap / 2);
   for (size_t c = 0; c < used.size(); ++c) {
     const std::vector<int32_t>& u = used[c];
@@ -220,18 +231,20 @@ int64_t estimate_cost(const std::vector<std::vector<int32_t>>& used,
     for (size_t i = 0; i < u.size(); ++i) {
       const int e = u[down ? u.size() - 1 - i : i];
       if (hot[e]) continue;
-      if (last[e] < 0) {
+      if (in[e]) {
+        unlink(e);
+      } else {
         ++copies;
         if (resident == cap) {                 // evict the least recently used
-          int v = -1;
-          for (int f = 0; f < E; ++f)
-            if (last[f] >= 0 && (v < 0 || last[f] < last[v])) v = f;
-          last[v] = -1;
+          const int v = tail;
+          unlink(v);
+          in[v] = 0;
           --resident;
         }
+        in[e] = 1;
         ++resident;
       }
-      last[e] = ++clock;
+      push_front(e);
     }
   }
   return kCopyPerWave * copies + waves;

@@ -164,9 +164,11 @@ bool uniform_lines(const void* const* lines, int E, int64_t* stride) {
       return set_error(MOE_ERR_HIP, "%s: %s", #call, hipGetErrorString(e_));               \
   } while (0)
 
+// counts_in_chunks: the caller's chunk loop fills chunk_counts (each chunk's bucketing writes
+// its row), so the per-chunk histogram is not launched here.
 moe_status route_impl(const moe_layer* L, const void* x, int64_t T, int64_t chunk,
                       int32_t* ids, float* weights, int32_t* chunk_counts, float* logits,
-                      hipStream_t s) {
+                      hipStream_t s, bool counts_in_chunks = false) {
   const moe_shape& sh = L->shape;
   MOE_HIP(launch_router_gemm(sh.dtype, x, L->w_router, L->router_bias, T, sh.d, sh.n_experts,
                              logits, s));
@@ -176,8 +178,10 @@ moe_status route_impl(const moe_layer* L, const void* x, int64_t T, int64_t chun
                                      chunk_counts, n_cc, s));
     return MOE_OK;
   }
-  MOE_HIP(launch_topk(logits, T, sh.n_experts, sh.top_k, ids, weights, chunk_counts, n_cc, s));
-  MOE_HIP(launch_chunk_hist(ids, T, sh.top_k, sh.n_experts, chunk, chunk_counts, s));
+  MOE_HIP(launch_topk(logits, T, sh.n_experts, sh.top_k, ids, weights, chunk_counts,
+                      counts_in_chunks ? 0 : n_cc, s));
+  if (!counts_in_chunks)
+    MOE_HIP(launch_chunk_hist(ids, T, sh.top_k, sh.n_experts, chunk, chunk_counts, s));
   return MOE_OK;
 }
 
@@ -441,7 +445,7 @@ moe_status ring_waves(const moe_layer* L, const void* x, int64_t t0, int64_t n,
 moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const int32_t* ids,
                       const float* weights, int64_t t0, int64_t n, const int32_t* counts_host,
                       void* out, void* ws_v, size_t ws_bytes, hipStream_t s, hipStream_t cs,
-                      const Pinned* pin = nullptr) {
+                      const Pinned* pin = nullptr, int32_t* counts_out = nullptr) {
   const moe_shape& sh = L->shape;
   const int E = sh.n_experts, k = sh.top_k;
   WsLayout W;
@@ -485,7 +489,7 @@ moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const i
   int64_t stride = 0;
   const bool uniform = !offloaded && uniform_lines(L->expert_lines, E, &stride);
   if (!uniform) MOE_HIP(launch_upload_ptrs(wtab, L->expert_lines, 0, E, s));
-  MOE_HIP(launch_bucket(ids + t0 * k, n, k, E, bm, ws, W, s));
+  MOE_HIP(launch_bucket(ids + t0 * k, n, k, E, bm, ws, W, s, counts_out));
   float* y = reinterpret_cast<float*>(ws + W.y);
   if (!offloaded) {
     GemmGroups g{reinterpret_cast<const MTile*>(ws + W.mtiles),
@@ -724,8 +728,12 @@ moe_status moe_prefill_layer(const moe_layer* layer, const void* x, int64_t T, i
                      ws_bytes, need, static_cast<long long>(cmax));
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipStream_t cs = static_cast<hipStream_t>(copy_stream);
-  if ((st = moe::route_impl(layer, x, T, chunk, ids, weights, chunk_counts, logits, s)) !=
-      MOE_OK)
+  // With every expert resident nothing reads the chunk counts before the chunks run, so
+  // each chunk's bucketing writes its own row (the same integers: ids from the router never
+  // repeat an expert within a token) and the per-chunk histogram launch is saved; a ring
+  // plans its waves from them, so they are counted up front.
+  if ((st = moe::route_impl(layer, x, T, chunk, ids, weights, chunk_counts, logits, s,
+                            /*counts_in_chunks=*/!offloaded)) != MOE_OK)
     return st;
   const int E = layer->shape.n_experts;
   const int64_t n_chunks = (T + chunk - 1) / chunk;
@@ -765,7 +773,8 @@ moe_status moe_prefill_layer(const moe_layer* layer, const void* x, int64_t T, i
     const int64_t n = std::min(chunk, T - t0);
     st = moe::chunk_impl(layer, offloaded, x, ids, weights, t0, n,
                          offloaded ? hc.data() + c * E : nullptr, out, ws, ws_bytes, s, cs,
-                         pin.experts.empty() ? nullptr : &pin);
+                         pin.experts.empty() ? nullptr : &pin,
+                         offloaded ? nullptr : chunk_counts + c * E);
     if (st != MOE_OK) break;
   }
   if (!pin.experts.empty()) {

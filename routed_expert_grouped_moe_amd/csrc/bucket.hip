@@ -67,14 +67,17 @@ __global__ __launch_bounds__(kTokBlock) void block_hist_kernel(const int32_t* __
 // One workgroup of 1024 threads; thread e owns expert e.
 //   blk_base[b][e] = slots of e in blocks before b; counts[e]; offsets = exclusive scan of
 //   counts; M-tiles: expert e contributes ceil(counts[e]/bm) tiles (e, 0), (e, bm), ... at
-//   position (exclusive scan of the tile counts); meta = {number of tiles, number of rows}.
+//   position (exclusive scan of the tile counts); meta = {number of tiles, number of rows};
+//   counts_out (if not NULL) = counts as well, the chunk's row of the layer call's
+//   chunk_counts.
 __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ blk_counts,
                                                     int nb, int E, int bm,
                                                     int32_t* __restrict__ blk_base,
                                                     int32_t* __restrict__ counts,
                                                     int32_t* __restrict__ offsets,
                                                     MTile* __restrict__ mtiles,
-                                                    int32_t* __restrict__ meta) {
+                                                    int32_t* __restrict__ meta,
+                                                    int32_t* __restrict__ counts_out) {
   __shared__ int32_t s_rows[kMaxE];
   __shared__ int32_t s_tiles[kMaxE];
   const int e = threadIdx.x;
@@ -94,6 +97,7 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
         }
     }
     counts[e] = run;
+    if (counts_out) counts_out[e] = run;
   }
   const int32_t ntile = (run + bm - 1) / bm;
   s_rows[e] = run;
@@ -172,7 +176,8 @@ __global__ __launch_bounds__(kTokBlock) void permute_scan_kernel(
     const int32_t* __restrict__ ids, int64_t n, int k, int E, int bm, int nb,
     const int32_t* __restrict__ blk_counts, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, MTile* __restrict__ mtiles, int32_t* __restrict__ meta,
-    int32_t* __restrict__ row_tok, int32_t* __restrict__ row_slot) {
+    int32_t* __restrict__ row_tok, int32_t* __restrict__ row_slot,
+    int32_t* __restrict__ counts_out) {
   constexpr int PER = kMaxE / kTokBlock;         // experts per thread in the scans
   __shared__ int32_t s_tot[kMaxE];               // rows of e in the chunk
   __shared__ int32_t s_pre[kMaxE];               // rows of e in blocks before this one
@@ -236,6 +241,7 @@ __global__ __launch_bounds__(kTokBlock) void permute_scan_kernel(
     s_off[e] = roff;
     if (b == 0 && e < E) {
       counts[e] = rows[q];
+      if (counts_out) counts_out[e] = rows[q];
       offsets[e] = roff;
       for (int i = 0; i < tiles[q]; ++i) mtiles[toff + i] = MTile{e, i * bm};
     }
@@ -310,7 +316,7 @@ hipError_t launch_upload_pairs(const void** table, const int32_t* idx, const voi
 }
 
 hipError_t launch_bucket(const int32_t* ids_chunk, int64_t n, int k, int E, int tile_rows,
-                         char* ws, const WsLayout& L, hipStream_t s) {
+                         char* ws, const WsLayout& L, hipStream_t s, int32_t* counts_out) {
   const int nb = static_cast<int>((n + kTokBlock - 1) / kTokBlock);
   int32_t* blk_counts = reinterpret_cast<int32_t*>(ws + L.blk_counts);
   int32_t* blk_base = reinterpret_cast<int32_t*>(ws + L.blk_base);
@@ -324,7 +330,8 @@ hipError_t launch_bucket(const int32_t* ids_chunk, int64_t n, int k, int E, int 
     permute_scan_kernel<true><<<1, kTokBlock, 0, s>>>(ids_chunk, n, k, E, tile_rows, nb,
                                                       blk_counts, counts, offsets, mtiles, meta,
                                                       reinterpret_cast<int32_t*>(ws + L.row_tok),
-                                                      reinterpret_cast<int32_t*>(ws + L.row_slot));
+                                                      reinterpret_cast<int32_t*>(ws + L.row_slot),
+                                                      counts_out);
     return hipGetLastError();
   }
   {
@@ -338,13 +345,14 @@ hipError_t launch_bucket(const int32_t* ids_chunk, int64_t n, int k, int E, int 
     permute_scan_kernel<false><<<nb, kTokBlock, 0, s>>>(ids_chunk, n, k, E, tile_rows, nb,
                                                         blk_counts, counts, offsets, mtiles, meta,
                                                         reinterpret_cast<int32_t*>(ws + L.row_tok),
-                                                        reinterpret_cast<int32_t*>(ws + L.row_slot));
+                                                        reinterpret_cast<int32_t*>(ws + L.row_slot),
+                                                        counts_out);
     return hipGetLastError();
   }
   {
     ProfScope prof(MOE_STAGE_SCAN, s);
     scan_kernel<<<1, 1024, 0, s>>>(blk_counts, nb, E, tile_rows, blk_base, counts, offsets,
-                                   mtiles, meta);
+                                   mtiles, meta, counts_out);
     err = hipGetLastError();
   }
   if (err != hipSuccess) return err;

@@ -77,8 +77,11 @@ MOE_HIDDEN hipError_t launch_upload_ptrs(const void** dst_table, const void* con
                                          int first, int n, hipStream_t s);
 MOE_HIDDEN hipError_t launch_upload_pairs(const void** table, const int32_t* idx,
                                          const void* const* ptr, int n, hipStream_t s);
+// Bucketing of a chunk's slots by expert into the workspace (counts, offsets, M-tiles, member
+// lists); counts_out (if not NULL) receives the chunk's expert counts as well.
 MOE_HIDDEN hipError_t launch_bucket(const int32_t* ids_chunk, int64_t n, int k, int E,
-                                    int tile_rows, char* ws, const WsLayout& L, hipStream_t s);
+                                    int tile_rows, char* ws, const WsLayout& L, hipStream_t s,
+                                    int32_t* counts_out = nullptr);
 
 // M-tile height of the routed GEMMs for a chunk of n tokens: 320 when experts average 192 to
 // 320 rows, else 256 from 128 rows up, else 64. The choice changes speed only, never a

@@ -655,7 +655,7 @@ __device__ __forceinline__ int down_units(const DownParams& p) {
   return m_tiles * NT;
 }
 
-template <typename T, class TL, bool kGrouped>
+template <typename T, class TL, bool kGrouped, bool kEarlySlots = kGrouped>
 __device__ __forceinline__ void down_tile(const DownParams& p, int t, char* lds);
 
 template <typename T, class TL, bool kGrouped>
@@ -679,10 +679,10 @@ void down_mixed_kernel(DownParams shared, DownParams routed) {
   if (t < ns)
     down_tile<T, TL, false>(shared, t, lds);
   else
-    down_tile<T, TL, true>(routed, t - ns, lds);
+    down_tile<T, TL, true, false>(routed, t - ns, lds);
 }
 
-template <typename T, class TL, bool kGrouped>
+template <typename T, class TL, bool kGrouped, bool kEarlySlots>
 __device__ __forceinline__ void down_tile(const DownParams& p, int t, char* lds) {
   const int NT = (p.d + TL::BN - 1) / TL::BN;
   const int sub = kGrouped ? p.g.tile_rows / TL::BM : 1;
@@ -721,15 +721,18 @@ __device__ __forceinline__ void down_tile(const DownParams& p, int t, char* lds)
     }
     src[q] = base + 16 * stage_seg<TL>();
   }
-  // The output row (token slot) of each of the wave's rows, loaded before the mainloop so its
-  // latency hides behind the first stage, and written to LDS beside the staging area after it
-  // (the stage buffers hold that space until then). Looked up per store instead, each lookup
-  // would wait on a global load, and that wait (vmcnt) also waits for every store the wave has
-  // issued before it.
+  // The output row (token slot) of each of the wave's rows, written to LDS beside the staging
+  // area after the mainloop (the stage buffers hold that space until then). Looked up per
+  // store instead, each lookup would wait on a global load, and that wait (vmcnt) also waits
+  // for every store the wave has issued before it. With kEarlySlots the slots are loaded
+  // before the mainloop, so their latency hides behind the first stage. Not in the launch that
+  // also runs dense tiles (down_mixed_kernel): the compiler shares one stage loop between its
+  // two tile kinds, and the early load's register, live into that loop, made it wait for every
+  // stage load at each stage (the decode-sized down 30 -> 40 us).
   constexpr int kTab = TL::FM * 16;
   constexpr int kTabPerLane = (kTab + 63) / 64;
   int slot_of[kTabPerLane];
-  if (kGrouped) {
+  auto load_slots = [&]() {
     const int lane = threadIdx.x & 63, wm = (threadIdx.x >> 6) / TL::WN;
 #pragma unroll
     for (int q = 0; q < kTabPerLane; ++q) {
@@ -737,7 +740,8 @@ __device__ __forceinline__ void down_tile(const DownParams& p, int t, char* lds)
       const int tr = block_row<TL>(idx >> 4, wm) + (idx & 15);
       slot_of[q] = (idx < kTab && tr < rows) ? p.row_slot[row0 + tr] : -1;
     }
-  }
+  };
+  if constexpr (kGrouped && kEarlySlots) load_slots();
   f32x4_t acc[TL::FM][TL::FN];
   if (!missing)
     mainloop<T, TL, false>(src, stages<T, TL>(p.K), lds, acc, rows);
@@ -749,6 +753,7 @@ __device__ __forceinline__ void down_tile(const DownParams& p, int t, char* lds)
   };
   const int col0 = n0 + wn * TL::TN;
   if (kGrouped) {
+    if constexpr (!kEarlySlots) load_slots();
     const int lane = threadIdx.x & 63;
     constexpr int kStage = 16 * TL::TN * static_cast<int>(sizeof(float)) * TL::NW;
     static_assert(kStage + TL::NW * kTab * 4 <= TL::LDS, "slot table fits in LDS");

@@ -4,7 +4,8 @@
   before each load; the compiler treats M0 as reserved, so this checks that no other
   instruction of those kernels writes or reads M0.
 * No kernel writes through the scalar data cache (scalar stores, scalar atomics, scalar
-  cache write-back)."""
+  cache write-back).
+* No GEMM stage loop drains its loads in flight before reading a stage's fragments."""
 import os
 import re
 import subprocess
@@ -56,3 +57,19 @@ def test_no_scalar_cache_writes(src):
         op = t.split()[0]
         assert not re.match(r"s_(store|buffer_store|scratch_store|atomic|buffer_atomic|dcache_wb)",
                             op), (src, t)
+
+
+def test_stage_loops_keep_their_loads_in_flight():
+    """The mainloop's own waits for stage loads all come before its barrier. A wait for every
+    outstanding vector-memory load right before LDS fragment reads, with no barrier in
+    between, was put there by the compiler, and it drains the loads the pipeline keeps in
+    flight at every stage. That happened when a load issued before the mainloop was live into
+    a stage loop the compiler shared between a launch's two tile kinds (decode-sized down
+    30 -> 40 us); this guards against its return."""
+    ins = list(_instructions(_device_asm("gemm.hip")))
+    for i, t in enumerate(ins):
+        if t.startswith("s_waitcnt") and "vmcnt(0)" in t:
+            nxt = ins[i + 1:i + 4]
+            drains = any(x.startswith("ds_read") for x in nxt) and \
+                not any(x.startswith("s_barrier") for x in nxt[:2])
+            assert not drains, (i, t, nxt)

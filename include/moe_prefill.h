@@ -343,8 +343,8 @@ enum {
   MOE_STAGE_COMBINE = 11,    /* the combine alone: layers without a shared expert */
   MOE_STAGE_RMSNORM = 12,
   MOE_STAGE_DOWN_SHARED_COMBINE = 13, /* shared down GEMM with the combine in its epilogue */
-  MOE_STAGE_GU_MIXED = 14,  /* shared and routed gate/up GEMMs in one launch (resident experts,
-                               tall or big routed tiles) */
+  MOE_STAGE_GU_MIXED = 14,  /* shared and routed gate/up GEMMs in one launch (resident
+                               experts) */
   MOE_STAGE_GU_DOWN_FUSED = 15, /* routed gate/up and down GEMMs in one launch, h kept on chip
                                    (MOE_OPT_FUSED_GU_DOWN) */
   MOE_STAGE_DOWN_MIXED = 16, /* the shared expert's down GEMM (S alone) and the routed down GEMM

@@ -464,13 +464,16 @@ moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const i
   JoinOnExit pending{side, s};
   hipStream_t ss = offloaded ? nullptr : s;
   const int bm = routed_tile_rows(n, k, E);
-  // With every expert resident and tall or big routed tiles, the shared GU's units join the
-  // routed GU's launch (launch_gu_mixed), so the compute-bound shared tiles run beside the
-  // weight-streaming routed ones. A chunk of at most kSmallChunkRows tokens (decode tiles)
+  // With every expert resident, the shared GU's units join the routed GU's launch
+  // (launch_gu_mixed, on the routed tile shape), so the compute-bound shared tiles run beside
+  // the weight-streaming routed ones. A chunk of at most kSmallChunkRows tokens (decode tiles)
   // does the same with both shared GEMMs: alone, each would fill a few dozen CUs and wait on
   // load latency. Its shared down GEMM then writes S to the workspace and the stand-alone
   // combine follows (the same operations in the same order as the folded one, the same bits).
-  const bool mixed = !offloaded && sh.inter_shared && gu_mixed_supported(bm, n);
+  // (MOE_OPT_FUSED_GU_DOWN, where it applies, keeps the routed GEMMs in its fused launch.)
+  const bool fused = g_opt_fused_gu_down.load(std::memory_order_relaxed) &&
+                     gu_down_fused_supported(sh.dtype, bm, sh.inter);
+  const bool mixed = !offloaded && sh.inter_shared && !fused && gu_mixed_supported(bm, n);
   const bool small = mixed && n <= kSmallChunkRows && bm == kSmallChunkRows;
   if (sh.inter_shared && !mixed) {
     if (offloaded) {

@@ -1109,7 +1109,8 @@ static void gu_mixed(int dtype, const GuParams& ps, const GuParams& pr, hipStrea
 }
 
 bool gu_mixed_supported(int tile_rows, int64_t n) {
-  return tile_rows == TallTile::BM || tile_rows == BigTile::BM ||
+  return tile_rows == TallTile::BM || tile_rows == BigTile::BM || tile_rows == MidTile::BM ||
+         (tile_rows == SmallTile::BM && n > DecodeTile::BM) ||
          (tile_rows == DecodeTile::BM && n <= DecodeTile::BM);
 }
 
@@ -1125,6 +1126,8 @@ hipError_t launch_gu_mixed(int dtype, const void* x, int64_t t0, int64_t n, int 
   pr.row_tok = row_tok; pr.h = h; pr.clk = ps.clk;
   if (g.tile_rows == TallTile::BM) gu_mixed<TallTile>(dtype, ps, pr, s);
   else if (g.tile_rows == BigTile::BM) gu_mixed<BigTile>(dtype, ps, pr, s);
+  else if (g.tile_rows == MidTile::BM) gu_mixed<MidTile>(dtype, ps, pr, s);
+  else if (g.tile_rows == SmallTile::BM && n > DecodeTile::BM) gu_mixed<SmallTile>(dtype, ps, pr, s);
   else if (g.tile_rows == DecodeTile::BM && n <= DecodeTile::BM) gu_mixed<DecodeTile>(dtype, ps, pr, s);
   else return hipErrorInvalidValue;
   return hipGetLastError();

@@ -107,8 +107,8 @@ MOE_HIDDEN hipError_t launch_gu_routed(int dtype, const void* x, int64_t t0, int
 MOE_HIDDEN hipError_t launch_gu_dense(int dtype, const void* x, int64_t t0, int64_t n, int d,
                                       int Is, const void* w_gu, void* h, hipStream_t s);
 // The shared expert's gate/up GEMM and the routed one in one launch (routed M-tiles of
-// tile_rows rows for a chunk of n tokens, for which gu_mixed_supported holds: tall or big
-// tiles, or decode tiles when the chunk itself fits one).
+// tile_rows rows for a chunk of n tokens, for which gu_mixed_supported holds: 320-, 256-, 128-
+// or 64-row tiles, or decode tiles when the chunk itself fits one).
 MOE_HIDDEN bool gu_mixed_supported(int tile_rows, int64_t n);
 MOE_HIDDEN hipError_t launch_gu_mixed(int dtype, const void* x, int64_t t0, int64_t n, int d,
                                       int I, int Is, const void* w_gu_shared, void* h_shared,

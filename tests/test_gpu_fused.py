@@ -78,8 +78,9 @@ def test_fused_equals_separate(moe, T, chunk, d, E, k, I, Is, zipf):
     x = mi.make_x(wl, device="cuda")
     ref, p0 = _layer(moe, L, x, chunk, False)
     got, p1 = _layer(moe, L, x, chunk, True)
-    assert p0["gu_down_fused"] == 0 and p0["gu_routed"] > 0
-    assert p1["gu_down_fused"] > 0 and p1["gu_routed"] == 0 and p1["down_routed"] == 0
+    assert p0["gu_down_fused"] == 0 and p0["gu_routed"] + p0["gu_mixed"] > 0
+    assert p1["gu_down_fused"] > 0 and p1["gu_routed"] == 0 and p1["gu_mixed"] == 0
+    assert p1["down_routed"] == 0
     assert torch.equal(bits(got), bits(ref))
     n = min(chunk, T)
     assert torch.equal(_y_of_chunk(moe, L, x, chunk, 0, n, True),
@@ -116,7 +117,7 @@ def test_fused_option_leaves_other_chunks_alone(moe, case):
     x = mi.make_x(wl, device="cuda")
     ref, _ = _layer(moe, L, x, chunk, False)
     got, p = _layer(moe, L, x, chunk, True)
-    assert p["gu_down_fused"] == 0 and p["gu_routed"] > 0
+    assert p["gu_down_fused"] == 0 and p["gu_routed"] + p["gu_mixed"] > 0
     assert torch.equal(bits(got), bits(ref))
 
 
@@ -129,5 +130,5 @@ def test_fused_full_layer_chunk2048(moe):
     x = mi.make_x(wl, device="cuda")
     ref, _ = _layer(moe, L, x, 2048, False)
     got, p = _layer(moe, L, x, 2048, True)
-    assert p["gu_down_fused"] == 8 and p["gu_routed"] == 0
+    assert p["gu_down_fused"] == 8 and p["gu_routed"] == 0 and p["gu_mixed"] == 0
     assert torch.equal(bits(got), bits(ref))

@@ -432,7 +432,8 @@ def test_add_rmsnorm(moe):
 
 def test_profile_times_and_clocks(moe):
     """The opt-in profiling counts every GEMM launch and samples a plausible shader clock for
-    each GEMM stage; turning it off records nothing more."""
+    each GEMM stage; turning it off records nothing more. (Experts resident, so the shared
+    and routed gate/up GEMMs share one launch per chunk.)"""
     wl = mi.custom_workload("prof", T=700, d=256, E=64, k=6, inter=128, inter_shared=256,
                             seed=9)
     params, L = place(wl)
@@ -444,12 +445,13 @@ def test_profile_times_and_clocks(moe):
     finally:
         moe.moe_profile_enable(False)
     prof = moe.moe_profile_read(reset=True, clocks=True)
-    for stage in ("router", "gu_routed", "down_routed", "gu_shared", "down_shared_combine"):
+    for stage in ("router", "gu_mixed", "down_routed", "down_shared_combine"):
         ms, n, mhz = prof[stage]
         assert n >= 1 and ms > 0, (stage, prof[stage])
         assert 100 < mhz < 3500, (stage, mhz)
-    assert prof["down_shared_combine"][1] == 3                    # one per chunk
+    assert prof["down_shared_combine"][1] == 3 and prof["gu_mixed"][1] == 3   # one per chunk
     assert prof["combine"][1] == 0 and prof["down_shared"][1] == 0  # folded together
+    assert prof["gu_routed"][1] == 0 and prof["gu_shared"][1] == 0
     _run(moe, L, x, 256)
     assert all(v[1] == 0 for v in moe.moe_profile_read(reset=True).values())
 

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 5
+#define MOE_ABI_VERSION 6
 
 typedef enum {
   MOE_OK = 0,
@@ -100,6 +100,13 @@ const char* moe_last_error(void);
 /* Bytes of device workspace moe_prefill_chunk needs for chunks of up to max_chunk_tokens rows
  * (0 for an invalid shape). Pure host computation. */
 size_t moe_workspace_bytes(const moe_shape* shape, int64_t max_chunk_tokens);
+
+/* Bytes of workspace with which moe_prefill_layer over T tokens in chunks of `chunk` buckets
+ * every chunk up front: moe_workspace_bytes(shape, min(chunk, T)) plus every chunk's member
+ * lists (block histograms, counts, offsets, M-tiles, row_tok, row_slot; a few hundred KB per
+ * chunk). Equal to moe_workspace_bytes for a single chunk; 0 for an invalid shape, T < 0 or
+ * chunk < 1. Pure host computation. */
+size_t moe_layer_workspace_bytes(const moe_shape* shape, int64_t T, int64_t chunk);
 
 /* Where a moe_prefill_chunk call over n rows leaves its expert-major member lists and its
  * intermediate results inside the workspace (byte offsets from the workspace start; the
@@ -207,7 +214,10 @@ moe_status moe_prefill_chunk_noalloc(const moe_layer* layer, const void* x, cons
  * other experts through the remaining lines (a quarter, half or three quarters of the ring,
  * or nothing, whichever a least-recently-used estimate over the known chunk counts says
  * copies least); the output bytes are the same either way. Arguments as in the two calls above;
- * ws must hold moe_workspace_bytes(shape, min(chunk, T)). */
+ * ws must hold moe_workspace_bytes(shape, min(chunk, T)). With every expert resident, several
+ * chunks and ws_bytes >= moe_layer_workspace_bytes(shape, T, chunk), every chunk is bucketed
+ * up front in one set of launches (its member lists kept past the base workspace) instead of
+ * before its own GEMMs; the bytes of every output are the same. */
 moe_status moe_prefill_layer(const moe_layer* layer, const void* x, int64_t T, int64_t chunk,
                              int32_t* ids, float* weights, int32_t* chunk_counts, float* logits,
                              void* out, void* ws, size_t ws_bytes, void* stream,

@@ -18,6 +18,7 @@ from ._abi import (MOE_BF16, MOE_F32, MoeError, MoeLayer, MoeRingStats, MoeShape
 
 __all__ = [
     "MOE_BF16", "MOE_F32", "MoeError", "Layer", "Ring", "make_shape", "moe_workspace_bytes",
+    "moe_layer_workspace_bytes",
     "moe_prefill_route", "moe_prefill_chunk", "moe_prefill_layer", "moe_stage_experts",
     "moe_add_rmsnorm", "moe_abi_version", "line_elems", "moe_workspace_offsets",
     "layer_buffers", "moe_profile_enable", "moe_profile_read", "moe_prefill_stack",
@@ -65,6 +66,10 @@ def line_elems(sh: MoeShape) -> int:
 
 def moe_workspace_bytes(sh: MoeShape, max_chunk_tokens: int) -> int:
     return int(lib().moe_workspace_bytes(ctypes.byref(sh), int(max_chunk_tokens)))
+
+
+def moe_layer_workspace_bytes(sh: MoeShape, T: int, chunk: int) -> int:
+    return int(lib().moe_layer_workspace_bytes(ctypes.byref(sh), int(T), int(chunk)))
 
 
 def moe_workspace_offsets(sh: MoeShape, n: int) -> dict:
@@ -308,7 +313,7 @@ def layer_buffers(layer: Layer, T: int, chunk: int, device="cuda") -> dict:
         "weights": torch.empty((T, k), dtype=torch.float32, device=device),
         "chunk_counts": torch.empty((n_chunks, E), dtype=torch.int32, device=device),
         "logits": torch.empty((T, E), dtype=torch.float32, device=device),
-        "workspace": torch.empty(moe_workspace_bytes(sh, min(chunk, max(T, 1))),
+        "workspace": torch.empty(moe_layer_workspace_bytes(sh, max(T, 0), chunk),
                                  dtype=torch.uint8, device=device),
     }
 

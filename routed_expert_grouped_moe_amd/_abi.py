@@ -60,6 +60,7 @@ SIGNATURES = {
     "moe_status_string": (ctypes.c_char_p, [c_i32]),
     "moe_last_error": (ctypes.c_char_p, []),
     "moe_workspace_bytes": (c_sz, [ctypes.POINTER(MoeShape), c_i64]),
+    "moe_layer_workspace_bytes": (c_sz, [ctypes.POINTER(MoeShape), c_i64, c_i64]),
     "moe_workspace_offsets": (c_i32, [ctypes.POINTER(MoeShape), c_i64,
                                       ctypes.POINTER(MoeWsOffsets)]),
     "moe_prefill_route": (c_i32, [ctypes.POINTER(MoeLayer), c_vp, c_i64, c_i64, c_vp, c_vp,
@@ -92,7 +93,7 @@ SIGNATURES = {
 _lib = None
 
 
-ABI_VERSION = 5     # MOE_ABI_VERSION of include/moe_prefill.h
+ABI_VERSION = 6     # MOE_ABI_VERSION of include/moe_prefill.h
 
 
 def lib():

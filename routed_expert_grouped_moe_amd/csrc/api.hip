@@ -445,7 +445,8 @@ moe_status ring_waves(const moe_layer* L, const void* x, int64_t t0, int64_t n,
 moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const int32_t* ids,
                       const float* weights, int64_t t0, int64_t n, const int32_t* counts_host,
                       void* out, void* ws_v, size_t ws_bytes, hipStream_t s, hipStream_t cs,
-                      const Pinned* pin = nullptr, int32_t* counts_out = nullptr) {
+                      const Pinned* pin = nullptr, int32_t* counts_out = nullptr,
+                      const WsLayout* lists = nullptr) {
   const moe_shape& sh = L->shape;
   const int E = sh.n_experts, k = sh.top_k;
   WsLayout W;
@@ -454,6 +455,16 @@ moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const i
     return set_error(MOE_ERR_WORKSPACE, "workspace %zu bytes, %zu needed for %lld rows",
                      ws_bytes, W.total, static_cast<long long>(n));
   char* ws = static_cast<char*>(ws_v);
+  if (lists) {                  // the chunk was bucketed up front (moe_prefill_layer)
+    W.blk_counts = lists->blk_counts;
+    W.blk_base = lists->blk_base;
+    W.counts = lists->counts;
+    W.offsets = lists->offsets;
+    W.meta = lists->meta;
+    W.mtiles = lists->mtiles;
+    W.row_tok = lists->row_tok;
+    W.row_slot = lists->row_slot;
+  }
   const void** wtab = reinterpret_cast<const void**>(ws + W.wtab);
   // The shared expert's GU depends only on x. With every expert resident it runs in order
   // on the caller's stream: its GEMM and the routed ones each fill the chip, and running them
@@ -492,7 +503,7 @@ moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const i
   int64_t stride = 0;
   const bool uniform = !offloaded && uniform_lines(L->expert_lines, E, &stride);
   if (!uniform) MOE_HIP(launch_upload_ptrs(wtab, L->expert_lines, 0, E, s));
-  MOE_HIP(launch_bucket(ids + t0 * k, n, k, E, bm, ws, W, s, counts_out));
+  if (!lists) MOE_HIP(launch_bucket(ids + t0 * k, n, k, E, bm, ws, W, s, counts_out));
   float* y = reinterpret_cast<float*>(ws + W.y);
   if (!offloaded) {
     GemmGroups g{reinterpret_cast<const MTile*>(ws + W.mtiles),
@@ -612,6 +623,25 @@ bool ws_layout(const moe_shape& sh, int64_t max_n, WsLayout* L) {
   return true;
 }
 
+// A layer call's per-chunk member lists, when its workspace holds them all: the list part of
+// the layout for chunks of `chunk` tokens (block histograms through row_slot, contiguous) for
+// each chunk in turn, after the base workspace. Returns the bytes of one chunk's block and
+// moves L's list offsets to chunk 0's block at byte `base`.
+size_t chunk_lists_layout(const moe_shape& sh, int64_t chunk, size_t base, WsLayout* L) {
+  ws_layout(sh, chunk, L);
+  const size_t stride = L->h - L->blk_counts;
+  const size_t shift = base - L->blk_counts;
+  L->blk_counts += shift;
+  L->blk_base += shift;
+  L->counts += shift;
+  L->offsets += shift;
+  L->meta += shift;
+  L->mtiles += shift;
+  L->row_tok += shift;
+  L->row_slot += shift;
+  return stride;
+}
+
 }  // namespace moe
 
 using moe::set_error;
@@ -657,6 +687,16 @@ size_t moe_workspace_bytes(const moe_shape* shape, int64_t max_chunk_tokens) {
   moe::WsLayout L;
   moe::ws_layout(*shape, max_chunk_tokens, &L);
   return L.total;
+}
+
+size_t moe_layer_workspace_bytes(const moe_shape* shape, int64_t T, int64_t chunk) {
+  if (chunk < 1 || T < 0) return 0;
+  const size_t base = moe_workspace_bytes(shape, std::min(chunk, std::max<int64_t>(T, 1)));
+  if (base == 0) return 0;
+  const int64_t n_chunks = (T + chunk - 1) / chunk;
+  if (n_chunks < 2) return base;
+  moe::WsLayout L;
+  return base + static_cast<size_t>(n_chunks) * moe::chunk_lists_layout(*shape, chunk, base, &L);
 }
 
 moe_status moe_workspace_offsets(const moe_shape* shape, int64_t n, moe_ws_offsets* out) {
@@ -771,13 +811,43 @@ moe_status moe_prefill_layer(const moe_layer* layer, const void* x, int64_t T, i
       if (st != MOE_OK) return st;
     }
   }
+  // With every expert resident and room for every chunk's member lists, all chunks are
+  // bucketed up front in one set of launches (the same kernels on the same ids, so the same
+  // lists), and no chunk's GEMMs wait for bucketing launches of their own.
+  moe::WsLayout lists;
+  size_t list_stride = 0;
+  const bool prebucket = !offloaded && n_chunks >= 2 &&
+                         ws_bytes >= moe_layer_workspace_bytes(&layer->shape, T, chunk);
+  if (prebucket) {
+    const int k = layer->shape.top_k;
+    list_stride = moe::chunk_lists_layout(layer->shape, chunk, need, &lists);
+    hipError_t err = moe::launch_bucket_chunks(
+        ids, T, chunk, k, E, moe::routed_tile_rows(chunk, k, E),
+        moe::routed_tile_rows(T - (n_chunks - 1) * chunk, k, E), static_cast<char*>(ws), lists,
+        static_cast<int64_t>(list_stride), chunk_counts, s);
+    if (err != hipSuccess)
+      return set_error(MOE_ERR_HIP, "bucketing: %s", hipGetErrorString(err));
+  }
   for (int64_t c = 0; c < n_chunks; ++c) {
     const int64_t t0 = c * chunk;
     const int64_t n = std::min(chunk, T - t0);
+    moe::WsLayout lc = lists;
+    if (prebucket) {
+      const size_t o = static_cast<size_t>(c) * list_stride;
+      lc.blk_counts += o;
+      lc.blk_base += o;
+      lc.counts += o;
+      lc.offsets += o;
+      lc.meta += o;
+      lc.mtiles += o;
+      lc.row_tok += o;
+      lc.row_slot += o;
+    }
     st = moe::chunk_impl(layer, offloaded, x, ids, weights, t0, n,
                          offloaded ? hc.data() + c * E : nullptr, out, ws, ws_bytes, s, cs,
                          pin.experts.empty() ? nullptr : &pin,
-                         offloaded ? nullptr : chunk_counts + c * E);
+                         offloaded || prebucket ? nullptr : chunk_counts + c * E,
+                         prebucket ? &lc : nullptr);
     if (st != MOE_OK) break;
   }
   if (!pin.experts.empty()) {

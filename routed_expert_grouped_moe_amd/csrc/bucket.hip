@@ -13,6 +13,7 @@
 // every member-list row is written, and no access depends on an unchecked id. Ids as
 // moe_prefill_route writes them are always kept.
 #include <algorithm>
+#include <type_traits>
 
 #include "device_common.h"
 #include "moe_internal.h"
@@ -43,12 +44,45 @@ __device__ __forceinline__ bool slot_kept(const int32_t* tok_ids, int j, int e, 
   return true;
 }
 
+// Which chunk a workgroup buckets: chunk blockIdx.y of a prompt of T tokens cut into chunks of
+// `chunk`, its lists in the block of workspace stride * blockIdx.y bytes past the pointers
+// given (one chunk: chunk = T = n, stride 0). The bucketing of every chunk of a layer call can
+// so run in one set of launches, each chunk's lists exactly those of its own launches.
+struct ChunkSeg {
+  int64_t chunk, T;
+  int64_t stride;        // bytes between consecutive chunks' list blocks
+  int bm_last;           // M-tile rows of the last chunk (the others: the bm argument)
+  int32_t* counts_out;   // [chunks, E] each chunk's expert counts as well, or NULL
+};
+__device__ __forceinline__ int64_t seg_t0(const ChunkSeg& s) {
+  return static_cast<int64_t>(blockIdx.y) * s.chunk;
+}
+__device__ __forceinline__ int64_t seg_n(const ChunkSeg& s) {
+  return min(s.chunk, s.T - seg_t0(s));
+}
+template <typename P>
+__device__ __forceinline__ P* seg_at(P* p, const ChunkSeg& s) {
+  typedef typename std::conditional<std::is_const<P>::value, const char, char>::type C;
+  return reinterpret_cast<P*>(reinterpret_cast<C*>(p) + static_cast<int64_t>(blockIdx.y) * s.stride);
+}
+__device__ __forceinline__ int seg_bm(const ChunkSeg& s, int bm) {
+  return static_cast<int64_t>(blockIdx.y) == (s.T - 1) / s.chunk ? s.bm_last : bm;
+}
+__device__ __forceinline__ int32_t* seg_counts_out(const ChunkSeg& s, int E) {
+  return s.counts_out ? s.counts_out + static_cast<int64_t>(blockIdx.y) * E : nullptr;
+}
+
 // blk_counts[b][e] = kept slots of tokens [b*256, b*256+256) routed to e (LDS histogram).
 __global__ __launch_bounds__(kTokBlock) void block_hist_kernel(const int32_t* __restrict__ ids,
-                                                               int64_t n, int k, int E,
-                                                               int32_t* __restrict__ blk_counts) {
+                                                               int k, int E,
+                                                               int32_t* __restrict__ blk_counts,
+                                                               ChunkSeg seg) {
   __shared__ int32_t hist[kMaxE];
   __shared__ uint32_t mask[kMaxE * (kTokBlock / 32)];
+  const int64_t n = seg_n(seg);
+  if (static_cast<int64_t>(blockIdx.x) * kTokBlock >= n) return;   // past this chunk's blocks
+  ids += seg_t0(seg) * k;
+  blk_counts = seg_at(blk_counts, seg);
   const int tid = threadIdx.x;
   for (int e = tid; e < E; e += kTokBlock) hist[e] = 0;
   for (int w = tid; w < E * (kTokBlock / 32); w += kTokBlock) mask[w] = 0u;
@@ -71,15 +105,23 @@ __global__ __launch_bounds__(kTokBlock) void block_hist_kernel(const int32_t* __
 //   counts_out (if not NULL) = counts as well, the chunk's row of the layer call's
 //   chunk_counts.
 __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ blk_counts,
-                                                    int nb, int E, int bm,
+                                                    int E, int bm,
                                                     int32_t* __restrict__ blk_base,
                                                     int32_t* __restrict__ counts,
                                                     int32_t* __restrict__ offsets,
                                                     MTile* __restrict__ mtiles,
-                                                    int32_t* __restrict__ meta,
-                                                    int32_t* __restrict__ counts_out) {
+                                                    int32_t* __restrict__ meta, ChunkSeg seg) {
   __shared__ int32_t s_rows[kMaxE];
   __shared__ int32_t s_tiles[kMaxE];
+  const int nb = static_cast<int>((seg_n(seg) + kTokBlock - 1) / kTokBlock);
+  blk_counts = seg_at(blk_counts, seg);
+  blk_base = seg_at(blk_base, seg);
+  counts = seg_at(counts, seg);
+  offsets = seg_at(offsets, seg);
+  mtiles = seg_at(mtiles, seg);
+  meta = seg_at(meta, seg);
+  int32_t* counts_out = seg_counts_out(seg, E);
+  bm = seg_bm(seg, bm);
   const int e = threadIdx.x;
   int32_t run = 0;
   if (e < E) {
@@ -128,12 +170,20 @@ __global__ __launch_bounds__(1024) void scan_kernel(const int32_t* __restrict__ 
 // chose that expert in a 256-bit LDS mask; a token's rank among the block's tokens of expert
 // e is the number of marked tokens before it. Row = offsets[e] + blk_base[b][e] + rank.
 __global__ __launch_bounds__(kTokBlock) void permute_kernel(const int32_t* __restrict__ ids,
-                                                            int64_t n, int k, int E,
+                                                            int k, int E,
                                                             const int32_t* __restrict__ blk_base,
                                                             const int32_t* __restrict__ offsets,
                                                             int32_t* __restrict__ row_tok,
-                                                            int32_t* __restrict__ row_slot) {
+                                                            int32_t* __restrict__ row_slot,
+                                                            ChunkSeg seg) {
   __shared__ uint32_t mask[kMaxE * (kTokBlock / 32)];
+  const int64_t n = seg_n(seg);
+  if (static_cast<int64_t>(blockIdx.x) * kTokBlock >= n) return;   // past this chunk's blocks
+  ids += seg_t0(seg) * k;
+  blk_base = seg_at(blk_base, seg);
+  offsets = seg_at(offsets, seg);
+  row_tok = seg_at(row_tok, seg);
+  row_slot = seg_at(row_slot, seg);
   const int tid = threadIdx.x;
   for (int w = tid; w < E * (kTokBlock / 32); w += kTokBlock) mask[w] = 0u;
   __syncthreads();
@@ -173,17 +223,29 @@ __global__ __launch_bounds__(kTokBlock) void permute_kernel(const int32_t* __res
 constexpr int kScanBlocks = 8;
 template <bool kOneBlock>
 __global__ __launch_bounds__(kTokBlock) void permute_scan_kernel(
-    const int32_t* __restrict__ ids, int64_t n, int k, int E, int bm, int nb,
+    const int32_t* __restrict__ ids, int k, int E, int bm,
     const int32_t* __restrict__ blk_counts, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, MTile* __restrict__ mtiles, int32_t* __restrict__ meta,
-    int32_t* __restrict__ row_tok, int32_t* __restrict__ row_slot,
-    int32_t* __restrict__ counts_out) {
+    int32_t* __restrict__ row_tok, int32_t* __restrict__ row_slot, ChunkSeg seg) {
   constexpr int PER = kMaxE / kTokBlock;         // experts per thread in the scans
   __shared__ int32_t s_tot[kMaxE];               // rows of e in the chunk
   __shared__ int32_t s_pre[kMaxE];               // rows of e in blocks before this one
   __shared__ int32_t s_off[kMaxE + 1];           // exclusive scan of s_tot
   __shared__ int32_t s_part[2][kTokBlock];       // per-thread partial sums (rows, tiles)
   __shared__ uint32_t mask[kMaxE * (kTokBlock / 32)];
+  const int64_t n = seg_n(seg);
+  const int nb = static_cast<int>((n + kTokBlock - 1) / kTokBlock);
+  if (static_cast<int>(blockIdx.x) >= nb) return;                   // past this chunk's blocks
+  ids += seg_t0(seg) * k;
+  blk_counts = seg_at(blk_counts, seg);
+  counts = seg_at(counts, seg);
+  offsets = seg_at(offsets, seg);
+  mtiles = seg_at(mtiles, seg);
+  meta = seg_at(meta, seg);
+  row_tok = seg_at(row_tok, seg);
+  row_slot = seg_at(row_slot, seg);
+  int32_t* counts_out = seg_counts_out(seg, E);
+  bm = seg_bm(seg, bm);
   const int tid = threadIdx.x, b = blockIdx.x;
   for (int w = tid; w < E * (kTokBlock / 32); w += kTokBlock) mask[w] = 0u;
   const int64_t t = static_cast<int64_t>(b) * kTokBlock + tid;
@@ -315,52 +377,74 @@ hipError_t launch_upload_pairs(const void** table, const int32_t* idx, const voi
   return hipSuccess;
 }
 
-hipError_t launch_bucket(const int32_t* ids_chunk, int64_t n, int k, int E, int tile_rows,
-                         char* ws, const WsLayout& L, hipStream_t s, int32_t* counts_out) {
-  const int nb = static_cast<int>((n + kTokBlock - 1) / kTokBlock);
+namespace {
+
+// The bucketing launches for n_chunks chunks of seg.chunk tokens (grid.y = chunk): one
+// permute-with-scan launch when a chunk is one token block; else the block histograms, then
+// the scan inside the permute while a chunk has at most kScanBlocks blocks, or a scan launch
+// and the permute.
+hipError_t bucket_launches(const int32_t* ids, const ChunkSeg& seg, int n_chunks, int k, int E,
+                           int bm, char* ws, const WsLayout& L, hipStream_t s) {
+  const int nb = static_cast<int>((seg.chunk + kTokBlock - 1) / kTokBlock);
   int32_t* blk_counts = reinterpret_cast<int32_t*>(ws + L.blk_counts);
   int32_t* blk_base = reinterpret_cast<int32_t*>(ws + L.blk_base);
   int32_t* counts = reinterpret_cast<int32_t*>(ws + L.counts);
   int32_t* offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
   int32_t* meta = reinterpret_cast<int32_t*>(ws + L.meta);
   MTile* mtiles = reinterpret_cast<MTile*>(ws + L.mtiles);
+  int32_t* row_tok = reinterpret_cast<int32_t*>(ws + L.row_tok);
+  int32_t* row_slot = reinterpret_cast<int32_t*>(ws + L.row_slot);
+  const dim3 grid(static_cast<unsigned>(nb), static_cast<unsigned>(n_chunks));
   hipError_t err;
   if (nb == 1) {                // one launch: the block counts from its own masks
     ProfScope prof(MOE_STAGE_PERMUTE, s);
-    permute_scan_kernel<true><<<1, kTokBlock, 0, s>>>(ids_chunk, n, k, E, tile_rows, nb,
-                                                      blk_counts, counts, offsets, mtiles, meta,
-                                                      reinterpret_cast<int32_t*>(ws + L.row_tok),
-                                                      reinterpret_cast<int32_t*>(ws + L.row_slot),
-                                                      counts_out);
+    permute_scan_kernel<true><<<grid, kTokBlock, 0, s>>>(ids, k, E, bm, blk_counts, counts,
+                                                         offsets, mtiles, meta, row_tok,
+                                                         row_slot, seg);
     return hipGetLastError();
   }
   {
     ProfScope prof(MOE_STAGE_HIST, s);
-    block_hist_kernel<<<nb, kTokBlock, 0, s>>>(ids_chunk, n, k, E, blk_counts);
+    block_hist_kernel<<<grid, kTokBlock, 0, s>>>(ids, k, E, blk_counts, seg);
     err = hipGetLastError();
   }
   if (err != hipSuccess) return err;
   if (nb <= kScanBlocks) {
     ProfScope prof(MOE_STAGE_PERMUTE, s);
-    permute_scan_kernel<false><<<nb, kTokBlock, 0, s>>>(ids_chunk, n, k, E, tile_rows, nb,
-                                                        blk_counts, counts, offsets, mtiles, meta,
-                                                        reinterpret_cast<int32_t*>(ws + L.row_tok),
-                                                        reinterpret_cast<int32_t*>(ws + L.row_slot),
-                                                        counts_out);
+    permute_scan_kernel<false><<<grid, kTokBlock, 0, s>>>(ids, k, E, bm, blk_counts, counts,
+                                                          offsets, mtiles, meta, row_tok,
+                                                          row_slot, seg);
     return hipGetLastError();
   }
   {
     ProfScope prof(MOE_STAGE_SCAN, s);
-    scan_kernel<<<1, 1024, 0, s>>>(blk_counts, nb, E, tile_rows, blk_base, counts, offsets,
-                                   mtiles, meta, counts_out);
+    scan_kernel<<<dim3(1, static_cast<unsigned>(n_chunks)), 1024, 0, s>>>(
+        blk_counts, E, bm, blk_base, counts, offsets, mtiles, meta, seg);
     err = hipGetLastError();
   }
   if (err != hipSuccess) return err;
   ProfScope prof(MOE_STAGE_PERMUTE, s);
-  permute_kernel<<<nb, kTokBlock, 0, s>>>(ids_chunk, n, k, E, blk_base, offsets,
-                                          reinterpret_cast<int32_t*>(ws + L.row_tok),
-                                          reinterpret_cast<int32_t*>(ws + L.row_slot));
+  permute_kernel<<<grid, kTokBlock, 0, s>>>(ids, k, E, blk_base, offsets, row_tok, row_slot,
+                                            seg);
   return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bucket(const int32_t* ids_chunk, int64_t n, int k, int E, int tile_rows,
+                         char* ws, const WsLayout& L, hipStream_t s, int32_t* counts_out) {
+  if (n <= 0) return hipSuccess;
+  const ChunkSeg seg{n, n, 0, tile_rows, counts_out};
+  return bucket_launches(ids_chunk, seg, 1, k, E, tile_rows, ws, L, s);
+}
+
+hipError_t launch_bucket_chunks(const int32_t* ids, int64_t T, int64_t chunk, int k, int E,
+                                int tile_rows, int tile_rows_last, char* ws, const WsLayout& L,
+                                int64_t stride, int32_t* counts_out, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  const int64_t n_chunks = (T + chunk - 1) / chunk;
+  const ChunkSeg seg{chunk, T, stride, tile_rows_last, counts_out};
+  return bucket_launches(ids, seg, static_cast<int>(n_chunks), k, E, tile_rows, ws, L, s);
 }
 
 }  // namespace moe

@@ -82,6 +82,14 @@ MOE_HIDDEN hipError_t launch_upload_pairs(const void** table, const int32_t* idx
 MOE_HIDDEN hipError_t launch_bucket(const int32_t* ids_chunk, int64_t n, int k, int E,
                                     int tile_rows, char* ws, const WsLayout& L, hipStream_t s,
                                     int32_t* counts_out = nullptr);
+// The same for every chunk of a prompt of T tokens in one set of launches: chunk c's lists go
+// to the list offsets of L (a layout for chunks of `chunk` tokens) plus c * stride bytes, its
+// M-tiles are tile_rows tall (tile_rows_last for the last chunk), and counts_out [chunks, E]
+// (if not NULL) receives every chunk's expert counts.
+MOE_HIDDEN hipError_t launch_bucket_chunks(const int32_t* ids, int64_t T, int64_t chunk, int k,
+                                           int E, int tile_rows, int tile_rows_last, char* ws,
+                                           const WsLayout& L, int64_t stride,
+                                           int32_t* counts_out, hipStream_t s);
 
 // M-tile height of the routed GEMMs for a chunk of n tokens: 320 when experts average 192 to
 // 320 rows, else 256 from 128 rows up, else 64. The choice changes speed only, never a

@@ -48,7 +48,7 @@ def test_ctypes_table_matches_header(abi):
 
 def test_version_and_status_strings(abi):
     L = abi.lib()
-    assert L.moe_abi_version() == 5
+    assert L.moe_abi_version() == 6
     assert L.moe_status_string(abi.MOE_OK) == b"MOE_OK"
     assert L.moe_status_string(abi.MOE_ERR_WORKSPACE) == b"MOE_ERR_WORKSPACE"
     assert L.moe_status_string(99) == b"MOE_ERR_UNKNOWN"

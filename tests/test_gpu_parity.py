@@ -430,6 +430,50 @@ def test_add_rmsnorm(moe):
     assert torch.equal(x2.view(torch.int16), want.view(torch.int16))
 
 
+@pytest.mark.parametrize("T,chunk", [(3001, 1024), (700, 256), (900, 200), (16022, 4096)])
+def test_prebucketed_layer_equals_per_chunk(moe, T, chunk):
+    """A layer call whose workspace holds every chunk's member lists buckets all chunks in one
+    set of launches; with the base workspace each chunk buckets before its own GEMMs. Same
+    output bytes and chunk counts either way (and the batched pass's bytes), across a last
+    chunk with a lower tile height (3,001 at 1,024: 64-row, then 16-row tiles), one-block
+    chunks, chunks of 200 tokens that straddle token blocks, and the separate scan launch
+    (4,096-token chunks: 16 blocks)."""
+    wl = mi.custom_workload("prebucket", T=T, d=256, E=64, k=8, inter=128, inter_shared=256,
+                            zipf_s=1.1, seed=41)
+    print(f"[prebucket] T={T} chunk={chunk}", flush=True)
+    _, L = place(wl)
+    x = mi.make_x(wl, device="cuda")
+    bufs = moe.layer_buffers(L, T, chunk)
+    assert bufs["workspace"].numel() > moe.moe_workspace_bytes(L.shape, chunk)
+    moe.moe_profile_read(reset=True)
+    moe.moe_profile_enable(True)
+    try:
+        a = moe.moe_prefill_layer(L, x, chunk, bufs=bufs)
+        torch.cuda.synchronize()
+    finally:
+        moe.moe_profile_enable(False)
+    prof = moe.moe_profile_read(reset=True)
+    out_a, cc_a = a["out"].clone(), a["chunk_counts"].clone()
+    assert prof["permute"][1] == 1                                 # one launch, every chunk
+    small = dict(bufs)
+    small["workspace"] = torch.empty(moe.moe_workspace_bytes(L.shape, chunk), dtype=torch.uint8,
+                                     device="cuda")
+    moe.moe_profile_enable(True)
+    try:
+        b = moe.moe_prefill_layer(L, x, chunk, bufs=small)
+        torch.cuda.synchronize()
+    finally:
+        moe.moe_profile_enable(False)
+    prof = moe.moe_profile_read(reset=True)
+    assert prof["permute"][1] == (T + chunk - 1) // chunk        # one per chunk
+    assert torch.equal(bits(b["out"]), bits(out_a))
+    assert torch.equal(b["chunk_counts"], cc_a)
+    ref = _run(moe, L, x, T)["out"]
+    assert torch.equal(bits(ref), bits(out_a))
+    want = orc.chunk_counts(a["ids"].cpu().numpy(), chunk, wl.shape.n_experts)
+    assert np.array_equal(cc_a.cpu().numpy(), want)
+
+
 def test_profile_times_and_clocks(moe):
     """The opt-in profiling counts every GEMM launch and samples a plausible shader clock for
     each GEMM stage; turning it off records nothing more. (Experts resident, so the shared

@@ -40,7 +40,7 @@
 extern "C" {
 #endif
 
-#define MOE_ABI_VERSION 6
+#define MOE_ABI_VERSION 7
 
 typedef enum {
   MOE_OK = 0,
@@ -102,10 +102,12 @@ const char* moe_last_error(void);
 size_t moe_workspace_bytes(const moe_shape* shape, int64_t max_chunk_tokens);
 
 /* Bytes of workspace with which moe_prefill_layer over T tokens in chunks of `chunk` buckets
- * every chunk up front: moe_workspace_bytes(shape, min(chunk, T)) plus every chunk's member
- * lists (block histograms, counts, offsets, M-tiles, row_tok, row_slot; a few hundred KB per
- * chunk). Equal to moe_workspace_bytes for a single chunk; 0 for an invalid shape, T < 0 or
- * chunk < 1. Pure host computation. */
+ * every chunk up front and defers each chunk's shared down + combine: moe_workspace_bytes(shape,
+ * min(chunk, T)) plus every chunk's member lists (block histograms, counts, offsets, M-tiles,
+ * row_tok, row_slot; a few hundred KB per chunk) plus a second block for the shared expert's
+ * gate/up output (chunk * I_s elements of dtype; none when I_s == 0). Equal to
+ * moe_workspace_bytes for a single chunk; 0 for an invalid shape, T < 0 or chunk < 1. Pure host
+ * computation. */
 size_t moe_layer_workspace_bytes(const moe_shape* shape, int64_t T, int64_t chunk);
 
 /* Where a moe_prefill_chunk call over n rows leaves its expert-major member lists and its
@@ -217,7 +219,10 @@ moe_status moe_prefill_chunk_noalloc(const moe_layer* layer, const void* x, cons
  * ws must hold moe_workspace_bytes(shape, min(chunk, T)). With every expert resident, several
  * chunks and ws_bytes >= moe_layer_workspace_bytes(shape, T, chunk), every chunk is bucketed
  * up front in one set of launches (its member lists kept past the base workspace) instead of
- * before its own GEMMs; the bytes of every output are the same. */
+ * before its own GEMMs, and a chunk on 256-, 128- or 64-row routed tiles leaves its shared down
+ * GEMM and combine to the next chunk's gate/up launch (stage MOE_STAGE_GU_MIXED; the last
+ * chunk's, or one the next chunk's tiles cannot take, runs alone before it); the bytes of every
+ * output are the same. */
 moe_status moe_prefill_layer(const moe_layer* layer, const void* x, int64_t T, int64_t chunk,
                              int32_t* ids, float* weights, int32_t* chunk_counts, float* logits,
                              void* out, void* ws, size_t ws_bytes, void* stream,
@@ -354,7 +359,8 @@ enum {
   MOE_STAGE_RMSNORM = 12,
   MOE_STAGE_DOWN_SHARED_COMBINE = 13, /* shared down GEMM with the combine in its epilogue */
   MOE_STAGE_GU_MIXED = 14,  /* shared and routed gate/up GEMMs in one launch (resident
-                               experts) */
+                               experts); in a layer call of several chunks also the previous
+                               chunk's shared down GEMM with the combine */
   MOE_STAGE_GU_DOWN_FUSED = 15, /* routed gate/up and down GEMMs in one launch, h kept on chip
                                    (MOE_OPT_FUSED_GU_DOWN) */
   MOE_STAGE_DOWN_MIXED = 16, /* the shared expert's down GEMM (S alone) and the routed down GEMM

@@ -93,7 +93,7 @@ SIGNATURES = {
 _lib = None
 
 
-ABI_VERSION = 6     # MOE_ABI_VERSION of include/moe_prefill.h
+ABI_VERSION = 7     # MOE_ABI_VERSION of include/moe_prefill.h
 
 
 def lib():

@@ -442,15 +442,41 @@ moe_status ring_waves(const moe_layer* L, const void* x, int64_t t0, int64_t n,
   return MOE_OK;
 }
 
+// A layer call's deferred shared down + combine: a chunk on 256-, 128- or 64-row routed tiles
+// leaves its shared down GEMM and combine to the next chunk's gate/up launch
+// (launch_gu_mixed_combine). The deferring chunks alternate between two h_shared blocks, since
+// a chunk's gate/up writes its own while the previous chunk's down GEMM reads that one; every
+// chunk of the call uses the workspace layout of layout_rows rows, so Y, which the next
+// chunk's routed down GEMM overwrites only after that launch, is at one place.
+struct DeferredCombine {
+  void* h_shared[2] = {nullptr, nullptr};
+  int next = 0;                 // block of the next deferring chunk
+  bool pending = false;         // a chunk's shared down + combine has not run yet
+  const void* hs = nullptr;     // that chunk's h_shared block, first row and rows
+  int64_t t0 = 0, n = 0;
+  int64_t layout_rows = 0;
+};
+
+// Runs the pending shared down + combine in a launch of its own (after the last chunk, or
+// before a chunk whose tiles cannot take it). y: the workspace's Y, still that chunk's.
+hipError_t flush_deferred(const moe_layer* L, DeferredCombine* dc, const float* y,
+                          const float* weights, void* out, hipStream_t s) {
+  if (!dc->pending) return hipSuccess;
+  dc->pending = false;
+  const moe_shape& sh = L->shape;
+  return launch_down_combine(sh.dtype, dc->hs, dc->n, sh.d, sh.inter_shared, L->w_down_shared,
+                             y, weights, dc->t0, sh.top_k, out, s);
+}
+
 moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const int32_t* ids,
                       const float* weights, int64_t t0, int64_t n, const int32_t* counts_host,
                       void* out, void* ws_v, size_t ws_bytes, hipStream_t s, hipStream_t cs,
                       const Pinned* pin = nullptr, int32_t* counts_out = nullptr,
-                      const WsLayout* lists = nullptr) {
+                      const WsLayout* lists = nullptr, DeferredCombine* defer = nullptr) {
   const moe_shape& sh = L->shape;
   const int E = sh.n_experts, k = sh.top_k;
   WsLayout W;
-  ws_layout(sh, n, &W);
+  ws_layout(sh, defer ? defer->layout_rows : n, &W);
   if (ws_bytes < W.total)
     return set_error(MOE_ERR_WORKSPACE, "workspace %zu bytes, %zu needed for %lld rows",
                      ws_bytes, W.total, static_cast<long long>(n));
@@ -486,6 +512,9 @@ moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const i
                      gu_down_fused_supported(sh.dtype, bm, sh.inter);
   const bool mixed = !offloaded && sh.inter_shared && !fused && gu_mixed_supported(bm, n);
   const bool small = mixed && n <= kSmallChunkRows && bm == kSmallChunkRows;
+  const bool defer_this = defer && mixed && !small && gu_mixed_combine_supported(bm, n);
+  float* y = reinterpret_cast<float*>(ws + W.y);
+  if (defer && !defer_this) MOE_HIP(flush_deferred(L, defer, y, weights, out, s));
   if (sh.inter_shared && !mixed) {
     if (offloaded) {
       MOE_HIP(side.fork(s));
@@ -504,7 +533,6 @@ moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const i
   const bool uniform = !offloaded && uniform_lines(L->expert_lines, E, &stride);
   if (!uniform) MOE_HIP(launch_upload_ptrs(wtab, L->expert_lines, 0, E, s));
   if (!lists) MOE_HIP(launch_bucket(ids + t0 * k, n, k, E, bm, ws, W, s, counts_out));
-  float* y = reinterpret_cast<float*>(ws + W.y);
   if (!offloaded) {
     GemmGroups g{reinterpret_cast<const MTile*>(ws + W.mtiles),
                  reinterpret_cast<const int32_t*>(ws + W.meta) + kMetaMTiles,
@@ -522,6 +550,20 @@ moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const i
                                 L->w_down_shared, s_small, ws + W.h, sh.inter, g, row_slot, y,
                                 s));
       MOE_HIP(launch_combine(sh.dtype, y, s_small, weights, t0, n, k, sh.d, out, s));
+      return MOE_OK;
+    }
+    if (defer_this) {
+      void* hs = defer->h_shared[defer->next];
+      MOE_HIP(launch_gu_mixed_combine(sh.dtype, x, t0, n, sh.d, sh.inter, sh.inter_shared,
+                                      L->w_gu_shared, hs, g, row_tok, ws + W.h, defer->hs,
+                                      defer->t0, defer->pending ? defer->n : 0,
+                                      L->w_down_shared, y, weights, k, out, s));
+      MOE_HIP(launch_down_routed(sh.dtype, ws + W.h, sh.d, sh.inter, g, row_slot, y, s));
+      defer->pending = true;
+      defer->hs = hs;
+      defer->t0 = t0;
+      defer->n = n;
+      defer->next ^= 1;
       return MOE_OK;
     }
     if (mixed) {
@@ -623,23 +665,34 @@ bool ws_layout(const moe_shape& sh, int64_t max_n, WsLayout* L) {
   return true;
 }
 
-// A layer call's per-chunk member lists, when its workspace holds them all: the list part of
-// the layout for chunks of `chunk` tokens (block histograms through row_slot, contiguous) for
-// each chunk in turn, after the base workspace. Returns the bytes of one chunk's block and
-// moves L's list offsets to chunk 0's block at byte `base`.
-size_t chunk_lists_layout(const moe_shape& sh, int64_t chunk, size_t base, WsLayout* L) {
-  ws_layout(sh, chunk, L);
-  const size_t stride = L->h - L->blk_counts;
-  const size_t shift = base - L->blk_counts;
-  L->blk_counts += shift;
-  L->blk_base += shift;
-  L->counts += shift;
-  L->offsets += shift;
-  L->meta += shift;
-  L->mtiles += shift;
-  L->row_tok += shift;
-  L->row_slot += shift;
-  return stride;
+// Workspace of a layer call of two or more chunks of `chunk` tokens that buckets them all up
+// front: the one-chunk layout for `chunk` rows (base bytes), then every chunk's member lists
+// in turn (that layout's block histograms through row_slot, one contiguous block of
+// list_stride bytes per chunk), then a second h_shared block (none without a shared expert)
+// for the deferred shared down + combine. `lists` is the one-chunk layout with its list
+// offsets moved to chunk 0's block.
+struct LayerWs {
+  WsLayout lists;
+  size_t base, list_stride, h_shared2, total;
+};
+
+void layer_ws_layout(const moe_shape& sh, int64_t T, int64_t chunk, LayerWs* L) {
+  WsLayout& W = L->lists;
+  ws_layout(sh, chunk, &W);
+  L->base = W.total;
+  L->list_stride = W.h - W.blk_counts;
+  const size_t shift = L->base - W.blk_counts;
+  W.blk_counts += shift;
+  W.blk_base += shift;
+  W.counts += shift;
+  W.offsets += shift;
+  W.meta += shift;
+  W.mtiles += shift;
+  W.row_tok += shift;
+  W.row_slot += shift;
+  const int64_t n_chunks = (T + chunk - 1) / chunk;
+  L->h_shared2 = L->base + static_cast<size_t>(n_chunks) * L->list_stride;
+  L->total = L->h_shared2 + (W.y - W.h_shared);
 }
 
 }  // namespace moe
@@ -695,8 +748,9 @@ size_t moe_layer_workspace_bytes(const moe_shape* shape, int64_t T, int64_t chun
   if (base == 0) return 0;
   const int64_t n_chunks = (T + chunk - 1) / chunk;
   if (n_chunks < 2) return base;
-  moe::WsLayout L;
-  return base + static_cast<size_t>(n_chunks) * moe::chunk_lists_layout(*shape, chunk, base, &L);
+  moe::LayerWs L;
+  moe::layer_ws_layout(*shape, T, chunk, &L);
+  return L.total;
 }
 
 moe_status moe_workspace_offsets(const moe_shape* shape, int64_t n, moe_ws_offsets* out) {
@@ -813,27 +867,36 @@ moe_status moe_prefill_layer(const moe_layer* layer, const void* x, int64_t T, i
   }
   // With every expert resident and room for every chunk's member lists, all chunks are
   // bucketed up front in one set of launches (the same kernels on the same ids, so the same
-  // lists), and no chunk's GEMMs wait for bucketing launches of their own.
-  moe::WsLayout lists;
-  size_t list_stride = 0;
+  // lists), and no chunk's GEMMs wait for bucketing launches of their own. With a shared
+  // expert, chunks then also defer their shared down + combine to the next chunk's gate/up
+  // launch where the tiles allow (DeferredCombine); the bytes are the same.
+  moe::LayerWs lw{};
   const bool prebucket = !offloaded && n_chunks >= 2 &&
                          ws_bytes >= moe_layer_workspace_bytes(&layer->shape, T, chunk);
+  moe::DeferredCombine dc;
+  moe::DeferredCombine* defer = nullptr;
   if (prebucket) {
     const int k = layer->shape.top_k;
-    list_stride = moe::chunk_lists_layout(layer->shape, chunk, need, &lists);
+    moe::layer_ws_layout(layer->shape, T, chunk, &lw);
     hipError_t err = moe::launch_bucket_chunks(
         ids, T, chunk, k, E, moe::routed_tile_rows(chunk, k, E),
-        moe::routed_tile_rows(T - (n_chunks - 1) * chunk, k, E), static_cast<char*>(ws), lists,
-        static_cast<int64_t>(list_stride), chunk_counts, s);
+        moe::routed_tile_rows(T - (n_chunks - 1) * chunk, k, E), static_cast<char*>(ws),
+        lw.lists, static_cast<int64_t>(lw.list_stride), chunk_counts, s);
     if (err != hipSuccess)
       return set_error(MOE_ERR_HIP, "bucketing: %s", hipGetErrorString(err));
+    if (layer->shape.inter_shared > 0) {
+      dc.h_shared[0] = static_cast<char*>(ws) + lw.lists.h_shared;
+      dc.h_shared[1] = static_cast<char*>(ws) + lw.h_shared2;
+      dc.layout_rows = chunk;
+      defer = &dc;
+    }
   }
   for (int64_t c = 0; c < n_chunks; ++c) {
     const int64_t t0 = c * chunk;
     const int64_t n = std::min(chunk, T - t0);
-    moe::WsLayout lc = lists;
+    moe::WsLayout lc = lw.lists;
     if (prebucket) {
-      const size_t o = static_cast<size_t>(c) * list_stride;
+      const size_t o = static_cast<size_t>(c) * lw.list_stride;
       lc.blk_counts += o;
       lc.blk_base += o;
       lc.counts += o;
@@ -847,8 +910,15 @@ moe_status moe_prefill_layer(const moe_layer* layer, const void* x, int64_t T, i
                          offloaded ? hc.data() + c * E : nullptr, out, ws, ws_bytes, s, cs,
                          pin.experts.empty() ? nullptr : &pin,
                          offloaded || prebucket ? nullptr : chunk_counts + c * E,
-                         prebucket ? &lc : nullptr);
+                         prebucket ? &lc : nullptr, defer);
     if (st != MOE_OK) break;
+  }
+  if (st == MOE_OK && defer) {
+    hipError_t err = moe::flush_deferred(
+        layer, defer, reinterpret_cast<const float*>(static_cast<char*>(ws) + lw.lists.y),
+        weights, out, s);
+    if (err != hipSuccess)
+      st = set_error(MOE_ERR_HIP, "shared down + combine: %s", hipGetErrorString(err));
   }
   if (!pin.experts.empty()) {
     moe_status rst = moe::ring_release(layer->ring, pin.lines.data(),

@@ -336,6 +336,21 @@ __device__ __forceinline__ bool xcd_tile(int n_tiles, int* t) {
 inline unsigned xcd_grid(int64_t n_tiles) {
   return static_cast<unsigned>((n_tiles + kXcds - 1) / kXcds * kXcds);
 }
+// Two unit sequences in one launch: each XCD works through its contiguous slice of sequence A
+// (na units), then its slice of sequence B (nb units), slices as in xcd_tile. Workgroups are
+// dispatched in order, so A's units start first on every XCD. The grid is
+// xcd_grid(na) + xcd_grid(nb) (nb may be an upper bound: surplus workgroups have no unit).
+__device__ __forceinline__ bool xcd_tile_two(int na, int nb, int* t, bool* in_a) {
+  const int w = static_cast<int>(blockIdx.x);
+  const int qa = (na + kXcds - 1) / kXcds, qb = (nb + kXcds - 1) / kXcds;
+  const int x = w % kXcds, j = w / kXcds;
+  const bool a = j < qa;
+  const int tt = a ? x * qa + j : x * qb + (j - qa);
+  if (tt >= (a ? na : nb) || (!a && j - qa >= qb)) return false;
+  *t = tt;
+  *in_a = a;
+  return true;
+}
 
 // Output of one wave's blocks through LDS in 16-row rounds: the lanes write their accumulator
 // values (transformed by `val`) into a per-wave staging area, then store whole rows with
@@ -680,6 +695,33 @@ void down_mixed_kernel(DownParams shared, DownParams routed) {
     down_tile<T, TL, false>(shared, t, lds);
   else
     down_tile<T, TL, true, false>(routed, t - ns, lds);
+}
+
+// The previous chunk's shared down GEMM with the combine in its epilogue (dense down units, as
+// down_kernel works them) and this chunk's shared and routed gate/up units, in one launch: a
+// layer call of several chunks defers each chunk's shared down + combine to the next chunk's
+// gate/up launch, which does not depend on it. Alone, that GEMM gives the chip one tile per CU
+// or less at 1,024 to 4,096 tokens a chunk; here its units run beside the gate/up units. Same
+// tiles, instruction and K order as the stand-alone launch (row-invariant), so the same bits.
+// On 64-row tiles the down units start first on every XCD; on taller ones they come last and
+// fill the gate/up launch's partial last round (each order measured faster on its tiles).
+template <typename T, class TL>
+__global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(2)))
+void gu_mixed_combine_kernel(DownParams prev, GuParams shared, GuParams routed) {
+  __shared__ __attribute__((aligned(1024))) char lds[TL::LDS];
+  constexpr bool kDownFirst = TL::BM == SmallTile::BM;
+  const int nd = prev.cout ? down_units<TL, false>(prev) : 0;
+  const int ns = gu_units<TL, false>(shared);
+  const int ng = ns + gu_units<TL, true>(routed);
+  int t;
+  bool in_a;
+  if (!(kDownFirst ? xcd_tile_two(nd, ng, &t, &in_a) : xcd_tile_two(ng, nd, &t, &in_a))) return;
+  if (in_a == kDownFirst)
+    down_tile<T, TL, false>(prev, t, lds);
+  else if (t < ns)
+    gu_tile<T, TL, false>(shared, t, lds);
+  else
+    gu_tile<T, TL, true>(routed, t - ns, lds);
 }
 
 template <typename T, class TL, bool kGrouped, bool kEarlySlots>
@@ -1130,6 +1172,48 @@ hipError_t launch_gu_mixed(int dtype, const void* x, int64_t t0, int64_t n, int 
   else if (g.tile_rows == SmallTile::BM && n > DecodeTile::BM) gu_mixed<SmallTile>(dtype, ps, pr, s);
   else if (g.tile_rows == DecodeTile::BM && n <= DecodeTile::BM) gu_mixed<DecodeTile>(dtype, ps, pr, s);
   else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+template <class TL>
+static void gu_mixed_combine(int dtype, const DownParams& pd, const GuParams& ps,
+                             const GuParams& pr, hipStream_t s) {
+  constexpr int HC = TL::BN / 2;
+  const int64_t nd = pd.cout ? (pd.n + TL::BM - 1) / TL::BM * ((pd.d + TL::BN - 1) / TL::BN) : 0;
+  const int64_t ng = (ps.n + TL::BM - 1) / TL::BM * ((ps.I + HC - 1) / HC) +
+                     static_cast<int64_t>(pr.g.tile_cap) * ((pr.I + HC - 1) / HC);
+  const unsigned grid = xcd_grid(nd) + xcd_grid(ng);
+  if (dtype == MOE_BF16) gu_mixed_combine_kernel<uint16_t, TL><<<grid, TL::NT, 0, s>>>(pd, ps, pr);
+  else gu_mixed_combine_kernel<float, TL><<<grid, TL::NT, 0, s>>>(pd, ps, pr);
+}
+
+bool gu_mixed_combine_supported(int tile_rows, int64_t n) {
+  return tile_rows == BigTile::BM || tile_rows == MidTile::BM ||
+         (tile_rows == SmallTile::BM && n > DecodeTile::BM);
+}
+
+hipError_t launch_gu_mixed_combine(int dtype, const void* x, int64_t t0, int64_t n, int d, int I,
+                                   int Is, const void* w_gu_shared, void* h_shared,
+                                   const GemmGroups& g, const int32_t* row_tok, void* h,
+                                   const void* prev_h_shared, int64_t prev_t0, int64_t prev_n,
+                                   const void* w_down_shared, const float* y,
+                                   const float* weights, int k, void* out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (!gu_mixed_combine_supported(g.tile_rows, n)) return hipErrorInvalidValue;
+  ProfScope prof(MOE_STAGE_GU_MIXED, s);
+  GuParams ps{}, pr{};
+  ps.x = x; ps.t0 = t0; ps.n = n; ps.d = d; ps.I = Is; ps.w = w_gu_shared; ps.h = h_shared;
+  ps.clk = prof_clock(MOE_STAGE_GU_MIXED);
+  pr.x = x; pr.t0 = t0; pr.n = 0; pr.d = d; pr.I = I; pr.w = nullptr; pr.g = g;
+  pr.row_tok = row_tok; pr.h = h; pr.clk = ps.clk;
+  DownParams pd{};
+  pd.h = prev_h_shared; pd.n = prev_n; pd.d = d; pd.K = Is; pd.w = w_down_shared;
+  pd.line_down_off = 0; pd.row_slot = nullptr; pd.out = nullptr; pd.clk = ps.clk;
+  pd.y = y; pd.wts = weights; pd.t0 = prev_t0; pd.k = k;
+  pd.cout = prev_n > 0 ? out : nullptr;
+  if (g.tile_rows == BigTile::BM) gu_mixed_combine<BigTile>(dtype, pd, ps, pr, s);
+  else if (g.tile_rows == MidTile::BM) gu_mixed_combine<MidTile>(dtype, pd, ps, pr, s);
+  else gu_mixed_combine<SmallTile>(dtype, pd, ps, pr, s);
   return hipGetLastError();
 }
 

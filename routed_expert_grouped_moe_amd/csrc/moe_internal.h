@@ -122,6 +122,20 @@ MOE_HIDDEN hipError_t launch_gu_mixed(int dtype, const void* x, int64_t t0, int6
                                       int I, int Is, const void* w_gu_shared, void* h_shared,
                                       const GemmGroups& g, const int32_t* row_tok, void* h,
                                       hipStream_t s);
+// launch_gu_mixed with the previous chunk's shared down GEMM and combine (prev_n rows from
+// prev_t0, its h_shared rows in prev_h_shared, its Y in y; prev_n == 0: none) in the same
+// launch. For 256-, 128- and 64-row routed tiles (gu_mixed_combine_supported; 64-row ones for
+// more than 16 tokens). h_shared must not be prev_h_shared: this chunk's gate/up writes it
+// while the previous chunk's down GEMM reads that one.
+MOE_HIDDEN bool gu_mixed_combine_supported(int tile_rows, int64_t n);
+MOE_HIDDEN hipError_t launch_gu_mixed_combine(int dtype, const void* x, int64_t t0, int64_t n,
+                                              int d, int I, int Is, const void* w_gu_shared,
+                                              void* h_shared, const GemmGroups& g,
+                                              const int32_t* row_tok, void* h,
+                                              const void* prev_h_shared, int64_t prev_t0,
+                                              int64_t prev_n, const void* w_down_shared,
+                                              const float* y, const float* weights, int k,
+                                              void* out, hipStream_t s);
 MOE_HIDDEN hipError_t launch_down_routed(int dtype, const void* h, int d, int I,
                                          const GemmGroups& g, const int32_t* row_slot,
                                          float* y, hipStream_t s);

@@ -48,7 +48,7 @@ def test_ctypes_table_matches_header(abi):
 
 def test_version_and_status_strings(abi):
     L = abi.lib()
-    assert L.moe_abi_version() == 6
+    assert L.moe_abi_version() == 7
     assert L.moe_status_string(abi.MOE_OK) == b"MOE_OK"
     assert L.moe_status_string(abi.MOE_ERR_WORKSPACE) == b"MOE_ERR_WORKSPACE"
     assert L.moe_status_string(99) == b"MOE_ERR_UNKNOWN"
@@ -89,6 +89,37 @@ def test_workspace_bytes(abi):
     assert o.total == w100
     assert o.counts < o.offsets < o.row_tok < o.row_slot < o.total
     assert all(v % 256 == 0 for v in (o.counts, o.offsets, o.row_tok, o.row_slot))
+
+
+def test_layer_workspace_bytes(abi):
+    """A layer call's workspace for up-front bucketing and the deferred shared down + combine:
+    the one-chunk workspace, one block of member lists per chunk (the one-chunk layout's
+    block histograms through row_slot: from after the expert-line table up to h) and a second
+    h_shared block for a chunk's rows; no extra block without a shared expert, nothing extra
+    for a single chunk."""
+    L = abi.lib()
+
+    def size(sh, T, chunk):
+        return L.moe_layer_workspace_bytes(ctypes.byref(sh), T, chunk)
+
+    for Is in (64, 0):
+        sh = _shape(abi, Is=Is)
+        E = sh.n_experts
+        base = L.moe_workspace_bytes(ctypes.byref(sh), 100)
+        o = abi.MoeWsOffsets()
+        assert L.moe_workspace_offsets(ctypes.byref(sh), 100, ctypes.byref(o)) == abi.MOE_OK
+        stride = o.h - -(-8 * E // 256) * 256          # lists: after the line table, up to h
+        second = o.y - o.h_shared
+        assert second == (-(-100 * Is * 2 // 256) * 256 if Is else 0)    # bf16 rows of I_s
+        assert size(sh, 100, 100) == base
+        assert size(sh, 60, 100) == L.moe_workspace_bytes(ctypes.byref(sh), 60)
+        assert size(sh, 0, 100) == L.moe_workspace_bytes(ctypes.byref(sh), 1)
+        for T in (101, 200, 201, 1000):
+            n_chunks = -(-T // 100)
+            assert size(sh, T, 100) == base + n_chunks * stride + second, (Is, T)
+    sh = _shape(abi)
+    assert size(sh, 100, 0) == 0 and size(sh, -1, 10) == 0
+    assert size(_shape(abi, d=96), 200, 100) == 0
 
 
 def test_validation_before_device_work(abi):

@@ -430,12 +430,18 @@ def test_add_rmsnorm(moe):
     assert torch.equal(x2.view(torch.int16), want.view(torch.int16))
 
 
-@pytest.mark.parametrize("T,chunk", [(3001, 1024), (700, 256), (900, 200), (16022, 4096)])
-def test_prebucketed_layer_equals_per_chunk(moe, T, chunk):
+@pytest.mark.parametrize("T,chunk,alone", [(3001, 1024, 1), (700, 256, 1), (900, 200, 2),
+                                           (16022, 4096, 1), (6096, 4096, 2)])
+def test_prebucketed_layer_equals_per_chunk(moe, T, chunk, alone):
     """A layer call whose workspace holds every chunk's member lists buckets all chunks in one
-    set of launches; with the base workspace each chunk buckets before its own GEMMs. Same
-    output bytes and chunk counts either way (and the batched pass's bytes), across a last
-    chunk with a lower tile height (3,001 at 1,024: 64-row, then 16-row tiles), one-block
+    set of launches and defers each chunk's shared down + combine to the next chunk's gate/up
+    launch where both chunks' tiles allow; with the base workspace each chunk buckets before
+    its own GEMMs and runs its own shared down + combine. Same output bytes and chunk counts
+    either way (and the batched pass's bytes). E = 64, k = 8: 1,024- and 4,096-token chunks
+    take 256-row tiles (down units last), a last chunk of 953 tokens 128-row ones, 256 and 200
+    tokens 64-row ones (down units first); a last chunk of 100 tokens (16-row tiles) and one of
+    2,000 (320-row tiles) cannot take the deferred launch, which then runs alone before them
+    (`alone`: stand-alone shared down + combine launches of the layer call). Also one-block
     chunks, chunks of 200 tokens that straddle token blocks, and the separate scan launch
     (4,096-token chunks: 16 blocks)."""
     wl = mi.custom_workload("prebucket", T=T, d=256, E=64, k=8, inter=128, inter_shared=256,
@@ -454,7 +460,10 @@ def test_prebucketed_layer_equals_per_chunk(moe, T, chunk):
         moe.moe_profile_enable(False)
     prof = moe.moe_profile_read(reset=True)
     out_a, cc_a = a["out"].clone(), a["chunk_counts"].clone()
+    n_chunks = (T + chunk - 1) // chunk
     assert prof["permute"][1] == 1                                 # one launch, every chunk
+    assert prof["down_shared_combine"][1] == alone
+    assert prof["gu_mixed"][1] + prof["gu_shared"][1] == n_chunks
     small = dict(bufs)
     small["workspace"] = torch.empty(moe.moe_workspace_bytes(L.shape, chunk), dtype=torch.uint8,
                                      device="cuda")
@@ -465,7 +474,8 @@ def test_prebucketed_layer_equals_per_chunk(moe, T, chunk):
     finally:
         moe.moe_profile_enable(False)
     prof = moe.moe_profile_read(reset=True)
-    assert prof["permute"][1] == (T + chunk - 1) // chunk        # one per chunk
+    assert prof["permute"][1] == n_chunks                         # one per chunk
+    assert prof["down_shared_combine"][1] == n_chunks
     assert torch.equal(bits(b["out"]), bits(out_a))
     assert torch.equal(b["chunk_counts"], cc_a)
     ref = _run(moe, L, x, T)["out"]
@@ -493,7 +503,9 @@ def test_profile_times_and_clocks(moe):
         ms, n, mhz = prof[stage]
         assert n >= 1 and ms > 0, (stage, prof[stage])
         assert 100 < mhz < 3500, (stage, mhz)
-    assert prof["down_shared_combine"][1] == 3 and prof["gu_mixed"][1] == 3   # one per chunk
+    # one gate/up launch per chunk; the first two chunks' shared down + combine run inside the
+    # next chunk's, the last chunk's alone
+    assert prof["down_shared_combine"][1] == 1 and prof["gu_mixed"][1] == 3
     assert prof["combine"][1] == 0 and prof["down_shared"][1] == 0  # folded together
     assert prof["gu_routed"][1] == 0 and prof["gu_shared"][1] == 0
     _run(moe, L, x, 256)

@@ -69,6 +69,17 @@ def test_tiny_fp32(moe):
     _full_parity(moe, mi.WORKLOADS["tiny_fp32"], F32_TOL, chunks=(40, 7, 1))
 
 
+def test_fp32_tile_heights_and_deferred_combine(moe):
+    """fp32 storage through the 256-, 128- and 64-row routed tiles (E = 16, k = 4: 600 tokens
+    batched and 520-token chunks take 256-row tiles, 200-token chunks 128-row ones, 64-token
+    chunks and the 80-token tail 64-row ones, a 24-token tail 16-row ones), each chunked call
+    deferring its shared down + combine into the next chunk's gate/up launch: the batched
+    bytes at every chunk size, and oracle parity."""
+    wl = mi.custom_workload("f32_tiles", T=600, d=128, E=16, k=4, inter=64, inter_shared=128,
+                            dtype="f32", zipf_s=1.1, seed=5)
+    _full_parity(moe, wl, F32_TOL, chunks=(64, 200, 520, 600))
+
+
 def test_small_bf16_many_chunks(moe):
     wl = mi.custom_workload("small", T=300, d=128, E=16, k=4, inter=64, inter_shared=128,
                             zipf_s=1.1, seed=3)

@@ -496,7 +496,8 @@ moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const i
   // on the caller's stream: its GEMM and the routed ones each fill the chip, and running them
   // side by side measured slower than in sequence. With a ring it runs on a side stream
   // (joined before the last kernel), filling the time the routed GEMMs wait for copies. Its
-  // down GEMM runs last, with the combine folded into its epilogue.
+  // down GEMM runs last, with the combine folded into its epilogue (in a layer call, possibly
+  // inside the next chunk's gate/up launch: DeferredCombine).
   SideStream side;
   JoinOnExit pending{side, s};
   hipStream_t ss = offloaded ? nullptr : s;

@@ -442,7 +442,7 @@ def test_add_rmsnorm(moe):
 
 
 @pytest.mark.parametrize("T,chunk,alone", [(3001, 1024, 1), (700, 256, 1), (900, 200, 2),
-                                           (16022, 4096, 1), (6096, 4096, 2)])
+                                           (16022, 4096, 1), (6096, 4096, 2), (1800, 800, 1)])
 def test_prebucketed_layer_equals_per_chunk(moe, T, chunk, alone):
     """A layer call whose workspace holds every chunk's member lists buckets all chunks in one
     set of launches and defers each chunk's shared down + combine to the next chunk's gate/up
@@ -450,7 +450,9 @@ def test_prebucketed_layer_equals_per_chunk(moe, T, chunk, alone):
     its own GEMMs and runs its own shared down + combine. Same output bytes and chunk counts
     either way (and the batched pass's bytes). E = 64, k = 8: 1,024- and 4,096-token chunks
     take 256-row tiles (down units last), a last chunk of 953 tokens 128-row ones, 256 and 200
-    tokens 64-row ones (down units first); a last chunk of 100 tokens (16-row tiles) and one of
+    tokens 64-row ones (down units first; 800-token chunks take 128-row tiles and hand their
+    shared down + combine to a 200-token last chunk on 64-row tiles); a last chunk of 100
+    tokens (16-row tiles) and one of
     2,000 (320-row tiles) cannot take the deferred launch, which then runs alone before them
     (`alone`: stand-alone shared down + combine launches of the layer call). Also one-block
     chunks, chunks of 200 tokens that straddle token blocks, and the separate scan launch

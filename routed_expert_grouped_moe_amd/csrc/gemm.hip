@@ -77,6 +77,12 @@ using MidTile = Tile<128, 256, 2, 4, 3>;   // 8 waves, 64 x 64 each; 3 stage buf
 // Decode-sized calls: a GEMM of at most 16 rows has few tiles, and each walks its K stages one
 // round trip at a time; narrow one-wave tiles with three stages in flight (40 KB LDS).
 using DecodeTile = Tile<16, 64, 1, 1, 4>;
+// Routers of short prompts: with few rows, tiles narrow in N give the chip more workgroups,
+// each with its own stage loads in flight. 16x16 one-wave tiles (16 KB LDS) while they make at
+// most 128 workgroups (and always for at most 16 rows), then 64x64 tiles of four waves of
+// 64x16 (64 KB) while they make at most 512.
+using RouterTile16 = Tile<16, 16, 1, 1, 4>;
+using RouterTile64 = Tile<64, 64, 1, 4, 4>;
 
 // Segment swizzle of tile row r (16-row blocks start at multiples of 16, so a lane's row
 // within its MFMA block decides it): 16-byte segment g of the row sits at g ^ swz(r). For
@@ -1090,10 +1096,14 @@ hipError_t launch_router_gemm(int dtype, const void* x, const void* w_router, co
   ProfScope prof(MOE_STAGE_ROUTER, s);
   RouterParams p{x, w_router, bias, logits, T, d, E, prof_clock(MOE_STAGE_ROUTER)};
   const int64_t mid_tiles = (T + MidTile::BM - 1) / MidTile::BM * ((E + MidTile::BN - 1) / MidTile::BN);
-  if (T <= DecodeTile::BM) {
-    const unsigned grid = xcd_grid((E + DecodeTile::BN - 1) / DecodeTile::BN);
-    if (dtype == MOE_BF16) router_kernel<uint16_t, DecodeTile><<<grid, DecodeTile::NT, 0, s>>>(p);
-    else router_kernel<float, DecodeTile><<<grid, DecodeTile::NT, 0, s>>>(p);
+  const int64_t t16 = (T + RouterTile16::BM - 1) / RouterTile16::BM *
+                      ((E + RouterTile16::BN - 1) / RouterTile16::BN);
+  const int64_t t64 = (T + RouterTile64::BM - 1) / RouterTile64::BM *
+                      ((E + RouterTile64::BN - 1) / RouterTile64::BN);
+  if (T <= RouterTile16::BM || t16 <= 128) {
+    const unsigned grid = xcd_grid(t16);
+    if (dtype == MOE_BF16) router_kernel<uint16_t, RouterTile16><<<grid, RouterTile16::NT, 0, s>>>(p);
+    else router_kernel<float, RouterTile16><<<grid, RouterTile16::NT, 0, s>>>(p);
   } else if (use_big_dense(T, (E + BigTile::BN - 1) / BigTile::BN)) {
     const unsigned grid = xcd_grid((T + BigTile::BM - 1) / BigTile::BM * ((E + BigTile::BN - 1) / BigTile::BN));
     if (dtype == MOE_BF16) router_kernel<uint16_t, BigTile><<<grid, BigTile::NT, 0, s>>>(p);
@@ -1105,6 +1115,10 @@ hipError_t launch_router_gemm(int dtype, const void* x, const void* w_router, co
     const unsigned grid = xcd_grid(mid_tiles);
     if (dtype == MOE_BF16) router_kernel<uint16_t, MidTile><<<grid, MidTile::NT, 0, s>>>(p);
     else router_kernel<float, MidTile><<<grid, MidTile::NT, 0, s>>>(p);
+  } else if (t64 <= 512) {
+    const unsigned grid = xcd_grid(t64);
+    if (dtype == MOE_BF16) router_kernel<uint16_t, RouterTile64><<<grid, RouterTile64::NT, 0, s>>>(p);
+    else router_kernel<float, RouterTile64><<<grid, RouterTile64::NT, 0, s>>>(p);
   } else if (const int64_t st = (T + SmallTile::BM - 1) / SmallTile::BM * ((E + SmallTile::BN - 1) / SmallTile::BN);
              st <= kCus) {
     const unsigned grid = xcd_grid(st);

@@ -352,15 +352,16 @@ def test_workspace_too_small_leaves_output(moe):
 
 
 def test_router_logits_independent_of_tile_shape(moe):
-    """The router GEMM picks its tile (16, 64 with two or four stage buffers, 128 or 256 rows)
-    from T; a token's logits, and so its routing, are the same bytes whichever tile computed
-    them."""
+    """The router GEMM picks its tile (256 or 128 rows; 64 rows by 256 columns with two or four
+    stage buffers; 64 by 64; 16 by 16) from T; a token's logits, and so its routing, are the
+    same bytes whichever tile computed them."""
     wl = mi.custom_workload("rtile", T=49152, d=256, E=512, k=8, inter=64, inter_shared=0,
                             seed=23)
     params, L = place(wl)
     x = mi.make_x(wl, device="cuda")
     ref = moe.moe_prefill_route(L, x, 49152)      # 192 x 2 = 384 tiles of 256 rows
-    for T in (12288, 10000, 700, 9):              # 128, 64 (2 and 4 buffers) and 16 rows
+    # 128 rows; 64 x 256 (2 and 4 buffers); 64 x 64; 16 x 16 (3 row blocks, and one)
+    for T in (12288, 10000, 6000, 700, 40, 9):
         got = moe.moe_prefill_route(L, x[:T].contiguous(), T)
         torch.cuda.synchronize()
         for key in ("logits", "ids", "weights"):

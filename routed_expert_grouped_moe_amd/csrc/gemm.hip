@@ -83,6 +83,11 @@ using DecodeTile = Tile<16, 64, 1, 1, 4>;
 // 64x16 (64 KB) while they make at most 512.
 using RouterTile16 = Tile<16, 16, 1, 1, 4>;
 using RouterTile64 = Tile<64, 64, 1, 4, 4>;
+// The shared expert's GEMMs of short prompts (17 to 512 rows) for the same reason: decode tiles
+// over 16-row blocks up to 64 rows, then 64x64 tiles (the down GEMM on RouterTile64; the
+// gate/up on two waves of 64x32, so that each wave holds the gate and the up half of its h
+// columns).
+using PairTile64 = Tile<64, 64, 1, 2, 4>;
 
 // Segment swizzle of tile row r (16-row blocks start at multiples of 16, so a lane's row
 // within its MFMA block decides it): 16-byte segment g of the row sits at g ^ swz(r). For
@@ -566,7 +571,8 @@ __device__ __forceinline__ void combine_slab(char* lds, Val val, int wm, int64_t
                                              const float* __restrict__ wts, int64_t t0, int k,
                                              int d, T* __restrict__ out, int col0, int cols) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  constexpr int NCOL = TL::TN, RB = NCOL * 4, CPR = RB / 16, U = TL::FM * TL::FN * 4 >= 128 ? 1 : 2;
+  constexpr int NCOL = TL::TN, RB = NCOL * 4, CPR = RB / 16,
+                U = (TL::FM * TL::FN * 4 >= 128 || 16 * CPR < 128) ? 1 : 2;
   static_assert(16 * RB * TL::NW <= TL::LDS, "staging fits in LDS");
   static_assert((16 * CPR) % (64 * U) == 0, "whole groups of U chunks per block");
   float* stg = reinterpret_cast<float*>(lds + wave * (16 * RB));
@@ -1070,7 +1076,8 @@ constexpr int64_t kCus = 256;      // compute units of an MI355X
 // times), else small ones: with four stage buffers when there is at most one per CU, so the
 // few tiles keep three K stages in flight instead of one, and half as wide when there would be
 // at most half a tile per CU (twice the tiles; in the shared down each then combines half the
-// columns).
+// columns). The shared expert's GEMMs of at most 512 rows take narrower tiles ahead of these
+// (decode tiles up to 64 rows, then 64x64).
 inline bool use_big_dense(int64_t n, int64_t n_tiles_big) {
   return n >= BigTile::BM && ((n + BigTile::BM - 1) / BigTile::BM) * n_tiles_big >= 384;
 }
@@ -1259,10 +1266,16 @@ hipError_t launch_gu_dense(int dtype, const void* x, int64_t t0, int64_t n, int 
   p.x = x; p.t0 = t0; p.n = n; p.d = d; p.I = Is; p.w = w_gu; p.row_tok = nullptr; p.h = h;
   p.clk = prof_clock(MOE_STAGE_GU_SHARED);
   const int64_t nt_big = (Is + BigTile::BN / 2 - 1) / (BigTile::BN / 2);
-  if (n <= DecodeTile::BM) {
-    const unsigned grid = xcd_grid((Is + DecodeTile::BN / 2 - 1) / (DecodeTile::BN / 2));
+  if (n <= 4 * DecodeTile::BM) {
+    const unsigned grid = xcd_grid((n + DecodeTile::BM - 1) / DecodeTile::BM *
+                                   ((Is + DecodeTile::BN / 2 - 1) / (DecodeTile::BN / 2)));
     if (dtype == MOE_BF16) gu_kernel<uint16_t, DecodeTile, false><<<grid, DecodeTile::NT, 0, s>>>(p);
     else gu_kernel<float, DecodeTile, false><<<grid, DecodeTile::NT, 0, s>>>(p);
+  } else if (n <= 8 * PairTile64::BM) {
+    const unsigned grid = xcd_grid((n + PairTile64::BM - 1) / PairTile64::BM *
+                                   ((Is + PairTile64::BN / 2 - 1) / (PairTile64::BN / 2)));
+    if (dtype == MOE_BF16) gu_kernel<uint16_t, PairTile64, false><<<grid, PairTile64::NT, 0, s>>>(p);
+    else gu_kernel<float, PairTile64, false><<<grid, PairTile64::NT, 0, s>>>(p);
   } else if (use_big_dense(n, nt_big)) {
     const unsigned grid = xcd_grid((n + BigTile::BM - 1) / BigTile::BM * nt_big);
     if (dtype == MOE_BF16) gu_kernel<uint16_t, BigTile, false><<<grid, BigTile::NT, 0, s>>>(p);
@@ -1340,10 +1353,16 @@ hipError_t launch_gu_down_fused(const void* x, int64_t t0, int d, int I, const G
 // Tile choice of the dense (shared-expert) down GEMM, with or without the combine.
 static void down_dense(int dtype, const DownParams& p, int64_t n, int d, hipStream_t s) {
   const int64_t nt_big = (d + BigTile::BN - 1) / BigTile::BN;
-  if (n <= DecodeTile::BM) {
-    const unsigned grid = xcd_grid((d + DecodeTile::BN - 1) / DecodeTile::BN);
+  if (n <= 4 * DecodeTile::BM) {
+    const unsigned grid = xcd_grid((n + DecodeTile::BM - 1) / DecodeTile::BM *
+                                   ((d + DecodeTile::BN - 1) / DecodeTile::BN));
     if (dtype == MOE_BF16) down_kernel<uint16_t, DecodeTile, false><<<grid, DecodeTile::NT, 0, s>>>(p);
     else down_kernel<float, DecodeTile, false><<<grid, DecodeTile::NT, 0, s>>>(p);
+  } else if (n <= 8 * RouterTile64::BM) {
+    const unsigned grid = xcd_grid((n + RouterTile64::BM - 1) / RouterTile64::BM *
+                                   ((d + RouterTile64::BN - 1) / RouterTile64::BN));
+    if (dtype == MOE_BF16) down_kernel<uint16_t, RouterTile64, false><<<grid, RouterTile64::NT, 0, s>>>(p);
+    else down_kernel<float, RouterTile64, false><<<grid, RouterTile64::NT, 0, s>>>(p);
   } else if (use_big_dense(n, nt_big)) {
     const unsigned grid = xcd_grid((n + BigTile::BM - 1) / BigTile::BM * nt_big);
     if (dtype == MOE_BF16) down_kernel<uint16_t, BigTile, false><<<grid, BigTile::NT, 0, s>>>(p);

@@ -159,9 +159,10 @@ moe_status moe_prefill_route(const moe_layer* layer, const void* x, int64_t T, i
  * fused silu(gate)*up epilogue and its down GEMM (grouped, bf16 MFMA, fp32 accumulation), the
  * shared expert over all n rows, then the fixed-order combine into out rows t0..t0+n-1. With a
  * shared expert its down GEMM runs last and forms the combine in its epilogue (same operations
- * in the same order as the stand-alone combine, so the same bits); for chunks of at most 16
- * tokens with every expert resident, the shared expert's tiles run instead inside the routed
- * gate/up and down launches, the down writing S, and the stand-alone combine follows.
+ * in the same order as the stand-alone combine, so the same bits); for chunks of at most 192
+ * tokens whose experts average fewer than 16 rows (decode tiles) and are all resident, the
+ * shared expert's tiles run instead inside the routed gate/up and down launches, the down
+ * writing S, and the stand-alone combine follows.
  *   x, ids, weights: the whole prompt's tensors as passed to / returned by moe_prefill_route
  *   counts_host  HOST [E] int32 expert counts of this chunk, or NULL. Only used with a ring: if
  *                NULL the call copies the counts to the host and waits for them (its only
@@ -351,8 +352,8 @@ enum {
   MOE_STAGE_PERMUTE = 6,    /* stable member-list permute */
   MOE_STAGE_GU_SHARED = 7,
   MOE_STAGE_DOWN_SHARED = 8,  /* shared down GEMM alone (S); unused by the layer calls, which
-                                 fold it into the combine (stage 13) or, for chunks of at most
-                                 16 tokens, into the routed down launch (stage 16) */
+                                 fold it into the combine (stage 13) or, for decode-sized
+                                 chunks, into the routed down launch (stage 16) */
   MOE_STAGE_GU_ROUTED = 9,
   MOE_STAGE_DOWN_ROUTED = 10,
   MOE_STAGE_COMBINE = 11,    /* the combine alone: layers without a shared expert */
@@ -364,7 +365,8 @@ enum {
   MOE_STAGE_GU_DOWN_FUSED = 15, /* routed gate/up and down GEMMs in one launch, h kept on chip
                                    (MOE_OPT_FUSED_GU_DOWN) */
   MOE_STAGE_DOWN_MIXED = 16, /* the shared expert's down GEMM (S alone) and the routed down GEMM
-                                in one launch (chunks of at most 16 tokens, experts resident) */
+                                in one launch (chunks of at most 192 tokens on decode tiles,
+                                experts resident) */
   MOE_STAGE_COUNT = 17
 };
 #define MOE_PROFILE_SLOTS 32    /* entries per array of moe_profile_t (>= MOE_STAGE_COUNT) */

@@ -504,15 +504,15 @@ moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const i
   const int bm = routed_tile_rows(n, k, E);
   // With every expert resident, the shared GU's units join the routed GU's launch
   // (launch_gu_mixed, on the routed tile shape), so the compute-bound shared tiles run beside
-  // the weight-streaming routed ones. A chunk of at most kSmallChunkRows tokens (decode tiles)
-  // does the same with both shared GEMMs: alone, each would fill a few dozen CUs and wait on
-  // load latency. Its shared down GEMM then writes S to the workspace and the stand-alone
+  // the weight-streaming routed ones. A chunk on decode tiles of at most kMixedDecodeRows tokens
+  // does the same with both shared GEMMs (16-row blocks): alone, each would fill a few dozen CUs
+  // and wait on load latency. Its shared down GEMM then writes S to the workspace and the stand-alone
   // combine follows (the same operations in the same order as the folded one, the same bits).
   // (MOE_OPT_FUSED_GU_DOWN, where it applies, keeps the routed GEMMs in its fused launch.)
   const bool fused = g_opt_fused_gu_down.load(std::memory_order_relaxed) &&
                      gu_down_fused_supported(sh.dtype, bm, sh.inter);
   const bool mixed = !offloaded && sh.inter_shared && !fused && gu_mixed_supported(bm, n);
-  const bool small = mixed && n <= kSmallChunkRows && bm == kSmallChunkRows;
+  const bool small = mixed && bm == kDecodeTileRows;
   const bool defer_this = defer && mixed && !small && gu_mixed_combine_supported(bm, n);
   float* y = reinterpret_cast<float*>(ws + W.y);
   if (defer && !defer_this) MOE_HIP(flush_deferred(L, defer, y, weights, out, s));
@@ -657,7 +657,7 @@ bool ws_layout(const moe_shape& sh, int64_t max_n, WsLayout* L) {
   L->h = take(elt * rows * I);
   L->h_shared = take(elt * max_n * Is);
   L->y = take(sizeof(float) * rows * d);
-  L->s_small = take(Is ? sizeof(float) * std::min<int64_t>(max_n, kSmallChunkRows) * d : 0);
+  L->s_small = take(Is ? sizeof(float) * std::min<int64_t>(max_n, kMixedDecodeRows) * d : 0);
   L->total = off;
   L->max_n = max_n;
   L->max_rows = rows;

@@ -1174,7 +1174,7 @@ static void gu_mixed(int dtype, const GuParams& ps, const GuParams& pr, hipStrea
 bool gu_mixed_supported(int tile_rows, int64_t n) {
   return tile_rows == TallTile::BM || tile_rows == BigTile::BM || tile_rows == MidTile::BM ||
          (tile_rows == SmallTile::BM && n > DecodeTile::BM) ||
-         (tile_rows == DecodeTile::BM && n <= DecodeTile::BM);
+         (tile_rows == DecodeTile::BM && n <= kMixedDecodeRows);
 }
 
 hipError_t launch_gu_mixed(int dtype, const void* x, int64_t t0, int64_t n, int d, int I, int Is,
@@ -1191,7 +1191,7 @@ hipError_t launch_gu_mixed(int dtype, const void* x, int64_t t0, int64_t n, int 
   else if (g.tile_rows == BigTile::BM) gu_mixed<BigTile>(dtype, ps, pr, s);
   else if (g.tile_rows == MidTile::BM) gu_mixed<MidTile>(dtype, ps, pr, s);
   else if (g.tile_rows == SmallTile::BM && n > DecodeTile::BM) gu_mixed<SmallTile>(dtype, ps, pr, s);
-  else if (g.tile_rows == DecodeTile::BM && n <= DecodeTile::BM) gu_mixed<DecodeTile>(dtype, ps, pr, s);
+  else if (g.tile_rows == DecodeTile::BM && n <= kMixedDecodeRows) gu_mixed<DecodeTile>(dtype, ps, pr, s);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
@@ -1244,7 +1244,7 @@ hipError_t launch_down_mixed(int dtype, const void* h_shared, int64_t n, int d, 
                              hipStream_t s) {
   using TL = DecodeTile;
   if (n <= 0) return hipSuccess;
-  if (g.tile_rows != TL::BM || n > TL::BM) return hipErrorInvalidValue;
+  if (g.tile_rows != TL::BM || n > kMixedDecodeRows) return hipErrorInvalidValue;
   ProfScope prof(MOE_STAGE_DOWN_MIXED, s);
   DownParams ps{}, pr{};
   ps.h = h_shared; ps.n = n; ps.d = d; ps.K = Is; ps.w = w_down_shared; ps.out = s_out;

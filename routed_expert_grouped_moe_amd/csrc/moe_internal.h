@@ -15,9 +15,10 @@ namespace moe {
 // ------------------------------------------------------------------ tiling constants
 constexpr int kMinTileRows = 16;  // smallest M-tile height of the routed GEMMs
 constexpr int kTokBlock = 256;    // tokens per block of the bucketing kernels
-// Chunks of at most this many tokens (one decode tile) run the shared expert's tiles inside
-// the routed launches and the stand-alone combine after them.
-constexpr int kSmallChunkRows = 16;
+constexpr int kDecodeTileRows = 16;   // routed M-tile height below 16 rows per expert
+// Chunks of at most this many tokens on decode tiles run the shared expert's tiles (16-row
+// blocks) inside the routed launches and the stand-alone combine after them.
+constexpr int kMixedDecodeRows = 192;
 
 // ------------------------------------------------------------------ device-side records
 struct MTile {                    // one M-tile of a routed expert: rows [m0, m0 + tile rows)
@@ -92,8 +93,8 @@ MOE_HIDDEN hipError_t launch_bucket_chunks(const int32_t* ids, int64_t T, int64_
                                            int32_t* counts_out, hipStream_t s);
 
 // M-tile height of the routed GEMMs for a chunk of n tokens: 320 when experts average 192 to
-// 320 rows, else 256 from 128 rows up, else 64. The choice changes speed only, never a
-// result bit.
+// 320 rows, 256 from 128 rows up otherwise, 128 from 48, 64 from 16 and 16 (decode tiles)
+// below. The choice changes speed only, never a result bit.
 MOE_HIDDEN int routed_tile_rows(int64_t n, int k, int E);
 
 struct GemmGroups {               // routed (grouped) problem description
@@ -116,7 +117,8 @@ MOE_HIDDEN hipError_t launch_gu_dense(int dtype, const void* x, int64_t t0, int6
                                       int Is, const void* w_gu, void* h, hipStream_t s);
 // The shared expert's gate/up GEMM and the routed one in one launch (routed M-tiles of
 // tile_rows rows for a chunk of n tokens, for which gu_mixed_supported holds: 320-, 256-, 128-
-// or 64-row tiles, or decode tiles when the chunk itself fits one).
+// or 64-row tiles, or decode tiles for a chunk of at most kMixedDecodeRows tokens, whose shared
+// rows then run as 16-row blocks).
 MOE_HIDDEN bool gu_mixed_supported(int tile_rows, int64_t n);
 MOE_HIDDEN hipError_t launch_gu_mixed(int dtype, const void* x, int64_t t0, int64_t n, int d,
                                       int I, int Is, const void* w_gu_shared, void* h_shared,
@@ -151,7 +153,7 @@ MOE_HIDDEN hipError_t launch_down_combine(int dtype, const void* h, int64_t n, i
                                           const float* weights, int64_t t0, int k, void* out,
                                           hipStream_t s);
 // The shared expert's down GEMM (S alone) and the routed one in one launch, for a chunk of at
-// most 16 tokens on decode tiles (g.tile_rows == 16).
+// most kMixedDecodeRows tokens on decode tiles (g.tile_rows == 16).
 MOE_HIDDEN hipError_t launch_down_mixed(int dtype, const void* h_shared, int64_t n, int d,
                                         int Is, const void* w_down_shared, float* s_out,
                                         const void* h, int I, const GemmGroups& g,

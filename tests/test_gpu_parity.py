@@ -82,11 +82,12 @@ def test_fp32_tile_heights_and_deferred_combine(moe):
 
 @pytest.mark.parametrize("dtype,tol", [("f32", F32_TOL), ("bf16", None)])
 def test_short_prompt_shared_tiles(moe, dtype, tol):
-    """Chunks averaging fewer than 16 rows per expert (E = 64, k = 2: up to 511 tokens) run
-    the shared expert's GEMMs in launches of their own, on decode tiles over 16-row blocks up
-    to 64 rows and on 64x64 tiles up to 512: 300, 100 and 40 tokens a chunk give the same
-    bytes, and in fp32 the oracle's values. (bf16 at d = 128: the end-to-end error gate is
-    left to the wider layers and the stage checks; routing is still gated.)"""
+    """Chunks averaging fewer than 16 rows per expert (E = 64, k = 2: up to 511 tokens) of
+    more than 192 tokens run the shared expert's GEMMs in launches of their own, here on 64x64
+    tiles (300 tokens); smaller ones run them inside the routed launches as 16-row blocks (100
+    and 40 tokens). All give the same bytes, and in fp32 the oracle's values. (bf16 at
+    d = 128: the end-to-end error gate is left to the wider layers and the stage checks;
+    routing is still gated.)"""
     wl = mi.custom_workload("short_" + dtype, T=300, d=128, E=64, k=2, inter=64,
                             inter_shared=128, dtype=dtype, zipf_s=1.1, seed=29)
     _full_parity(moe, wl, tol, chunks=(40, 100, 300))
@@ -454,7 +455,7 @@ def test_add_rmsnorm(moe):
     assert torch.equal(x2.view(torch.int16), want.view(torch.int16))
 
 
-@pytest.mark.parametrize("T,chunk,alone", [(3001, 1024, 1), (700, 256, 1), (900, 200, 2),
+@pytest.mark.parametrize("T,chunk,alone", [(3001, 1024, 1), (700, 256, 1), (900, 200, 1),
                                            (16022, 4096, 1), (6096, 4096, 2), (1800, 800, 1)])
 def test_prebucketed_layer_equals_per_chunk(moe, T, chunk, alone):
     """A layer call whose workspace holds every chunk's member lists buckets all chunks in one
@@ -465,9 +466,10 @@ def test_prebucketed_layer_equals_per_chunk(moe, T, chunk, alone):
     take 256-row tiles (down units last), a last chunk of 953 tokens 128-row ones, 256 and 200
     tokens 64-row ones (down units first; 800-token chunks take 128-row tiles and hand their
     shared down + combine to a 200-token last chunk on 64-row tiles); a last chunk of 100
-    tokens (16-row tiles) and one of
-    2,000 (320-row tiles) cannot take the deferred launch, which then runs alone before them
-    (`alone`: stand-alone shared down + combine launches of the layer call). Also one-block
+    tokens (16-row tiles, its shared expert inside the routed launches and the stand-alone
+    combine after them) and one of 2,000 (320-row tiles) cannot take the deferred launch, which
+    then runs alone before them (`alone`: stand-alone shared down + combine launches of the
+    layer call). Also one-block
     chunks, chunks of 200 tokens that straddle token blocks, and the separate scan launch
     (4,096-token chunks: 16 blocks)."""
     wl = mi.custom_workload("prebucket", T=T, d=256, E=64, k=8, inter=128, inter_shared=256,
@@ -501,7 +503,10 @@ def test_prebucketed_layer_equals_per_chunk(moe, T, chunk, alone):
         moe.moe_profile_enable(False)
     prof = moe.moe_profile_read(reset=True)
     assert prof["permute"][1] == n_chunks                         # one per chunk
-    assert prof["down_shared_combine"][1] == n_chunks
+    sizes = [min(chunk, T - t0) for t0 in range(0, T, chunk)]    # decode-sized: combine alone
+    n_small = sum(n <= 192 and n * 8 < 16 * 64 for n in sizes)
+    assert prof["down_shared_combine"][1] == n_chunks - n_small
+    assert prof["combine"][1] == n_small
     assert torch.equal(bits(b["out"]), bits(out_a))
     assert torch.equal(b["chunk_counts"], cc_a)
     ref = _run(moe, L, x, T)["out"]
@@ -539,15 +544,17 @@ def test_profile_times_and_clocks(moe):
 
 
 def test_small_chunks_mix_the_shared_expert_in(moe):
-    """Chunks of at most 16 tokens run the shared expert's tiles inside the routed gate/up and
-    down launches and the stand-alone combine after them; larger chunks fold the combine into
-    the shared down GEMM. Both give the batched pass's bytes."""
-    wl = mi.custom_workload("side", T=100, d=256, E=32, k=4, inter=128, inter_shared=256,
+    """Chunks on decode tiles (fewer than 16 rows per expert) of at most 192 tokens run the
+    shared expert's tiles, as 16-row blocks, inside the routed gate/up and down launches and
+    the stand-alone combine after them; larger chunks fold the combine into the shared down
+    GEMM. Both give the batched pass's bytes. (E = 64, k = 2: decode tiles below 512 tokens;
+    chunks of 5, 16, 17 and 192 tokens and a 108-token tail are mixed, 250 and 300 not.)"""
+    wl = mi.custom_workload("side", T=300, d=256, E=64, k=2, inter=128, inter_shared=256,
                             zipf_s=1.1, seed=19)
     params, L = place(wl)
     x = mi.make_x(wl, device="cuda")
     base = _run(moe, L, x, wl.T)
-    for chunk in (16, 17, 5):
+    for chunk in (16, 17, 5, 192, 250):
         moe.moe_profile_read(reset=True)
         moe.moe_profile_enable(True)
         try:
@@ -557,10 +564,12 @@ def test_small_chunks_mix_the_shared_expert_in(moe):
             moe.moe_profile_enable(False)
         prof = moe.moe_profile_read(reset=True)
         sizes = [min(chunk, wl.T - t0) for t0 in range(0, wl.T, chunk)]
-        n_small = sum(n <= 16 for n in sizes)
+        n_small = sum(n <= 192 and n * wl.shape.top_k < 16 * wl.shape.n_experts for n in sizes)
+        assert 0 < n_small
         assert prof["gu_mixed"][1] == n_small and prof["down_mixed"][1] == n_small
         assert prof["combine"][1] == n_small and prof["down_shared"][1] == 0
         assert prof["down_shared_combine"][1] == len(sizes) - n_small
+        assert prof["gu_shared"][1] == len(sizes) - n_small
         assert torch.equal(bits(got["out"]), bits(base["out"])), chunk
 
 

@@ -364,12 +364,13 @@ def test_workspace_too_small_leaves_output(moe):
     assert torch.equal(bits(out), bits(full))
 
 
-def test_router_logits_independent_of_tile_shape(moe):
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_router_logits_independent_of_tile_shape(moe, dtype):
     """The router GEMM picks its tile (256 or 128 rows; 64 rows by 256 columns with two or four
     stage buffers; 64 by 64; 16 by 16) from T; a token's logits, and so its routing, are the
     same bytes whichever tile computed them."""
     wl = mi.custom_workload("rtile", T=49152, d=256, E=512, k=8, inter=64, inter_shared=0,
-                            seed=23)
+                            dtype=dtype, seed=23)
     params, L = place(wl)
     x = mi.make_x(wl, device="cuda")
     ref = moe.moe_prefill_route(L, x, 49152)      # 192 x 2 = 384 tiles of 256 rows

@@ -220,10 +220,10 @@ moe_status moe_prefill_chunk_noalloc(const moe_layer* layer, const void* x, cons
  * ws must hold moe_workspace_bytes(shape, min(chunk, T)). With every expert resident, several
  * chunks and ws_bytes >= moe_layer_workspace_bytes(shape, T, chunk), every chunk is bucketed
  * up front in one set of launches (its member lists kept past the base workspace) instead of
- * before its own GEMMs, and a chunk on 256-, 128- or 64-row routed tiles leaves its shared down
- * GEMM and combine to the next chunk's gate/up launch (stage MOE_STAGE_GU_MIXED; the last
- * chunk's, or one the next chunk's tiles cannot take, runs alone before it); the bytes of every
- * output are the same. */
+ * before its own GEMMs, and a chunk on 256-, 128- or 64-row routed tiles (or on decode tiles,
+ * with 193 to 512 tokens) leaves its shared down GEMM and combine to the next chunk's gate/up
+ * launch (stage MOE_STAGE_GU_MIXED; the last chunk's, or one the next chunk's tiles cannot
+ * take, runs alone before it); the bytes of every output are the same. */
 moe_status moe_prefill_layer(const moe_layer* layer, const void* x, int64_t T, int64_t chunk,
                              int32_t* ids, float* weights, int32_t* chunk_counts, float* logits,
                              void* out, void* ws, size_t ws_bytes, void* stream,

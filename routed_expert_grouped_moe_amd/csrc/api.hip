@@ -513,10 +513,14 @@ moe_status chunk_impl(const moe_layer* L, bool offloaded, const void* x, const i
                      gu_down_fused_supported(sh.dtype, bm, sh.inter);
   const bool mixed = !offloaded && sh.inter_shared && !fused && gu_mixed_supported(bm, n);
   const bool small = mixed && bm == kDecodeTileRows;
-  const bool defer_this = defer && mixed && !small && gu_mixed_combine_supported(bm, n);
+  // In a layer call, a chunk on tiles gu_mixed_combine_supported takes leaves its shared down +
+  // combine to the next chunk's gate/up launch (DeferredCombine); on decode tiles (193 to 512
+  // tokens) its shared gate/up runs in that launch too.
+  const bool defer_this = defer && !offloaded && sh.inter_shared && !fused && !small &&
+                          gu_mixed_combine_supported(bm, n);
   float* y = reinterpret_cast<float*>(ws + W.y);
   if (defer && !defer_this) MOE_HIP(flush_deferred(L, defer, y, weights, out, s));
-  if (sh.inter_shared && !mixed) {
+  if (sh.inter_shared && !mixed && !defer_this) {
     if (offloaded) {
       MOE_HIP(side.fork(s));
       ss = side.stream;

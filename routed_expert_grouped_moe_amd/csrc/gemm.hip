@@ -715,13 +715,15 @@ void down_mixed_kernel(DownParams shared, DownParams routed) {
 // gate/up launch, which does not depend on it. Alone, that GEMM gives the chip one tile per CU
 // or less at 1,024 to 4,096 tokens a chunk; here its units run beside the gate/up units. Same
 // tiles, instruction and K order as the stand-alone launch (row-invariant), so the same bits.
-// On 64-row tiles the down units start first on every XCD; on taller ones they come last and
-// fill the gate/up launch's partial last round (each order measured faster on its tiles).
+// On 64-row and decode tiles the down units start first on every XCD; on taller ones they come
+// last and fill the gate/up launch's partial last round (each order measured faster on its
+// tiles). On decode tiles (chunks of 193 to 512 tokens) the shared gate/up units are 16-row
+// blocks too.
 template <typename T, class TL>
 __global__ __launch_bounds__(TL::NT) __attribute__((amdgpu_waves_per_eu(2)))
 void gu_mixed_combine_kernel(DownParams prev, GuParams shared, GuParams routed) {
   __shared__ __attribute__((aligned(1024))) char lds[TL::LDS];
-  constexpr bool kDownFirst = TL::BM == SmallTile::BM;
+  constexpr bool kDownFirst = TL::BM <= SmallTile::BM;
   const int nd = prev.cout ? down_units<TL, false>(prev) : 0;
   const int ns = gu_units<TL, false>(shared);
   const int ng = ns + gu_units<TL, true>(routed);
@@ -1210,7 +1212,8 @@ static void gu_mixed_combine(int dtype, const DownParams& pd, const GuParams& ps
 
 bool gu_mixed_combine_supported(int tile_rows, int64_t n) {
   return tile_rows == BigTile::BM || tile_rows == MidTile::BM ||
-         (tile_rows == SmallTile::BM && n > DecodeTile::BM);
+         (tile_rows == SmallTile::BM && n > DecodeTile::BM) ||
+         (tile_rows == DecodeTile::BM && n > kMixedDecodeRows && n <= kDeferDecodeRows);
 }
 
 hipError_t launch_gu_mixed_combine(int dtype, const void* x, int64_t t0, int64_t n, int d, int I,
@@ -1234,6 +1237,7 @@ hipError_t launch_gu_mixed_combine(int dtype, const void* x, int64_t t0, int64_t
   pd.cout = prev_n > 0 ? out : nullptr;
   if (g.tile_rows == BigTile::BM) gu_mixed_combine<BigTile>(dtype, pd, ps, pr, s);
   else if (g.tile_rows == MidTile::BM) gu_mixed_combine<MidTile>(dtype, pd, ps, pr, s);
+  else if (g.tile_rows == DecodeTile::BM) gu_mixed_combine<DecodeTile>(dtype, pd, ps, pr, s);
   else gu_mixed_combine<SmallTile>(dtype, pd, ps, pr, s);
   return hipGetLastError();
 }

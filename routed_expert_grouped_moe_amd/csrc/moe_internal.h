@@ -19,6 +19,10 @@ constexpr int kDecodeTileRows = 16;   // routed M-tile height below 16 rows per 
 // Chunks of at most this many tokens on decode tiles run the shared expert's tiles (16-row
 // blocks) inside the routed launches and the stand-alone combine after them.
 constexpr int kMixedDecodeRows = 192;
+// In a layer call, chunks on decode tiles of up to this many tokens (and more than
+// kMixedDecodeRows) defer their shared down + combine to the next chunk's gate/up launch, which
+// also runs their shared gate/up as 16-row blocks.
+constexpr int kDeferDecodeRows = 512;
 
 // ------------------------------------------------------------------ device-side records
 struct MTile {                    // one M-tile of a routed expert: rows [m0, m0 + tile rows)
@@ -127,8 +131,9 @@ MOE_HIDDEN hipError_t launch_gu_mixed(int dtype, const void* x, int64_t t0, int6
 // launch_gu_mixed with the previous chunk's shared down GEMM and combine (prev_n rows from
 // prev_t0, its h_shared rows in prev_h_shared, its Y in y; prev_n == 0: none) in the same
 // launch. For 256-, 128- and 64-row routed tiles (gu_mixed_combine_supported; 64-row ones for
-// more than 16 tokens). h_shared must not be prev_h_shared: this chunk's gate/up writes it
-// while the previous chunk's down GEMM reads that one.
+// more than 16 tokens) and decode tiles for kMixedDecodeRows + 1 to kDeferDecodeRows tokens.
+// h_shared must not be prev_h_shared: this chunk's gate/up writes it while the previous
+// chunk's down GEMM reads that one.
 MOE_HIDDEN bool gu_mixed_combine_supported(int tile_rows, int64_t n);
 MOE_HIDDEN hipError_t launch_gu_mixed_combine(int dtype, const void* x, int64_t t0, int64_t n,
                                               int d, int I, int Is, const void* w_gu_shared,

@@ -516,6 +516,43 @@ def test_prebucketed_layer_equals_per_chunk(moe, T, chunk, alone):
     assert np.array_equal(cc_a.cpu().numpy(), want)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_decode_tile_chunks_defer_shared_combine(moe, dtype):
+    """Chunks on decode tiles (E = 64, k = 2: fewer than 512 tokens) of 193 to 512 tokens, in a
+    layer call that buckets up front, run their shared gate/up as 16-row blocks inside their
+    gate/up launch and leave their shared down + combine to the next chunk's: the 300-token
+    chunks of a 1,100-token prompt and its 200-token tail launch one stand-alone shared down +
+    combine (the last chunk's) and no stand-alone shared gate/up, the per-chunk path four of
+    each, with the same bytes (and the batched pass's)."""
+    wl = mi.custom_workload("ddefer", T=1100, d=256, E=64, k=2, inter=128, inter_shared=256,
+                            dtype=dtype, zipf_s=1.1, seed=43)
+    _, L = place(wl)
+    x = mi.make_x(wl, device="cuda")
+    T, chunk = wl.T, 300
+    bufs = moe.layer_buffers(L, T, chunk)
+    runs = {}
+    for name, ws in (("layer", bufs["workspace"]),
+                     ("per_chunk", torch.empty(moe.moe_workspace_bytes(L.shape, chunk),
+                                               dtype=torch.uint8, device="cuda"))):
+        b = dict(bufs)
+        b["workspace"] = ws
+        moe.moe_profile_read(reset=True)
+        moe.moe_profile_enable(True)
+        try:
+            r = moe.moe_prefill_layer(L, x, chunk, bufs=b)
+            torch.cuda.synchronize()
+        finally:
+            moe.moe_profile_enable(False)
+        runs[name] = (r["out"].clone(), moe.moe_profile_read(reset=True))
+    out_l, prof_l = runs["layer"]
+    out_c, prof_c = runs["per_chunk"]
+    assert prof_l["down_shared_combine"][1] == 1 and prof_l["gu_shared"][1] == 0
+    assert prof_l["gu_mixed"][1] == 4
+    assert prof_c["down_shared_combine"][1] == 4 and prof_c["gu_shared"][1] == 4
+    assert torch.equal(bits(out_l), bits(out_c))
+    assert torch.equal(bits(out_l), bits(_run(moe, L, x, T)["out"]))
+
+
 def test_profile_times_and_clocks(moe):
     """The opt-in profiling counts every GEMM launch and samples a plausible shader clock for
     each GEMM stage; turning it off records nothing more. (Experts resident, so the shared
@@ -549,7 +586,8 @@ def test_small_chunks_mix_the_shared_expert_in(moe):
     shared expert's tiles, as 16-row blocks, inside the routed gate/up and down launches and
     the stand-alone combine after them; larger chunks fold the combine into the shared down
     GEMM. Both give the batched pass's bytes. (E = 64, k = 2: decode tiles below 512 tokens;
-    chunks of 5, 16, 17 and 192 tokens and a 108-token tail are mixed, 250 and 300 not.)"""
+    chunks of 5, 16, 17 and 192 tokens and a 108-token tail are mixed, 250 and 300 not; in a
+    layer call the 250-token chunk defers its shared down + combine.)"""
     wl = mi.custom_workload("side", T=300, d=256, E=64, k=2, inter=128, inter_shared=256,
                             zipf_s=1.1, seed=19)
     params, L = place(wl)
@@ -565,12 +603,16 @@ def test_small_chunks_mix_the_shared_expert_in(moe):
             moe.moe_profile_enable(False)
         prof = moe.moe_profile_read(reset=True)
         sizes = [min(chunk, wl.T - t0) for t0 in range(0, wl.T, chunk)]
-        n_small = sum(n <= 192 and n * wl.shape.top_k < 16 * wl.shape.n_experts for n in sizes)
+        decode = [n * wl.shape.top_k < 16 * wl.shape.n_experts for n in sizes]
+        n_small = sum(dc and n <= 192 for n, dc in zip(sizes, decode))
+        # decode-tile chunks of 193 to 512 tokens run their shared gate/up inside their gate/up
+        # launch and leave their shared down + combine to the next one (in this layer call)
+        n_defer = sum(dc and 192 < n <= 512 for n, dc in zip(sizes, decode))
         assert 0 < n_small
-        assert prof["gu_mixed"][1] == n_small and prof["down_mixed"][1] == n_small
+        assert prof["gu_mixed"][1] == n_small + n_defer and prof["down_mixed"][1] == n_small
         assert prof["combine"][1] == n_small and prof["down_shared"][1] == 0
         assert prof["down_shared_combine"][1] == len(sizes) - n_small
-        assert prof["gu_shared"][1] == len(sizes) - n_small
+        assert prof["gu_shared"][1] == len(sizes) - n_small - n_defer
         assert torch.equal(bits(got["out"]), bits(base["out"])), chunk
 
 

@@ -354,7 +354,7 @@ moe_status ring_waves(const moe_layer* L, const void* x, int64_t t0, int64_t n,
   // nothing (6 MiB DMA copies behind such waits lose 10-45% of the link: 16,022 tokens through
   // 64 lines took 412-414 ms against 429-433 ms). With resident experts in the waves' ranges
   // the GEMMs fill the chip and the copy kernel would stall behind them (the 8-layer stack:
-  // 1,396 ms against 1,345-1,349 ms with DMA copies), so those layers keep hipMemcpyAsync.
+  // 1,141 ms against 1,113-1,119 ms with DMA copies), so those layers keep hipMemcpyAsync.
   // pinned experts sit in their held lines for the whole layer call and run with whichever
   // wave's expert-id range covers them, as resident experts do
   const int per_wave = std::max(1, (R->n_lines - n_pin) / 2);
